@@ -1,0 +1,339 @@
+"""CPU oracle for the forward pass of one sparse Mixture-of-Experts layer.
+
+TEST INFRASTRUCTURE ONLY. Nothing on the product path may import, call or
+execute this module: it is used by ``tests/``, by ``__graft_entry__.smoke()``
+(to check one small GPU invocation) and by the ``cpu_baseline`` leg of
+``bench.py``. It shares no code with the HIP library and imports nothing from
+the ``mixture_experts_layer_42_amd`` package.
+
+What it computes is the plain definition of the layer,
+
+    y(x) = sum_i G(x)_i * E_i(x)
+
+(page "mixture-of-experts" (dongbusteel), section on how MoE differs from the
+Transformer: the output is the gate-weighted sum of expert outputs, G being the
+router's selection weights), written out step by step in float64 unless a step
+is a fixed float32 encoding (the routing-score spec below). Steps:
+
+  router     l = fp32( x @ W_r + b )                      computed in fp64, rounded once
+  selection  one of
+     token choice   each token keeps its k largest logits (ties: lower expert
+                    index first); gates = softmax over all E, renormalised over
+                    the k picks (page "moe-vs-mot-routing-inference-cost", basic
+                    MoE structure; dongbusteel page, TopK(G(x), k))
+     expert choice  each expert keeps the c = floor(k*T/E) tokens with the
+                    largest logit in its column (ties: lower token first);
+                    weight = softmax over the T tokens of that column
+                    (hrletsgo page, Mixture-of-Tokens section)
+     capacity drop  after token choice, an expert with more than
+                    C = floor(gamma * T*k/E) candidates keeps the C with the
+                    highest routing score p32 (ties: lower token first); dropped
+                    pairs weigh 0 and are not renormalised (Capacity-Aware
+                    Inference summary, Methodology, Token Drop: capacity
+                    C = gamma * N-bar, lowest gating scores dropped)
+  dispatch   kept (token, expert) pairs grouped by expert, ascending token
+             inside each expert (a stable sort by expert id)
+  expert     E_e(v) = W_down_e ( silu(W_gate_e v) * (W_up_e v) ),  silu(z) = z/(1+exp(-z))
+  shared     E_s(v), weight 1, for every token (routing/active-parameter page,
+             section on how routing allocates compute: a path all tokens take)
+  combine    y_t = sum over kept (t,e) of w_te * E_e(x_t)  (+ E_s(x_t))
+
+The routing score p32 used to rank the capacity drop is a float32 encoding
+fixed here so that any implementation can reproduce it bit for bit:
+    m_t = max_e l_te;  q_te = rexp(l_te - m_t);  S_t = (((q_t0 + q_t1) + q_t2) + ...);
+    p32_te = q_te / S_t          (each operation one IEEE float32 op, no fused multiply-add)
+with rexp the Cody & Waite exponential (W. J. Cody, W. Waite, "Software Manual
+for the Elementary Functions", 1980): argument reduction by n = rint(x*log2(e))
+against ln 2 split into a short high part (exact products n*LN2_HI) and a low
+part, then the degree-7 Taylor polynomial of exp on the reduced argument r,
+evaluated as 1 + (r + r*(r*P(r))) with P(r) = 1/2! + r/3! + ... + r^5/7! in Horner
+form (adding the 1 last keeps the result monotone in x), then scaling by 2**n
+built in the exponent field; rexp(x) = +0 for x < -87.
+
+Pins (tests/test_oracle_*.py): brute-force enumeration for every selection form,
+a dense evaluation of the definition, closed forms (k = E gives the plain
+softmax mixture; E = k = 1 gives a textbook SwiGLU FFN through torch.nn.functional),
+invariants fixed by the pages (exactly k per token, exactly c per expert,
+no expert above C, dropped pairs never outrank kept ones), and an exhaustive
+check of rexp against the float64 exponential over every float32 in [-87, 0].
+"""
+from __future__ import annotations
+
+import math
+from typing import Optional
+
+import numpy as np
+
+F32 = np.float32
+
+
+# ----------------------------------------------------------------------------- inputs
+
+def widen(a: Optional[np.ndarray]) -> Optional[np.ndarray]:
+    """Exact float64 copy of a stored tensor (bf16 bit patterns as uint16, or float32)."""
+    if a is None:
+        return None
+    if a.dtype == np.uint16:
+        a = (a.astype(np.uint32) << np.uint32(16)).view(np.float32)
+    return np.asarray(a, dtype=np.float64)
+
+
+# ----------------------------------------------------------------------------- router
+
+def router_logits(x: np.ndarray, w_router: np.ndarray, bias: Optional[np.ndarray]) -> np.ndarray:
+    """l[t,e] = sum_j x[t,j] W_r[j,e] + b[e]: one float64 product, rounded once to float32.
+    (dongbusteel page: G(x) is the router's selection weight; the router is linear in x.)"""
+    l = widen(x) @ np.asarray(w_router, dtype=np.float64)
+    if bias is not None:
+        l = l + np.asarray(bias, dtype=np.float64)[None, :]
+    return l.astype(np.float32)
+
+
+def softmax_rows(l: np.ndarray) -> np.ndarray:
+    """softmax over the last axis, float64 (router probability P_i of the hrletsgo page)."""
+    z = np.asarray(l, dtype=np.float64)
+    z = z - z.max(axis=-1, keepdims=True)
+    e = np.exp(z)
+    return e / e.sum(axis=-1, keepdims=True)
+
+
+# ----------------------------------------------------------------------------- token choice
+
+def topk_select(logits: np.ndarray, k: int) -> np.ndarray:
+    """Per token, the k experts with the largest logit, in descending order; equal
+    logits go to the lower expert index. Ranking by logit is ranking by softmax
+    probability, which is strictly increasing along a row."""
+    order = np.argsort(-np.asarray(logits, dtype=np.float32), axis=1, kind="stable")
+    return order[:, :k].astype(np.int32)
+
+
+def topk_gates(logits: np.ndarray, ids: np.ndarray, renorm: bool = True) -> np.ndarray:
+    """Gate of each pick: the full softmax probability, renormalised over the k picks
+    when ``renorm`` (equal to a softmax over the k selected logits)."""
+    p = softmax_rows(logits)
+    g = np.take_along_axis(p, ids.astype(np.int64), axis=1)
+    if renorm:
+        g = g / g.sum(axis=1, keepdims=True)
+    return g
+
+
+# ----------------------------------------------------------------------------- expert choice
+
+def expert_choice_capacity(T: int, k: int, E: int) -> int:
+    """c = k*T/N (hrletsgo page, Mixture-of-Tokens section), floored when not an integer."""
+    return (k * T) // E
+
+
+def expert_choice_select(logits: np.ndarray, k: int):
+    """Each expert takes the c tokens with the largest logit in its column (ties: lower
+    token index). Returns (sel [T,E] bool, weights [T,E] float64) where the weight of a
+    selected pair is the softmax over all T tokens of that expert's column."""
+    l = np.asarray(logits, dtype=np.float32)
+    T, E = l.shape
+    c = expert_choice_capacity(T, k, E)
+    sel = np.zeros((T, E), dtype=bool)
+    for e in range(E):
+        order = np.argsort(-l[:, e], kind="stable")
+        sel[order[:c], e] = True
+    s = softmax_rows(l.T).T          # softmax over tokens, per expert column
+    return sel, np.where(sel, s, 0.0)
+
+
+# ----------------------------------------------------------------------------- routing-score spec
+
+def _rexp_constants():
+    ln2 = math.log(2.0)
+    log2e = F32(1.0 / ln2)
+    ln2_f = F32(ln2)
+    ln2_hi = (np.array(ln2_f).view(np.uint32) & np.uint32(0xFFFFFE00)).view(np.float32)[()]
+    ln2_lo = F32(ln2 - float(ln2_hi))
+    coef = [F32(1.0 / math.factorial(i)) for i in range(8)]
+    return log2e, F32(ln2_hi), ln2_lo, coef
+
+
+_LOG2E, _LN2_HI, _LN2_LO, _COEF = _rexp_constants()
+REXP_CUTOFF = F32(-87.0)
+
+
+def rexp(x: np.ndarray) -> np.ndarray:
+    """exp(x) for float32 x <= 0, Cody-Waite reduction + degree-7 Taylor polynomial, every
+    step a single float32 operation (numpy float32 arithmetic rounds each op, no fusion).
+    Measured over every float32 in [-87, 0]: within 1.03 ulp of exp, and non-decreasing."""
+    x = np.asarray(x, dtype=np.float32)
+    n = np.rint(x * _LOG2E).astype(np.float32)
+    r = (x - n * _LN2_HI) - n * _LN2_LO
+    # Taylor polynomial, Horner form on the tail: exp(r) - 1 = r + r*(r*(c2 + r*(c3 + ... + r*c7)))
+    p = np.full_like(r, _COEF[7])
+    for i in range(6, 1, -1):
+        p = p * r + _COEF[i]
+    p = p * r
+    p = p * r
+    p = p + r
+    p = p + _COEF[0]
+    ni = np.clip(n, -126, 127).astype(np.int32)
+    scale = ((ni + np.int32(127)).astype(np.uint32) << np.uint32(23)).view(np.float32)
+    out = (p * scale).astype(np.float32)
+    return np.where(x < REXP_CUTOFF, F32(0.0), out).astype(np.float32)
+
+
+def routing_score32(logits: np.ndarray) -> np.ndarray:
+    """p32[t,e]: the float32 routing score that ranks the capacity drop (see module header)."""
+    l = np.asarray(logits, dtype=np.float32)
+    m = l.max(axis=1, keepdims=True)
+    q = rexp((l - m).astype(np.float32))
+    s = q[:, 0].copy()
+    for e in range(1, l.shape[1]):
+        s = (s + q[:, e]).astype(np.float32)
+    p = (q / s[:, None]).astype(np.float32)
+    return p + F32(0.0)             # canonical +0.0
+
+
+# ----------------------------------------------------------------------------- capacity drop
+
+def capacity(T: int, k: int, E: int, gamma: float) -> int:
+    """C = gamma * N-bar, N-bar = T*k/E the mean load per expert (Capacity-Aware Inference
+    summary, Token Drop), floored so that 'count <= gamma*N-bar' holds literally."""
+    return int(math.floor(float(gamma) * (float(T) * float(k) / float(E))))
+
+
+def capacity_drop(ids: np.ndarray, p32: np.ndarray, C: int, E: int) -> np.ndarray:
+    """kept[t,j] = 1 unless expert ids[t,j] has more than C candidates and (t, ids[t,j]) is not
+    among its C best by (p32 desc, token asc)."""
+    T, k = ids.shape
+    kept = np.ones((T, k), dtype=np.uint8)
+    for e in range(E):
+        tt, jj = np.nonzero(ids == e)          # candidates in ascending token order
+        if tt.size <= C:
+            continue
+        key = p32[tt, e]
+        order = np.argsort(-key, kind="stable")
+        kept[tt[order[C:]], jj[order[C:]]] = 0
+    return kept
+
+
+# ----------------------------------------------------------------------------- dispatch
+
+def dispatch(pair_token: np.ndarray, pair_expert: np.ndarray, pair_weight: np.ndarray, T: int, E: int):
+    """Group kept (token, expert) pairs by expert, ascending token inside an expert.
+
+    The pairs must be given in the order the combine reads a token's rows (token-major).
+    Returns counts [E], offsets [E+1], perm_token [N], perm_w [N], tok_ptr [T+1], tok_pos [N]:
+    row p of the expert-sorted layout holds token perm_token[p] with weight perm_w[p], and
+    token t's rows are tok_pos[tok_ptr[t]:tok_ptr[t+1]] in the given pair order."""
+    pair_token = np.asarray(pair_token, dtype=np.int64)
+    pair_expert = np.asarray(pair_expert, dtype=np.int64)
+    order = np.lexsort((pair_token, pair_expert))     # by expert, then token
+    counts = np.bincount(pair_expert, minlength=E).astype(np.int32)
+    offsets = np.zeros(E + 1, dtype=np.int32)
+    offsets[1:] = np.cumsum(counts)
+    N = pair_token.size
+    perm_token = pair_token[order].astype(np.int32)
+    perm_w = np.asarray(pair_weight, dtype=np.float64)[order]
+    pos_of_pair = np.empty(N, dtype=np.int32)
+    pos_of_pair[order] = np.arange(N, dtype=np.int32)
+    tok_counts = np.bincount(pair_token, minlength=T)
+    tok_ptr = np.zeros(T + 1, dtype=np.int32)
+    tok_ptr[1:] = np.cumsum(tok_counts)
+    # pairs are token-major, so pair i of token t sits at tok_ptr[t] + (its rank in t)
+    tok_pos = pos_of_pair.copy()
+    return dict(counts=counts, offsets=offsets, perm_token=perm_token, perm_w=perm_w,
+                tok_ptr=tok_ptr, tok_pos=tok_pos)
+
+
+# ----------------------------------------------------------------------------- whole routing
+
+def route(cfg, x=None, w_router=None, bias=None, logits=None) -> dict:
+    """Router + selection + dispatch for all T tokens. ``cfg`` needs T, E, k, routing,
+    gamma, renorm_topk. Pass ``logits`` to skip the router (selection-only parity)."""
+    T, E, k = cfg.T, cfg.E, cfg.k
+    if logits is None:
+        logits = router_logits(x, w_router, bias)
+    logits = np.asarray(logits, dtype=np.float32)
+    out = dict(logits=logits)
+    if cfg.routing == "expert":
+        sel, wts = expert_choice_select(logits, k)
+        tt, ee = np.nonzero(sel)                       # token-major, expert ascending
+        out.update(sel=sel, sel_w=wts, c=expert_choice_capacity(T, k, E))
+        out.update(dispatch(tt, ee, wts[tt, ee], T, E))
+        return out
+    ids = topk_select(logits, k)
+    g = topk_gates(logits, ids, bool(cfg.renorm_topk))
+    kept = np.ones((T, k), dtype=np.uint8)
+    if cfg.gamma > 0:
+        C = capacity(T, k, E, cfg.gamma)
+        p32 = routing_score32(logits)
+        kept = capacity_drop(ids, p32, C, E)
+        out.update(C=C, p32=p32)
+    w = np.where(kept == 1, g, 0.0)
+    tt, jj = np.nonzero(kept)                          # token-major, slot ascending
+    out.update(ids=ids, gates=g, kept=kept, w=w)
+    out.update(dispatch(tt, ids[tt, jj], g[tt, jj], T, E))
+    return out
+
+
+# ----------------------------------------------------------------------------- experts
+
+def silu(z: np.ndarray) -> np.ndarray:
+    with np.errstate(over="ignore"):
+        return z / (1.0 + np.exp(-z))
+
+
+def swiglu_ffn(v: np.ndarray, w_gate: np.ndarray, w_up: np.ndarray, w_down: np.ndarray) -> np.ndarray:
+    """E(v) = W_down (silu(W_gate v) * (W_up v)) for row vectors v [n, d]; weights in the
+    [out, in] layout. Float64."""
+    v = np.asarray(v, dtype=np.float64)
+    a = v @ widen(w_gate).T
+    b = v @ widen(w_up).T
+    return (silu(a) * b) @ widen(w_down).T
+
+
+def layer_forward(inp, tokens: Optional[np.ndarray] = None, logits: Optional[np.ndarray] = None,
+                  routing: Optional[dict] = None):
+    """y for the tokens ``tokens`` (default: all), float64 [len(tokens), d_model].
+
+    Routing is global (it depends on every token), the expert FFNs are evaluated only for
+    the requested tokens. Returns (y, routing dict)."""
+    cfg = inp.cfg
+    T = cfg.T
+    if routing is None:
+        routing = route(cfg, inp.x, inp.w_router, inp.bias, logits=logits)
+    toks = np.arange(T) if tokens is None else np.asarray(tokens, dtype=np.int64)
+    X = widen(inp.x[toks])
+    y = np.zeros((toks.size, cfg.d_model), dtype=np.float64)
+    where = {int(t): i for i, t in enumerate(toks)}
+    ptr, pos, ptok = routing["tok_ptr"], routing["tok_pos"], routing["perm_token"]
+    offs = routing["offsets"]
+    # rows of the requested tokens, grouped by expert
+    rows_by_expert = {}
+    for t in toks:
+        for p in pos[ptr[t]:ptr[t + 1]]:
+            e = int(np.searchsorted(offs, p, side="right") - 1)
+            rows_by_expert.setdefault(e, []).append(int(p))
+    for e, rows in rows_by_expert.items():
+        rows = np.asarray(rows)
+        idx = np.array([where[int(ptok[p])] for p in rows])
+        o = swiglu_ffn(X[idx], inp.w_gate[e], inp.w_up[e], inp.w_down[e])
+        y[idx] += routing["perm_w"][rows][:, None] * o       # each (t,e) appears once
+    if cfg.d_ff_shared > 0:
+        y += swiglu_ffn(X, inp.ws_gate, inp.ws_up, inp.ws_down)
+    return y, routing
+
+
+def shared_expert(inp, tokens: Optional[np.ndarray] = None) -> np.ndarray:
+    toks = np.arange(inp.cfg.T) if tokens is None else np.asarray(tokens)
+    return swiglu_ffn(widen(inp.x[toks]), inp.ws_gate, inp.ws_up, inp.ws_down)
+
+
+def routing_stats(routing: dict, E: int, T: int, k: int) -> dict:
+    """Expert-utilisation statistics: f_i (fraction of kept assignments per expert),
+    P_i (mean router probability per expert), the Switch balance term E*sum f_i P_i,
+    max/mean load and drop fraction (hrletsgo page: the auxiliary balance loss is the
+    sum of f_i times P_i; routing/active-parameter page: the utilisation distribution is
+    the leading indicator of routing collapse)."""
+    counts = routing["counts"].astype(np.float64)
+    total = counts.sum()
+    f = counts / total if total > 0 else np.zeros(E)
+    P = softmax_rows(routing["logits"]).mean(axis=0)
+    return dict(f=f, P=P, balance=float(E * np.sum(f * P)),
+                max_over_mean=float(counts.max() / (total / E)) if total > 0 else 0.0,
+                dropped=int(T * k - total) if "kept" in routing else 0)
