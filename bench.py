@@ -1,0 +1,194 @@
+"""Throughput of the sparse MoE layer forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 1] [--y-dtype bf16]
+
+One step = one moe_layer_forward over the whole workload (router, selection, dispatch
+indices, row gather, grouped gate/up + SwiGLU GEMM, grouped down GEMM, weighted
+combine), inputs resident in HBM. Prints ONE JSON line. The per-stage durations come
+from HIP events that the library records on its own stream at each stage boundary
+(moe_layer_forward_traced), so the dominant kernel's time is measured inside the timed
+region. The cpu_baseline leg times the CPU oracle on a bounded token sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/s + grouped-GEMM MFMA util %, Mixtral-shaped layer bf16"
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=1)
+    ap.add_argument("--tokens", type=int, default=0, help="override T (decode-shaped runs)")
+    ap.add_argument("--y-dtype", default="", choices=["", "bf16", "f32"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample", type=int, default=0, help="tokens in the oracle sample")
+    ap.add_argument("--pmc-copy", action="store_true",
+                    help="after timing, run a plain 256 MiB device copy (counter calibration)")
+    return ap.parse_args()
+
+
+def algorithmic(cfg, n_kept):
+    """Algorithmic work per layer: flops of the two grouped GEMMs (kept rows only, no
+    padding) and bytes each memory-bound stage must move."""
+    d, f, fs, T, E, k = cfg.d_model, cfg.d_ff, cfg.d_ff_shared, cfg.T, cfg.E, cfg.k
+    elt = 2 if cfg.dtype == "bf16" else 4
+    yel = 2 if (cfg.y_dtype or cfg.dtype) == "bf16" else 4
+    gate_up = 4.0 * d * f * n_kept + 4.0 * d * fs * T
+    down = 2.0 * d * f * n_kept + 2.0 * d * fs * T
+    route = T * d * elt + d * E * 4 + T * E * 4 + T * k * 8
+    dispatch = n_kept * d * elt * 2 + n_kept * 4      # each kept row read once, written once
+    combine = n_kept * d * 4 + n_kept * 8 + T * d * yel + (T * d * 4 if fs else 0)
+    return dict(gate_up=gate_up, down=down, route=route, dispatch=dispatch, combine=combine)
+
+
+def cpu_baseline(inp, sample_tokens):
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    toks = np.arange(sample_tokens)
+    t0 = time.perf_counter()
+    oracle.layer_forward(inp, tokens=toks)
+    dt = time.perf_counter() - t0
+    return {"value": sample_tokens / dt, "unit": "tokens/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"first {sample_tokens} of {inp.cfg.T} tokens (routing over all {inp.cfg.T}),"
+                      f" float64 numpy, {dt:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(json.dumps({"error": "this build runs the layer on one GPU only; "
+                                   "--gpus must be 1 (multi-GPU expert sharding is not built)"}))
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import mixture_experts_layer_42_amd as moe
+    import moe_inputs as mi
+
+    cfg = mi.CONFIGS[args.config]
+    if args.tokens:
+        cfg = cfg.with_(T=args.tokens)
+    if args.y_dtype:
+        cfg = cfg.with_(y_dtype=args.y_dtype)
+    print(f"[bench] generating {cfg.name} T={cfg.T}", file=sys.stderr, flush=True)
+    inp = mi.make_inputs(cfg, threads=16)
+    dev = {n: moe.device_tensor(getattr(inp, n)) for n in
+           ("x", "w_router", "bias", "w_gate", "w_up", "w_down", "ws_gate", "ws_up", "ws_down")}
+    prob = moe.problem_of(cfg)
+    nbytes = moe.moe_workspace_bytes(prob)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    ydt = torch.bfloat16 if (cfg.y_dtype or cfg.dtype) == "bf16" else torch.float32
+    y = torch.empty(cfg.T, cfg.d_model, dtype=ydt, device="cuda")
+    rb = moe.RoutingBuffers(prob)
+    stream = torch.cuda.current_stream()
+    nev = moe.MOE_STAGE_COUNT + 1
+
+    def new_events():
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(nev)]
+        for e in evs:
+            e.record(stream)           # creates the underlying HIP event
+        return evs
+
+    def step(evs):
+        moe.moe_layer_forward_traced(prob, dev["x"], dev["w_router"], dev["bias"], dev["w_gate"],
+                                     dev["w_up"], dev["w_down"], dev["ws_gate"], dev["ws_up"],
+                                     dev["ws_down"], y, rb.struct, ws, nbytes, stream, evs)
+
+    warm = new_events()
+    for _ in range(args.warmup):
+        step(warm)
+    step_events = [new_events() for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    print(f"[bench] warmup done, timing {args.steps} steps", file=sys.stderr, flush=True)
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    h0 = time.perf_counter()
+    t_start.record(stream)
+    for i in range(args.steps):
+        step(step_events[i])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    host_s = time.perf_counter() - h0
+    total_ms = t_start.elapsed_time(t_end)
+    stage_ms = np.array([[step_events[i][s].elapsed_time(step_events[i][s + 1])
+                          for s in range(moe.MOE_STAGE_COUNT)] for i in range(args.steps)])
+    stage_avg = stage_ms.mean(axis=0)
+    n_kept = int(rb.offsets[-1].item())
+    work = algorithmic(cfg, n_kept)
+    ms_per_step = total_ms / args.steps
+    value = cfg.T / (ms_per_step * 1e-3)
+
+    if args.pmc_copy:
+        a = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+
+    gu_ms, dn_ms = stage_avg[moe.STAGE_NAMES.index("gate_up")], stage_avg[moe.STAGE_NAMES.index("down")]
+    gu_tf = work["gate_up"] / (gu_ms * 1e-3) / 1e12
+    gemm_tf = (work["gate_up"] + work["down"]) / ((gu_ms + dn_ms) * 1e-3) / 1e12
+    stages = {}
+    for i, name in enumerate(moe.STAGE_NAMES):
+        ent = {"us": round(float(stage_avg[i]) * 1e3, 2)}
+        if name in ("gate_up", "down"):
+            tf = work[name] / (stage_avg[i] * 1e-3) / 1e12
+            ent.update(tflops=round(tf, 1), mfma_frac=round(tf / PEAK_BF16_TFLOPS, 4))
+        else:
+            gbs = work[name] / (stage_avg[i] * 1e-3) / 1e9
+            ent.update(gbs=round(gbs, 1), hbm_frac=round(gbs / PEAK_HBM_GBS, 4))
+        stages[name] = ent
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic (seeded random inputs and random-init weights of the stated shape)",
+        "config": {"workload": f"{cfg.name}: T={cfg.T} d_model={cfg.d_model} E={cfg.E} k={cfg.k} "
+                               f"d_ff={cfg.d_ff} d_ff_shared={cfg.d_ff_shared} routing={cfg.routing} "
+                               f"gamma={cfg.gamma} {cfg.dtype} weights/activations, fp32 router, "
+                               f"y {cfg.y_dtype or cfg.dtype}",
+                   "tokens": cfg.T, "rows_kept": n_kept, "parallelism": "single GPU"},
+        "roofline": {"kernel": "grouped gate/up GEMM + SwiGLU (gemm_bf16_kernel<true>)",
+                     "bound": "mfma", "achieved": round(gu_tf, 1), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(gu_tf / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None},
+        "grouped_gemm_mfma_util": round(gemm_tf / PEAK_BF16_TFLOPS, 4),
+        "stages": stages,
+        "host_s": round(host_s, 4),
+    }
+    if not args.no_cpu_baseline:
+        sample = args.cpu_sample or min(cfg.T, 512)
+        print(f"[bench] cpu baseline: oracle on {sample} tokens", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(inp, sample)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

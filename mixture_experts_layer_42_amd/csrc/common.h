@@ -1,0 +1,106 @@
+// Shared device helpers of the MoE layer kernels (gfx950, wave64).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#define MOE_DEV __device__ __forceinline__
+
+typedef uint16_t bf16_t;   // bfloat16 storage
+
+namespace moe {
+
+constexpr int kWave = 64;
+
+MOE_DEV float bf16_to_f32(bf16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
+
+// round to nearest even; inputs are finite on the hot path, NaN stays NaN
+MOE_DEV bf16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (bf16_t)(u >> 16);
+}
+
+template <typename T> MOE_DEV float to_f32(T v);
+template <> MOE_DEV float to_f32<float>(float v) { return v; }
+template <> MOE_DEV float to_f32<bf16_t>(bf16_t v) { return bf16_to_f32(v); }
+
+template <typename T> MOE_DEV T from_f32(float v);
+template <> MOE_DEV float from_f32<float>(float v) { return v; }
+template <> MOE_DEV bf16_t from_f32<bf16_t>(float v) { return f32_to_bf16(v); }
+
+// order-preserving map float -> uint32 (larger float -> larger key); -0.0 maps like +0.0
+MOE_DEV uint32_t float_key(float f) {
+  if (f == 0.0f) f = 0.0f;
+  uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+MOE_DEV float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+MOE_DEV float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+MOE_DEV int wave_sum_int(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+// inclusive prefix sum over the 64 lanes of a wave
+MOE_DEV int wave_incl_scan(int v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    int n = __shfl_up(v, o, kWave);
+    if (lane >= o) v += n;
+  }
+  return v;
+}
+
+// Block-wide exclusive scan of one int per thread; returns the exclusive prefix and
+// writes the block total to *total. `smem` needs blockDim.x/64 + 1 ints. Contains barriers.
+MOE_DEV int block_excl_scan(int v, int *smem, int *total) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  int inc = wave_incl_scan(v);
+  if (lane == 63) smem[wid] = inc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int run = 0;
+    for (int w = 0; w < nw; ++w) { int t = smem[w]; smem[w] = run; run += t; }
+    smem[nw] = run;
+  }
+  __syncthreads();
+  int res = smem[wid] + inc - v;
+  *total = smem[nw];
+  __syncthreads();
+  return res;
+}
+
+MOE_DEV float block_sum(float v, float *smem) {   // smem: blockDim.x/64 floats; contains barriers
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  v = wave_sum(v);
+  if (lane == 0) smem[wid] = v;
+  __syncthreads();
+  float r = 0.f;
+  for (int w = 0; w < nw; ++w) r += smem[w];      // fixed order: deterministic
+  __syncthreads();
+  return r;
+}
+MOE_DEV float block_max(float v, float *smem) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  v = wave_max(v);
+  if (lane == 0) smem[wid] = v;
+  __syncthreads();
+  float r = smem[0];
+  for (int w = 1; w < nw; ++w) r = fmaxf(r, smem[w]);
+  __syncthreads();
+  return r;
+}
+
+}  // namespace moe

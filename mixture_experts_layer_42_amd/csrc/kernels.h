@@ -1,0 +1,65 @@
+// Internal launch interface between the host layer (moe_api.cpp) and the kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+constexpr int kMaxExperts = 1024;
+constexpr int kMaxGroups = kMaxExperts + 1;   // routed experts + one shared expert
+
+// Workspace regions used by the routing kernels.
+struct RouteScratch {
+  float *keys;          // [T*k] routing score of each pick (capacity drop)
+  int32_t *blk_cnt;     // [nblk*E] per-block per-expert counts
+  int32_t *blk_base;    // [nblk*E] exclusive scan over blocks
+  int32_t *cnt_pre;     // [E] candidates per expert (before the capacity drop)
+  int32_t *off_pre;     // [E+1]
+  int32_t *cand_token;  // [R] candidates grouped by expert
+  int32_t *cand_slot;   // [R]
+  float *cand_key;      // [R]
+  int32_t *slot_pos;    // [T*S] row of (token, slot) or -1; S = k (token choice) or E
+  uint32_t *colkeys;    // [E*T] expert-choice column keys
+  int32_t *tok_blk;     // [nblk] per-block row counts of the token CSR
+  int32_t *tok_blk_off; // [nblk]
+  float *stats_part;    // [nblk*E]
+};
+
+// Grouped GEMM: routed experts (rows from counts/offsets on the device) + optional shared.
+struct GemmArgs {
+  const void *A; int lda;          // routed rows, group e starts at row offsets[e]
+  const void *B0; const void *B1;  // [E, N, K] (B1: up weights for gate/up, else null)
+  void *C; int ldc;
+  const int32_t *counts, *offsets;
+  int E, N, K, elt;                // elt: bytes per A/B element
+  int c_elt;                       // bytes per C element (h: elt; o: 4)
+  const void *sA; const void *sB0; const void *sB1; void *sC;   // shared group
+  int s_rows, sN, sK, s_lda, s_ldc;
+};
+
+hipError_t launch_router(int dtype, const void *x, const float *w, const float *bias,
+                         float *logits, int T, int d, int E, hipStream_t st);
+hipError_t launch_topk(const float *logits, int T, int E, int k, int renorm, int want_key,
+                       int32_t *ids, float *gates, float *keys, hipStream_t st);
+hipError_t launch_token_dispatch(const RouteScratch &s, const int32_t *ids, const float *gates,
+                                 int T, int k, int E, int C, int32_t *perm_token, float *perm_w,
+                                 uint8_t *kept, int32_t *counts, int32_t *offsets,
+                                 hipStream_t st);
+hipError_t launch_expert_choice(const RouteScratch &s, const float *logits, int T, int E, int c,
+                                int32_t *perm_token, float *perm_w, int32_t *counts,
+                                int32_t *offsets, hipStream_t st);
+hipError_t launch_token_csr(const RouteScratch &s, int T, int S, int32_t *tok_ptr,
+                            int32_t *tok_pos, hipStream_t st);
+hipError_t launch_stats(const float *logits, const int32_t *counts, const int32_t *offsets, int T,
+                        int E, int k, int token_choice, float *part, float *out, hipStream_t st);
+hipError_t launch_gather(int elt, const void *x, const int32_t *perm_token,
+                         const int32_t *n_rows_dev, void *x_perm, int d, int max_rows,
+                         int num_cu, hipStream_t st);
+hipError_t launch_combine(int y_elt, const float *o, const float *o_shared,
+                          const int32_t *tok_ptr, const int32_t *tok_pos, const float *perm_w,
+                          void *y, int T, int d, hipStream_t st);
+hipError_t launch_gemm(const GemmArgs &a, bool gate_up, int max_rows, int num_cu,
+                       hipStream_t st);
+hipError_t gemm_setup_attributes();
+
+}  // namespace moe

@@ -1,0 +1,431 @@
+// Host layer of the C ABI: argument validation, workspace layout and launch sequencing.
+// Everything here runs on the host; every check happens before the first enqueue.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <mutex>
+
+#include "../../include/moe.h"
+#include "kernels.h"
+
+using namespace moe;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+size_t up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+struct Layout {
+  // route scratch
+  size_t keys, blk_cnt, blk_base, cnt_pre, off_pre, cand_token, cand_slot, cand_key, slot_pos,
+      colkeys, tok_blk, tok_blk_off, stats_part;
+  // routing arrays used when the caller passes no routing struct
+  size_t logits, ids, topk_w, kept, counts, offsets, perm_token, perm_w, tok_ptr, tok_pos;
+  // activations
+  size_t h, h_shared, x_perm, o_perm, o_shared;
+  size_t total;
+};
+
+int elt_of(const moe_problem &p) { return p.dtype == MOE_BF16 ? 2 : 4; }
+int64_t rows_cap(const moe_problem &p) { return (int64_t)p.T * p.k; }
+int slot_width(const moe_problem &p) { return p.routing == MOE_EXPERT_CHOICE ? p.E : p.k; }
+
+Layout make_layout(const moe_problem &p) {
+  Layout L{};
+  const size_t T = p.T, E = p.E, k = p.k, R = rows_cap(p), d = p.d_model, dff = p.d_ff,
+               dfs = p.d_ff_shared, elt = elt_of(p), S = slot_width(p);
+  const size_t nblk = (T + 255) / 256;
+  size_t o = 0;
+  auto take = [&](size_t bytes) { size_t at = o; o += up(bytes); return at; };
+  L.keys = take(T * k * 4);
+  L.blk_cnt = take(nblk * E * 4);
+  L.blk_base = take(nblk * E * 4);
+  L.cnt_pre = take(E * 4);
+  L.off_pre = take((E + 1) * 4);
+  L.cand_token = take(R * 4);
+  L.cand_slot = take(R * 4);
+  L.cand_key = take(R * 4);
+  L.slot_pos = take(T * S * 4);
+  L.colkeys = take(p.routing == MOE_EXPERT_CHOICE ? E * T * 4 : 0);
+  L.tok_blk = take(nblk * 4);
+  L.tok_blk_off = take(nblk * 4);
+  L.stats_part = take(nblk * E * 4);
+  L.logits = take(T * E * 4);
+  L.ids = take(T * k * 4);
+  L.topk_w = take(T * k * 4);
+  L.kept = take(T * k);
+  L.counts = take(E * 4);
+  L.offsets = take((E + 1) * 4);
+  L.perm_token = take(R * 4);
+  L.perm_w = take(R * 4);
+  L.tok_ptr = take((T + 1) * 4);
+  L.tok_pos = take(R * 4);
+  L.h = take(R * dff * elt);
+  L.h_shared = take(T * dfs * elt);
+  L.x_perm = take(R * d * elt);
+  L.o_perm = take(R * d * 4);
+  L.o_shared = take(dfs > 0 ? T * d * 4 : 0);
+  L.total = o;
+  return L;
+}
+
+bool aligned(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+bool ptr_ok(const void *p) { return p != nullptr && aligned(p); }
+bool opt_ptr_ok(const void *p) { return p == nullptr || aligned(p); }
+
+moe_status check_problem(const moe_problem *pp) {
+  if (!pp) return MOE_ERR_INVALID_ARG;
+  const moe_problem &p = *pp;
+  if (p.T < 1 || p.d_model < 1 || p.E < 1 || p.k < 1 || p.d_ff < 1 || p.d_ff_shared < 0)
+    return MOE_ERR_INVALID_ARG;
+  if (p.k > p.E) return MOE_ERR_INVALID_ARG;
+  if (p.routing != MOE_TOKEN_CHOICE && p.routing != MOE_EXPERT_CHOICE) return MOE_ERR_INVALID_ARG;
+  if (p.dtype != MOE_F32 && p.dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
+  if (p.y_dtype != MOE_F32 && p.y_dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
+  if (p.dtype == MOE_F32 && p.y_dtype != MOE_F32) return MOE_ERR_INVALID_ARG;
+  if (p.renorm_topk != 0 && p.renorm_topk != 1) return MOE_ERR_INVALID_ARG;
+  if (std::isnan(p.gamma) || std::isinf(p.gamma)) return MOE_ERR_INVALID_ARG;
+  if (p.routing == MOE_EXPERT_CHOICE && ((int64_t)p.k * p.T < p.E || p.gamma > 0.f))
+    return MOE_ERR_INVALID_ARG;
+  const int64_t R = rows_cap(p);
+  if (R > INT32_MAX || (int64_t)p.T * p.E > INT32_MAX) return MOE_ERR_INVALID_ARG;
+  if (p.E > kMaxExperts) return MOE_ERR_UNSUPPORTED;
+  if (p.dtype == MOE_BF16) {
+    if (p.d_model % 64 || p.d_ff % 64 || p.d_ff_shared % 64) return MOE_ERR_UNSUPPORTED;
+  } else {
+    if (p.d_model % 4) return MOE_ERR_UNSUPPORTED;
+  }
+  // 32-bit element offsets inside one operand panel
+  const int64_t big = (int64_t)1 << 32;
+  const int64_t wmax = (int64_t)p.d_ff * p.d_model;
+  const int64_t amax = R * (int64_t)(p.d_model > p.d_ff ? p.d_model : p.d_ff);
+  const int64_t smax = (int64_t)p.T * (p.d_model > p.d_ff_shared ? p.d_model : p.d_ff_shared);
+  if (wmax >= big || amax >= big || smax >= big) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+moe_status check_ws(const moe_problem &p, const void *ws, size_t ws_bytes) {
+  if (!ptr_ok(ws)) return MOE_ERR_INVALID_ARG;
+  if (ws_bytes < make_layout(p).total) return MOE_ERR_WORKSPACE;
+  return MOE_OK;
+}
+
+moe_status check_routing_out(const moe_problem &p, const moe_routing *r) {
+  if (!r) return MOE_ERR_INVALID_ARG;
+  if (!ptr_ok(r->logits) || !ptr_ok(r->counts) || !ptr_ok(r->offsets) ||
+      !ptr_ok(r->perm_token) || !ptr_ok(r->perm_w) || !ptr_ok(r->tok_ptr) || !ptr_ok(r->tok_pos))
+    return MOE_ERR_INVALID_ARG;
+  if (p.routing == MOE_TOKEN_CHOICE && (!ptr_ok(r->topk_ids) || !ptr_ok(r->topk_w)))
+    return MOE_ERR_INVALID_ARG;
+  if (!opt_ptr_ok(r->kept)) return MOE_ERR_INVALID_ARG;
+  return MOE_OK;
+}
+
+int num_cus() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
+    return 256;
+  return n;
+}
+
+std::once_flag g_attr_once;
+hipError_t g_attr_err = hipSuccess;
+hipError_t ensure_attributes() {
+  std::call_once(g_attr_once, [] { g_attr_err = gemm_setup_attributes(); });
+  return g_attr_err;
+}
+
+#define MOE_TRY(expr)                                   \
+  do {                                                  \
+    if ((expr) != hipSuccess) return MOE_ERR_HIP;       \
+  } while (0)
+
+RouteScratch scratch_of(const Layout &L, char *ws) {
+  RouteScratch s;
+  s.keys = (float *)(ws + L.keys);
+  s.blk_cnt = (int32_t *)(ws + L.blk_cnt);
+  s.blk_base = (int32_t *)(ws + L.blk_base);
+  s.cnt_pre = (int32_t *)(ws + L.cnt_pre);
+  s.off_pre = (int32_t *)(ws + L.off_pre);
+  s.cand_token = (int32_t *)(ws + L.cand_token);
+  s.cand_slot = (int32_t *)(ws + L.cand_slot);
+  s.cand_key = (float *)(ws + L.cand_key);
+  s.slot_pos = (int32_t *)(ws + L.slot_pos);
+  s.colkeys = (uint32_t *)(ws + L.colkeys);
+  s.tok_blk = (int32_t *)(ws + L.tok_blk);
+  s.tok_blk_off = (int32_t *)(ws + L.tok_blk_off);
+  s.stats_part = (float *)(ws + L.stats_part);
+  return s;
+}
+
+moe_routing internal_routing(const Layout &L, char *ws) {
+  moe_routing r;
+  r.logits = (float *)(ws + L.logits);
+  r.topk_ids = (int32_t *)(ws + L.ids);
+  r.topk_w = (float *)(ws + L.topk_w);
+  r.kept = (uint8_t *)(ws + L.kept);
+  r.counts = (int32_t *)(ws + L.counts);
+  r.offsets = (int32_t *)(ws + L.offsets);
+  r.perm_token = (int32_t *)(ws + L.perm_token);
+  r.perm_w = (float *)(ws + L.perm_w);
+  r.tok_ptr = (int32_t *)(ws + L.tok_ptr);
+  r.tok_pos = (int32_t *)(ws + L.tok_pos);
+  return r;
+}
+
+int capacity_of(const moe_problem &p) {
+  if (!(p.gamma > 0.f)) return -1;
+  const double nbar = (double)p.T * (double)p.k / (double)p.E;
+  return (int)std::floor((double)p.gamma * nbar);
+}
+
+// ---- the four steps, without validation --------------------------------------------------
+
+hipError_t do_route(const moe_problem &p, const void *x, const float *w_router,
+                    const float *bias, int flags, const moe_routing &r, char *ws,
+                    hipStream_t st) {
+  const Layout L = make_layout(p);
+  const RouteScratch s = scratch_of(L, ws);
+  hipError_t e;
+  if (!(flags & MOE_ROUTE_LOGITS_IN)) {
+    e = launch_router(p.dtype == MOE_BF16 ? 1 : 0, x, w_router, bias, r.logits, p.T, p.d_model,
+                      p.E, st);
+    if (e != hipSuccess) return e;
+  }
+  if (p.routing == MOE_TOKEN_CHOICE) {
+    const int C = capacity_of(p);
+    e = launch_topk(r.logits, p.T, p.E, p.k, p.renorm_topk, C >= 0 ? 1 : 0, r.topk_ids, r.topk_w,
+                    s.keys, st);
+    if (e != hipSuccess) return e;
+    e = launch_token_dispatch(s, r.topk_ids, r.topk_w, p.T, p.k, p.E, C, r.perm_token, r.perm_w,
+                              r.kept, r.counts, r.offsets, st);
+    if (e != hipSuccess) return e;
+  } else {
+    const int c = (int)(((int64_t)p.k * p.T) / p.E);
+    e = launch_expert_choice(s, r.logits, p.T, p.E, c, r.perm_token, r.perm_w, r.counts,
+                             r.offsets, st);
+    if (e != hipSuccess) return e;
+  }
+  return launch_token_csr(s, p.T, slot_width(p), r.tok_ptr, r.tok_pos, st);
+}
+
+hipError_t do_dispatch(const moe_problem &p, const void *x, const moe_routing &r, void *x_perm,
+                       hipStream_t st) {
+  return launch_gather(elt_of(p), x, r.perm_token, r.offsets + p.E, x_perm, p.d_model,
+                       (int)rows_cap(p), num_cus(), st);
+}
+
+GemmArgs gemm_args(const moe_problem &p, const moe_routing &r, bool gate_up, const void *a_rows,
+                   const void *w0, const void *w1, void *c_rows, const void *s_a,
+                   const void *s_w0, const void *s_w1, void *s_c) {
+  GemmArgs a{};
+  a.counts = r.counts;
+  a.offsets = r.offsets;
+  a.E = p.E;
+  a.elt = elt_of(p);
+  a.c_elt = gate_up ? a.elt : 4;
+  a.A = a_rows; a.B0 = w0; a.B1 = w1; a.C = c_rows;
+  if (gate_up) {
+    a.N = p.d_ff; a.K = p.d_model; a.lda = p.d_model; a.ldc = p.d_ff;
+  } else {
+    a.N = p.d_model; a.K = p.d_ff; a.lda = p.d_ff; a.ldc = p.d_model;
+  }
+  if (p.d_ff_shared > 0) {
+    a.sA = s_a; a.sB0 = s_w0; a.sB1 = s_w1; a.sC = s_c;
+    a.s_rows = p.T;
+    if (gate_up) {
+      a.sN = p.d_ff_shared; a.sK = p.d_model; a.s_lda = p.d_model; a.s_ldc = p.d_ff_shared;
+    } else {
+      a.sN = p.d_model; a.sK = p.d_ff_shared; a.s_lda = p.d_ff_shared; a.s_ldc = p.d_model;
+    }
+  }
+  return a;
+}
+
+hipError_t do_gate_up(const moe_problem &p, const void *x_perm, const moe_routing &r,
+                      const void *w_gate, const void *w_up, const void *x, const void *ws_gate,
+                      const void *ws_up, char *ws, hipStream_t st) {
+  const Layout L = make_layout(p);
+  const GemmArgs a = gemm_args(p, r, true, x_perm, w_gate, w_up, ws + L.h, x, ws_gate, ws_up,
+                               ws + L.h_shared);
+  return launch_gemm(a, true, (int)rows_cap(p), num_cus(), st);
+}
+
+hipError_t do_down(const moe_problem &p, const moe_routing &r, const void *w_down,
+                   const void *ws_down, void *o_perm, void *o_shared, char *ws, hipStream_t st) {
+  const Layout L = make_layout(p);
+  const GemmArgs a = gemm_args(p, r, false, ws + L.h, w_down, nullptr, o_perm, ws + L.h_shared,
+                               ws_down, nullptr, o_shared);
+  return launch_gemm(a, false, (int)rows_cap(p), num_cus(), st);
+}
+
+hipError_t do_combine(const moe_problem &p, const void *o_perm, const void *o_shared,
+                      const moe_routing &r, void *y, hipStream_t st) {
+  return launch_combine(p.y_dtype == MOE_BF16 ? 2 : 4, (const float *)o_perm,
+                        p.d_ff_shared > 0 ? (const float *)o_shared : nullptr, r.tok_ptr,
+                        r.tok_pos, r.perm_w, y, p.T, p.d_model, st);
+}
+
+moe_status layer_forward(const moe_problem *pp, const void *x, const float *w_router,
+                         const float *bias, const void *w_gate, const void *w_up,
+                         const void *w_down, const void *ws_gate, const void *ws_up,
+                         const void *ws_down, void *y, moe_routing *routing, void *ws,
+                         size_t ws_bytes, hipStream_t st, hipEvent_t *ev) {
+  moe_status s = check_problem(pp);
+  if (s != MOE_OK) return s;
+  const moe_problem &p = *pp;
+  if (!ptr_ok(x) || !ptr_ok(w_router) || !opt_ptr_ok(bias) || !ptr_ok(w_gate) || !ptr_ok(w_up) ||
+      !ptr_ok(w_down) || !ptr_ok(y))
+    return MOE_ERR_INVALID_ARG;
+  if (p.d_ff_shared > 0 && (!ptr_ok(ws_gate) || !ptr_ok(ws_up) || !ptr_ok(ws_down)))
+    return MOE_ERR_INVALID_ARG;
+  if ((s = check_ws(p, ws, ws_bytes)) != MOE_OK) return s;
+  char *w = (char *)ws;
+  const Layout L = make_layout(p);
+  moe_routing r = routing ? *routing : internal_routing(L, w);
+  if (routing && (s = check_routing_out(p, routing)) != MOE_OK) return s;
+  if (ensure_attributes() != hipSuccess) return MOE_ERR_HIP;
+  auto mark = [&](int i) { return ev ? hipEventRecord(ev[i], st) : hipSuccess; };
+  MOE_TRY(mark(MOE_STAGE_ROUTE));
+  MOE_TRY(do_route(p, x, w_router, bias, 0, r, w, st));
+  MOE_TRY(mark(MOE_STAGE_DISPATCH));
+  MOE_TRY(do_dispatch(p, x, r, w + L.x_perm, st));
+  MOE_TRY(mark(MOE_STAGE_GATE_UP));
+  MOE_TRY(do_gate_up(p, w + L.x_perm, r, w_gate, w_up, x, ws_gate, ws_up, w, st));
+  MOE_TRY(mark(MOE_STAGE_DOWN));
+  MOE_TRY(do_down(p, r, w_down, ws_down, w + L.o_perm, w + L.o_shared, w, st));
+  MOE_TRY(mark(MOE_STAGE_COMBINE));
+  MOE_TRY(do_combine(p, w + L.o_perm, w + L.o_shared, r, y, st));
+  MOE_TRY(mark(MOE_STAGE_COUNT));
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_workspace_bytes(const moe_problem *problem, size_t *bytes) {
+  moe_status s = check_problem(problem);
+  if (s != MOE_OK) return s;
+  if (!bytes) return MOE_ERR_INVALID_ARG;
+  *bytes = make_layout(*problem).total;
+  return MOE_OK;
+}
+
+moe_status moe_route(const moe_problem *problem, const void *x, const float *w_router,
+                     const float *bias, int flags, moe_routing *routing, void *ws,
+                     size_t ws_bytes, hipStream_t stream) {
+  moe_status s = check_problem(problem);
+  if (s != MOE_OK) return s;
+  const moe_problem &p = *problem;
+  if (flags & ~MOE_ROUTE_LOGITS_IN) return MOE_ERR_INVALID_ARG;
+  if (!(flags & MOE_ROUTE_LOGITS_IN) && (!ptr_ok(x) || !ptr_ok(w_router) || !opt_ptr_ok(bias)))
+    return MOE_ERR_INVALID_ARG;
+  if ((s = check_routing_out(p, routing)) != MOE_OK) return s;
+  if ((s = check_ws(p, ws, ws_bytes)) != MOE_OK) return s;
+  if (do_route(p, x, w_router, bias, flags, *routing, (char *)ws, stream) != hipSuccess)
+    return MOE_ERR_HIP;
+  return MOE_OK;
+}
+
+moe_status moe_dispatch(const moe_problem *problem, const void *x, const moe_routing *routing,
+                        void *x_perm, hipStream_t stream) {
+  moe_status s = check_problem(problem);
+  if (s != MOE_OK) return s;
+  if (!ptr_ok(x) || !ptr_ok(x_perm) || !routing || !ptr_ok(routing->perm_token) ||
+      !ptr_ok(routing->offsets))
+    return MOE_ERR_INVALID_ARG;
+  if (do_dispatch(*problem, x, *routing, x_perm, stream) != hipSuccess) return MOE_ERR_HIP;
+  return MOE_OK;
+}
+
+moe_status moe_expert_ffn(const moe_problem *problem, const void *x_perm,
+                          const moe_routing *routing, const void *w_gate, const void *w_up,
+                          const void *w_down, const void *x, const void *ws_gate,
+                          const void *ws_up, const void *ws_down, void *o_perm, void *o_shared,
+                          void *ws, size_t ws_bytes, hipStream_t stream) {
+  moe_status s = check_problem(problem);
+  if (s != MOE_OK) return s;
+  const moe_problem &p = *problem;
+  if (!ptr_ok(x_perm) || !routing || !ptr_ok(routing->counts) || !ptr_ok(routing->offsets) ||
+      !ptr_ok(w_gate) || !ptr_ok(w_up) || !ptr_ok(w_down) || !ptr_ok(o_perm))
+    return MOE_ERR_INVALID_ARG;
+  if (p.d_ff_shared > 0 && (!ptr_ok(x) || !ptr_ok(ws_gate) || !ptr_ok(ws_up) ||
+                            !ptr_ok(ws_down) || !ptr_ok(o_shared)))
+    return MOE_ERR_INVALID_ARG;
+  if ((s = check_ws(p, ws, ws_bytes)) != MOE_OK) return s;
+  if (ensure_attributes() != hipSuccess) return MOE_ERR_HIP;
+  char *w = (char *)ws;
+  if (do_gate_up(p, x_perm, *routing, w_gate, w_up, x, ws_gate, ws_up, w, stream) != hipSuccess)
+    return MOE_ERR_HIP;
+  if (do_down(p, *routing, w_down, ws_down, o_perm, o_shared, w, stream) != hipSuccess)
+    return MOE_ERR_HIP;
+  return MOE_OK;
+}
+
+moe_status moe_combine(const moe_problem *problem, const void *o_perm, const void *o_shared,
+                       const moe_routing *routing, void *y, hipStream_t stream) {
+  moe_status s = check_problem(problem);
+  if (s != MOE_OK) return s;
+  const moe_problem &p = *problem;
+  if (!ptr_ok(o_perm) || !ptr_ok(y) || !routing || !ptr_ok(routing->tok_ptr) ||
+      !ptr_ok(routing->tok_pos) || !ptr_ok(routing->perm_w))
+    return MOE_ERR_INVALID_ARG;
+  if (p.d_ff_shared > 0 && !ptr_ok(o_shared)) return MOE_ERR_INVALID_ARG;
+  if (do_combine(p, o_perm, o_shared, *routing, y, stream) != hipSuccess) return MOE_ERR_HIP;
+  return MOE_OK;
+}
+
+moe_status moe_layer_forward(const moe_problem *problem, const void *x, const float *w_router,
+                             const float *bias, const void *w_gate, const void *w_up,
+                             const void *w_down, const void *ws_gate, const void *ws_up,
+                             const void *ws_down, void *y, moe_routing *routing, void *ws,
+                             size_t ws_bytes, hipStream_t stream) {
+  return layer_forward(problem, x, w_router, bias, w_gate, w_up, w_down, ws_gate, ws_up, ws_down,
+                       y, routing, ws, ws_bytes, stream, nullptr);
+}
+
+moe_status moe_layer_forward_traced(const moe_problem *problem, const void *x,
+                                    const float *w_router, const float *bias,
+                                    const void *w_gate, const void *w_up, const void *w_down,
+                                    const void *ws_gate, const void *ws_up, const void *ws_down,
+                                    void *y, moe_routing *routing, void *ws, size_t ws_bytes,
+                                    hipStream_t stream, hipEvent_t *events, int n_events) {
+  if (!events || n_events != MOE_STAGE_COUNT + 1) return MOE_ERR_INVALID_ARG;
+  for (int i = 0; i < n_events; ++i)
+    if (!events[i]) return MOE_ERR_INVALID_ARG;
+  return layer_forward(problem, x, w_router, bias, w_gate, w_up, w_down, ws_gate, ws_up, ws_down,
+                       y, routing, ws, ws_bytes, stream, events);
+}
+
+moe_status moe_routing_stats(const moe_problem *problem, const moe_routing *routing, float *out,
+                             void *ws, size_t ws_bytes, hipStream_t stream) {
+  moe_status s = check_problem(problem);
+  if (s != MOE_OK) return s;
+  const moe_problem &p = *problem;
+  if (!routing || !ptr_ok(routing->logits) || !ptr_ok(routing->counts) ||
+      !ptr_ok(routing->offsets) || !ptr_ok(out))
+    return MOE_ERR_INVALID_ARG;
+  if ((s = check_ws(p, ws, ws_bytes)) != MOE_OK) return s;
+  const Layout L = make_layout(p);
+  if (launch_stats(routing->logits, routing->counts, routing->offsets, p.T, p.E, p.k,
+                   p.routing == MOE_TOKEN_CHOICE ? 1 : 0,
+                   (float *)((char *)ws + L.stats_part), out, stream) != hipSuccess)
+    return MOE_ERR_HIP;
+  return MOE_OK;
+}
+
+const char *moe_status_str(moe_status status) {
+  switch (status) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG: invalid shape, pointer or enum";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED: valid problem without a kernel";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE: workspace smaller than moe_workspace_bytes";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP: a HIP call failed";
+  }
+  return "unknown moe_status";
+}
+
+}  // extern "C"

@@ -1,0 +1,742 @@
+// Router, selection and dispatch-index kernels of the sparse MoE layer (gfx950).
+//
+// Steps (problem statement of the pages: T tokens, E experts, top-k, capacity gamma):
+//   router          l[t,e] = sum_j x[t,j] W_r[j,e] + b[e]                       (fp32)
+//   token choice    k largest logits per token, ties to the lower expert; gates =
+//                   softmax over all E renormalised over the picks
+//   capacity drop   C = floor(gamma*T*k/E); per expert keep the C candidates with the
+//                   highest routing score p32 (ties to the lower token)
+//   expert choice   c = floor(k*T/E) largest logits per expert column, ties to the
+//                   lower token; weight = softmax over the column's T tokens
+//   dispatch        per-expert histogram -> exclusive scan -> stable permutation
+//                   (ascending token inside an expert), CSR token -> rows
+// Integer decisions never depend on summation order or atomics: histograms are
+// built from bit masks and popcounts, positions from prefix scans.
+#include "common.h"
+#include "kernels.h"
+
+#pragma clang fp contract(off)
+
+namespace moe {
+
+// ----------------------------------------------------------------------------------------
+// Routing score p32: Cody & Waite exponential (W. J. Cody, W. Waite, Software Manual for
+// the Elementary Functions, 1980) on float32 with every operation rounded separately:
+// n = rint(x*log2 e); r = (x - n*LN2_HI) - n*LN2_LO with LN2_HI holding only the top 15
+// significant bits of ln 2 (so n*LN2_HI is exact); exp(r) from its degree-7 Taylor
+// polynomial as 1 + (r + r*(r*(1/2! + r*(1/3! + ... + r/7!)))); times 2^n built in the
+// exponent field. Inputs below -87 give +0. Constants are the float32 roundings of
+// log2(e), ln 2 (split), and 1/i!.
+MOE_DEV float rexp_spec(float x) {
+#pragma clang fp contract(off)
+  const float kLog2e = 0x1.715476p+0f;
+  const float kLn2Hi = 0x1.62e4p-1f;
+  const float kLn2Lo = 0x1.7f7d1cp-20f;
+  const float c2 = 0x1.0p-1f, c3 = 0x1.555556p-3f, c4 = 0x1.555556p-5f, c5 = 0x1.111112p-7f,
+              c6 = 0x1.6c16c2p-10f, c7 = 0x1.a01a02p-13f;
+  if (x < -87.0f) return 0.0f;
+  float n = __builtin_rintf(__fmul_rn(x, kLog2e));
+  float r = __fsub_rn(__fsub_rn(x, __fmul_rn(n, kLn2Hi)), __fmul_rn(n, kLn2Lo));
+  float p = c7;
+  p = __fadd_rn(__fmul_rn(p, r), c6);
+  p = __fadd_rn(__fmul_rn(p, r), c5);
+  p = __fadd_rn(__fmul_rn(p, r), c4);
+  p = __fadd_rn(__fmul_rn(p, r), c3);
+  p = __fadd_rn(__fmul_rn(p, r), c2);
+  p = __fmul_rn(p, r);
+  p = __fmul_rn(p, r);
+  p = __fadd_rn(p, r);
+  p = __fadd_rn(p, 1.0f);
+  const float scale = __uint_as_float((uint32_t)((int)n + 127) << 23);
+  return __fmul_rn(p, scale);
+}
+
+// ----------------------------------------------------------------------------------------
+// Router, E <= 8. One workgroup = 4 waves handles 8 tokens; wave w covers one quarter of
+// d_model, lane l the VEC consecutive columns l*VEC (+ 64*VEC steps). Each lane keeps
+// 8 tokens x 8 experts partial sums, a butterfly reduce-scatter leaves lane L with the
+// (token L/8, expert L%8) sum of its wave, and the 4 quarter sums are added in order.
+template <typename XT>
+__global__ __launch_bounds__(256) void router_narrow_kernel(const XT *__restrict__ x,
+                                                            const float *__restrict__ w,
+                                                            const float *__restrict__ bias,
+                                                            float *__restrict__ logits, int T,
+                                                            int d, int E) {
+  constexpr int VEC = 16 / sizeof(XT);
+  constexpr int TOK = 8, EP = 8;
+  __shared__ float part[4][64];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int t0 = blockIdx.x * TOK;
+  // quarter of d handled by this wave, multiple of VEC
+  const int q = ((d + 4 * VEC - 1) / (4 * VEC)) * VEC;
+  const int jb = wv * q, je = min(d, jb + q);
+  float acc[TOK][EP];
+#pragma unroll
+  for (int i = 0; i < TOK; ++i)
+#pragma unroll
+    for (int e = 0; e < EP; ++e) acc[i][e] = 0.f;
+
+  for (int j0 = jb + lane * VEC; j0 < je; j0 += 64 * VEC) {
+    float wv8[VEC][EP];
+    const bool full = (j0 + VEC <= je);
+    if (E == 8 && full) {
+#pragma unroll
+      for (int v = 0; v < VEC; ++v) {
+        const float4 *wp = reinterpret_cast<const float4 *>(w + (size_t)(j0 + v) * 8);
+        float4 a = wp[0], b = wp[1];
+        wv8[v][0] = a.x; wv8[v][1] = a.y; wv8[v][2] = a.z; wv8[v][3] = a.w;
+        wv8[v][4] = b.x; wv8[v][5] = b.y; wv8[v][6] = b.z; wv8[v][7] = b.w;
+      }
+    } else {
+#pragma unroll
+      for (int v = 0; v < VEC; ++v)
+#pragma unroll
+        for (int e = 0; e < EP; ++e)
+          wv8[v][e] = (j0 + v < je && e < E) ? w[(size_t)(j0 + v) * E + e] : 0.f;
+    }
+#pragma unroll
+    for (int i = 0; i < TOK; ++i) {
+      const int t = t0 + i;
+      float xv[VEC];
+      if (t < T && full) {
+        const XT *xp = x + (size_t)t * d + j0;
+        if constexpr (sizeof(XT) == 2) {
+          uint4 raw = *reinterpret_cast<const uint4 *>(xp);
+          uint32_t r4[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            xv[2 * v] = __uint_as_float(r4[v] << 16);
+            xv[2 * v + 1] = __uint_as_float(r4[v] & 0xffff0000u);
+          }
+        } else {
+          float4 raw = *reinterpret_cast<const float4 *>(xp);
+          xv[0] = raw.x; xv[1] = raw.y; xv[2] = raw.z; xv[3] = raw.w;
+        }
+      } else {
+#pragma unroll
+        for (int v = 0; v < VEC; ++v)
+          xv[v] = (t < T && j0 + v < je) ? to_f32<XT>(x[(size_t)t * d + j0 + v]) : 0.f;
+      }
+#pragma unroll
+      for (int v = 0; v < VEC; ++v)
+#pragma unroll
+        for (int e = 0; e < EP; ++e) acc[i][e] = fmaf(xv[v], wv8[v][e], acc[i][e]);
+    }
+  }
+  // butterfly reduce-scatter of the 64 (token, expert) sums across the wave
+  float v[64];
+#pragma unroll
+  for (int i = 0; i < 64; ++i) v[i] = acc[i / EP][i % EP];
+#pragma unroll
+  for (int o = 32, n = 64; o > 0; o >>= 1, n >>= 1) {
+    const bool up = (lane & o) != 0;
+#pragma unroll
+    for (int i = 0; i < n / 2; ++i) {
+      float send = up ? v[i] : v[i + n / 2];
+      float keep = up ? v[i + n / 2] : v[i];
+      v[i] = keep + __shfl_xor(send, o, 64);
+    }
+  }
+  part[wv][lane] = v[0];
+  __syncthreads();
+  if (wv == 0) {
+    const int t = t0 + lane / EP, e = lane % EP;
+    float s = ((part[0][lane] + part[1][lane]) + part[2][lane]) + part[3][lane];
+    if (t < T && e < E) logits[(size_t)t * E + e] = s + (bias ? bias[e] : 0.f);
+  }
+}
+
+// ----------------------------------------------------------------------------------------
+// Router, E > 8. One workgroup = 4 waves handles 64 tokens x up to 128 experts (grid.y
+// walks expert blocks of 128). x and W_r tiles of 64 columns are staged in LDS; lane l
+// owns experts l and l+64, wave w tokens w*16..w*16+15. Each 64-column chunk is summed
+// into a fresh partial before being added to the total (two-level float32 sum).
+template <typename XT>
+__global__ __launch_bounds__(256) void router_wide_kernel(const XT *__restrict__ x,
+                                                          const float *__restrict__ w,
+                                                          const float *__restrict__ bias,
+                                                          float *__restrict__ logits, int T, int d,
+                                                          int E) {
+  constexpr int TT = 64, BK = 64, TW = 16;
+  __shared__ float xs[TT][BK + 4];
+  __shared__ float ws[BK][128];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int t0 = blockIdx.x * TT, e0 = blockIdx.y * 128;
+  float acc[TW][2], part[TW][2];
+#pragma unroll
+  for (int i = 0; i < TW; ++i) acc[i][0] = acc[i][1] = 0.f;
+  for (int k0 = 0; k0 < d; k0 += BK) {
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < TT * BK; idx += 256) {
+      const int r = idx / BK, c = idx % BK, t = t0 + r, j = k0 + c;
+      xs[r][c] = (t < T && j < d) ? to_f32<XT>(x[(size_t)t * d + j]) : 0.f;
+    }
+    for (int idx = threadIdx.x; idx < BK * 128; idx += 256) {
+      const int r = idx / 128, c = idx % 128, j = k0 + r, e = e0 + c;
+      ws[r][c] = (j < d && e < E) ? w[(size_t)j * E + e] : 0.f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < TW; ++i) part[i][0] = part[i][1] = 0.f;
+    for (int c = 0; c < BK; c += 4) {
+      float w0[4], w1[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) { w0[u] = ws[c + u][lane]; w1[u] = ws[c + u][lane + 64]; }
+#pragma unroll
+      for (int i = 0; i < TW; ++i) {
+        const float4 xv = *reinterpret_cast<const float4 *>(&xs[wv * TW + i][c]);
+        part[i][0] = fmaf(xv.x, w0[0], part[i][0]); part[i][1] = fmaf(xv.x, w1[0], part[i][1]);
+        part[i][0] = fmaf(xv.y, w0[1], part[i][0]); part[i][1] = fmaf(xv.y, w1[1], part[i][1]);
+        part[i][0] = fmaf(xv.z, w0[2], part[i][0]); part[i][1] = fmaf(xv.z, w1[2], part[i][1]);
+        part[i][0] = fmaf(xv.w, w0[3], part[i][0]); part[i][1] = fmaf(xv.w, w1[3], part[i][1]);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < TW; ++i) { acc[i][0] += part[i][0]; acc[i][1] += part[i][1]; }
+  }
+#pragma unroll
+  for (int i = 0; i < TW; ++i) {
+    const int t = t0 + wv * TW + i;
+    if (t >= T) continue;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int e = e0 + lane + 64 * h;
+      if (e < E) logits[(size_t)t * E + e] = acc[i][h] + (bias ? bias[e] : 0.f);
+    }
+  }
+}
+
+// ----------------------------------------------------------------------------------------
+// Token-choice top-k. A group of G lanes (G = power of two >= min(E, 64)) handles one
+// token; lane i of the group holds experts i, i+G, i+2G, ... Each round takes the group
+// maximum (ties: lower expert index). Gates: exp(l - max) normalised over the picks (or
+// over all E). With a capacity limit the float32 routing score of each pick is written:
+// q_e = rexp_spec(l_e - max), S = q_0 + q_1 + ... left to right, p32 = q_e / S.
+template <int G>
+__global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ logits, int T, int E,
+                                                   int k, int renorm, int want_key,
+                                                   int32_t *__restrict__ ids,
+                                                   float *__restrict__ gates,
+                                                   float *__restrict__ keys) {
+  extern __shared__ float qsh[];   // [256/G][E] when want_key
+  const int gl = threadIdx.x % G, gi = threadIdx.x / G;
+  const int t = blockIdx.x * (256 / G) + gi;
+  const bool live = t < T;
+  const int npl = (E + G - 1) / G;
+  constexpr int MAXPL = (G < 64) ? 1 : kMaxExperts / 64;   // E <= G for G < 64
+  float lv[MAXPL];
+  uint32_t taken = 0u;
+#pragma unroll
+  for (int i = 0; i < MAXPL; ++i) {
+    const int e = gl + i * G;
+    lv[i] = (live && i < npl && e < E) ? logits[(size_t)t * E + e] : -INFINITY;
+  }
+  float mx = 0.f, qsum = 0.f;
+  for (int r = 0; r < k; ++r) {
+    float bv = -INFINITY;
+    int be = 0x7fffffff;
+#pragma unroll
+    for (int i = 0; i < MAXPL; ++i) {
+      const int e = gl + i * G;
+      if (i < npl && e < E && !((taken >> i) & 1u)) {
+        const float v = lv[i];
+        if (v > bv || (v == bv && e < be) || be == 0x7fffffff) { bv = v; be = e; }
+      }
+    }
+#pragma unroll
+    for (int o = G / 2; o > 0; o >>= 1) {
+      const float ov = __shfl_xor(bv, o, 64);
+      const int oe = __shfl_xor(be, o, 64);
+      if (ov > bv || (ov == bv && oe < be)) { bv = ov; be = oe; }
+    }
+    if (r == 0) mx = bv;
+    if ((be % G) == gl) taken |= 1u << (be / G);
+    const float q = expf(bv - mx);
+    qsum += q;
+    if (gl == 0 && live) {
+      ids[(size_t)t * k + r] = be;
+      gates[(size_t)t * k + r] = q;   // numerator for now
+    }
+  }
+  float denom = qsum;
+  if (!renorm) {
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < MAXPL; ++i) {
+      const int e = gl + i * G;
+      if (i < npl && e < E) s += expf(lv[i] - mx);
+    }
+#pragma unroll
+    for (int o = G / 2; o > 0; o >>= 1) s += __shfl_xor(s, o, 64);
+    denom = s;
+  }
+  if (gl == 0 && live) {
+    for (int r = 0; r < k; ++r) gates[(size_t)t * k + r] = gates[(size_t)t * k + r] / denom;
+  }
+  if (want_key) {
+    float *qrow = qsh + gi * E;
+#pragma unroll
+    for (int i = 0; i < MAXPL; ++i) {
+      const int e = gl + i * G;
+      if (i < npl && e < E) qrow[e] = live ? rexp_spec(__fsub_rn(lv[i], mx)) : 0.f;
+    }
+    __syncthreads();
+    if (gl == 0 && live) {
+      float S = qrow[0];
+      for (int e = 1; e < E; ++e) S = __fadd_rn(S, qrow[e]);
+      for (int r = 0; r < k; ++r) {
+        const int e = ids[(size_t)t * k + r];
+        keys[(size_t)t * k + r] = qrow[e] / S;
+      }
+    }
+  }
+}
+
+// ----------------------------------------------------------------------------------------
+// Dispatch histogram. Block b owns tokens [256b, 256b+256). For every expert a 256-bit
+// mask marks the block's tokens that chose it (LDS atomicOr of distinct bits, order free);
+// popcounts give the block's per-expert counts and, in the scatter, each pair's rank.
+MOE_DEV void build_masks(uint32_t *mask, const int32_t *ids, const uint8_t *kept, int T, int k,
+                         int E) {
+  for (int i = threadIdx.x; i < E * 8; i += blockDim.x) mask[i] = 0u;
+  __syncthreads();
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  if (t < T) {
+    for (int j = 0; j < k; ++j) {
+      if (kept && !kept[(size_t)t * k + j]) continue;
+      const int e = ids[(size_t)t * k + j];
+      atomicOr(&mask[e * 8 + (threadIdx.x >> 5)], 1u << (threadIdx.x & 31));
+    }
+  }
+  __syncthreads();
+}
+
+__global__ __launch_bounds__(256) void assign_count_kernel(const int32_t *__restrict__ ids, int T,
+                                                           int k, int E,
+                                                           int32_t *__restrict__ blk_cnt) {
+  extern __shared__ uint32_t mask[];
+  build_masks(mask, ids, nullptr, T, k, E);
+  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+    int c = 0;
+#pragma unroll
+    for (int w = 0; w < 8; ++w) c += __popc(mask[e * 8 + w]);
+    blk_cnt[(size_t)blockIdx.x * E + e] = c;
+  }
+}
+
+// Column scans of the block counts (one thread per expert, blocks in order), expert
+// totals, exclusive scan over experts. With a capacity C >= 0 the kept counts are
+// min(count, C) and a second offset table is produced for them.
+__global__ __launch_bounds__(1024) void assign_scan_kernel(const int32_t *__restrict__ blk_cnt,
+                                                           int nblk, int E, int C,
+                                                           int32_t *__restrict__ blk_base,
+                                                           int32_t *__restrict__ cnt_pre,
+                                                           int32_t *__restrict__ off_pre,
+                                                           int32_t *__restrict__ cnt_fin,
+                                                           int32_t *__restrict__ off_fin) {
+  __shared__ int sm[1024 / 64 + 1];
+  const int e = threadIdx.x;
+  int run = 0;
+  if (e < E) {
+    for (int b = 0; b < nblk; ++b) {
+      const int c = blk_cnt[(size_t)b * E + e];
+      blk_base[(size_t)b * E + e] = run;
+      run += c;
+    }
+    cnt_pre[e] = run;
+  }
+  int tot;
+  const int ex = block_excl_scan(e < E ? run : 0, sm, &tot);
+  if (e < E) off_pre[e] = ex;
+  if (e == 0) off_pre[E] = tot;
+  if (C >= 0) {
+    const int kc = (e < E) ? min(run, C) : 0;
+    const int ex2 = block_excl_scan(kc, sm, &tot);
+    if (e < E) { cnt_fin[e] = kc; off_fin[e] = ex2; }
+    if (e == 0) off_fin[E] = tot;
+  }
+}
+
+// Stable scatter: pair (t, j) of expert e goes to off[e] + blk_base[b][e] + (number of the
+// block's tokens before t that chose e). Without capacity the final arrays are written;
+// with capacity the candidate arrays (token, slot, key) that cap_select reads.
+__global__ __launch_bounds__(256) void assign_scatter_kernel(
+    const int32_t *__restrict__ ids, const float *__restrict__ gates,
+    const float *__restrict__ keys, int T, int k, int E, const int32_t *__restrict__ off,
+    const int32_t *__restrict__ blk_base, int candidates, int32_t *__restrict__ out_token,
+    float *__restrict__ out_w, int32_t *__restrict__ out_slot, float *__restrict__ out_key,
+    int32_t *__restrict__ slot_pos, uint8_t *__restrict__ kept) {
+  extern __shared__ uint32_t mask[];
+  build_masks(mask, ids, nullptr, T, k, E);
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  if (t >= T) return;
+  const int word = threadIdx.x >> 5, bit = threadIdx.x & 31;
+  for (int j = 0; j < k; ++j) {
+    const int e = ids[(size_t)t * k + j];
+    int rank = __popc(mask[e * 8 + word] & ((1u << bit) - 1u));
+    for (int w = 0; w < word; ++w) rank += __popc(mask[e * 8 + w]);
+    const int pos = off[e] + blk_base[(size_t)blockIdx.x * E + e] + rank;
+    if (candidates) {
+      out_token[pos] = t;
+      out_slot[pos] = j;
+      out_key[pos] = keys[(size_t)t * k + j];
+    } else {
+      out_token[pos] = t;
+      out_w[pos] = gates[(size_t)t * k + j];
+      slot_pos[(size_t)t * k + j] = pos;
+      if (kept) kept[(size_t)t * k + j] = 1;
+    }
+  }
+}
+
+// ----------------------------------------------------------------------------------------
+// Block-wide radix selection (1024 threads): among n uint32 keys, find the want-th largest
+// value tau and how many keys equal to tau are needed (need_eq) so that
+// {u > tau} + (first need_eq of {u == tau}) is exactly the top `want`. Histograms of one
+// byte per pass (LDS integer adds: the counts do not depend on order).
+struct SelectResult { uint32_t tau; int need_eq; };
+
+template <typename GetKey>
+MOE_DEV SelectResult block_radix_select(GetKey get, int n, int want, int *hist, int *sm) {
+  uint32_t prefix = 0u, pmask = 0u;
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    for (int i = threadIdx.x; i < 256; i += blockDim.x) hist[i] = 0;
+    __syncthreads();
+    for (int i = threadIdx.x; i < n; i += blockDim.x) {
+      const uint32_t u = get(i);
+      if ((u & pmask) == prefix) atomicAdd(&hist[(u >> shift) & 255u], 1);
+    }
+    __syncthreads();
+    // thread b looks at bin 255-b: inclusive scan from the top bin down
+    const int b = threadIdx.x;
+    const int h = (b < 256) ? hist[255 - b] : 0;
+    int tot;
+    const int ex = block_excl_scan(h, sm, &tot);
+    __shared__ int pick[2];
+    if (b < 256 && ex < want && want <= ex + h) { pick[0] = 255 - b; pick[1] = want - ex; }
+    __syncthreads();
+    prefix |= ((uint32_t)pick[0]) << shift;
+    pmask |= 255u << shift;
+    want = pick[1];
+    __syncthreads();
+  }
+  return SelectResult{prefix, want};
+}
+
+// Capacity-aware token drop, one workgroup per expert. The candidates of expert e sit in
+// ascending token order at [off_pre[e], off_pre[e] + cnt); if more than C, the C with the
+// largest (key, then lower token) stay. Survivors keep their order and go to off_fin[e] + rank.
+__global__ __launch_bounds__(1024) void cap_select_kernel(
+    const int32_t *__restrict__ cand_token, const int32_t *__restrict__ cand_slot,
+    const float *__restrict__ cand_key, const int32_t *__restrict__ cnt_pre,
+    const int32_t *__restrict__ off_pre, const int32_t *__restrict__ off_fin, int C, int k,
+    const float *__restrict__ gates, int32_t *__restrict__ perm_token,
+    float *__restrict__ perm_w, int32_t *__restrict__ slot_pos, uint8_t *__restrict__ kept) {
+  __shared__ int hist[256];
+  __shared__ int sm[1024 / 64 + 1];
+  const int e = blockIdx.x;
+  const int n = cnt_pre[e], base = off_pre[e], obase = off_fin[e];
+  // C == 0 keeps nothing: a threshold above every finite key
+  SelectResult sr{0xffffffffu, 0};
+  const bool drop = n > C;
+  if (drop && C > 0) {
+    auto get = [&](int i) { return float_key(cand_key[base + i]); };
+    sr = block_radix_select(get, n, C, hist, sm);
+  }
+  int run_eq = 0, run_sel = 0;
+  for (int c0 = 0; c0 < n; c0 += blockDim.x) {
+    const int i = c0 + threadIdx.x;
+    const bool in = i < n;
+    uint32_t u = 0u;
+    if (in && drop) u = float_key(cand_key[base + i]);
+    const int eqf = (in && drop && u == sr.tau) ? 1 : 0;
+    int tot;
+    const int eq_rank = run_eq + block_excl_scan(eqf, sm, &tot);
+    run_eq += tot;
+    const int self = in && (!drop || u > sr.tau || (eqf && eq_rank < sr.need_eq)) ? 1 : 0;
+    const int rank = run_sel + block_excl_scan(self, sm, &tot);
+    run_sel += tot;
+    if (in) {
+      const int t = cand_token[base + i], j = cand_slot[base + i];
+      if (self) {
+        const int q = obase + rank;
+        perm_token[q] = t;
+        perm_w[q] = gates[(size_t)t * k + j];
+        slot_pos[(size_t)t * k + j] = q;
+      } else {
+        slot_pos[(size_t)t * k + j] = -1;
+      }
+      if (kept) kept[(size_t)t * k + j] = (uint8_t)self;
+    }
+  }
+}
+
+// Expert choice, one workgroup per expert: column max and softmax denominator over all T
+// tokens, radix selection of the c largest logits (ties: lower token), then an ordered
+// compaction so that the expert's rows hold its tokens in ascending order.
+__global__ __launch_bounds__(1024) void ec_select_kernel(const float *__restrict__ logits, int T,
+                                                         int E, int c,
+                                                         uint32_t *__restrict__ colkeys,
+                                                         int32_t *__restrict__ perm_token,
+                                                         float *__restrict__ perm_w,
+                                                         int32_t *__restrict__ slot_pos,
+                                                         int32_t *__restrict__ counts,
+                                                         int32_t *__restrict__ offsets) {
+  __shared__ int hist[256];
+  __shared__ int sm[1024 / 64 + 1];
+  __shared__ float fsm[1024 / 64];
+  const int e = blockIdx.x;
+  uint32_t *keys = colkeys + (size_t)e * T;
+  float mx = -INFINITY;
+  for (int t = threadIdx.x; t < T; t += blockDim.x) {
+    const float v = logits[(size_t)t * E + e];
+    keys[t] = float_key(v);
+    mx = fmaxf(mx, v);
+  }
+  mx = block_max(mx, fsm);
+  float s = 0.f;
+  for (int t = threadIdx.x; t < T; t += blockDim.x) s += expf(logits[(size_t)t * E + e] - mx);
+  const float Z = block_sum(s, fsm);
+  __syncthreads();   // keys visible to the whole block
+  auto get = [&](int i) { return keys[i]; };
+  const SelectResult sr = block_radix_select(get, T, c, hist, sm);
+  int run_eq = 0, run_sel = 0;
+  for (int c0 = 0; c0 < T; c0 += blockDim.x) {
+    const int t = c0 + threadIdx.x;
+    const bool in = t < T;
+    const uint32_t u = in ? keys[t] : 0u;
+    const int eqf = (in && u == sr.tau) ? 1 : 0;
+    int tot;
+    const int eq_rank = run_eq + block_excl_scan(eqf, sm, &tot);
+    run_eq += tot;
+    const int self = in && (u > sr.tau || (eqf && eq_rank < sr.need_eq)) ? 1 : 0;
+    const int rank = run_sel + block_excl_scan(self, sm, &tot);
+    run_sel += tot;
+    if (in) {
+      if (self) {
+        const int q = e * c + rank;
+        perm_token[q] = t;
+        perm_w[q] = expf(logits[(size_t)t * E + e] - mx) / Z;
+        slot_pos[(size_t)t * E + e] = q;
+      } else {
+        slot_pos[(size_t)t * E + e] = -1;
+      }
+    }
+  }
+  if (threadIdx.x == 0) {
+    counts[e] = c;
+    offsets[e] = e * c;
+    if (e == E - 1) offsets[E] = E * c;
+  }
+}
+
+// ----------------------------------------------------------------------------------------
+// CSR over tokens from the slot table slot_pos[T, S] (row index or -1): per-block totals,
+// one scan over blocks, then per-token offsets and the row lists in slot order.
+__global__ __launch_bounds__(256) void tok_count_kernel(const int32_t *__restrict__ slot_pos, int T,
+                                                        int S, int32_t *__restrict__ blk_sum) {
+  __shared__ int sm[256 / 64 + 1];
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  int c = 0;
+  if (t < T)
+    for (int s = 0; s < S; ++s) c += slot_pos[(size_t)t * S + s] >= 0;
+  int tot;
+  block_excl_scan(c, sm, &tot);
+  if (threadIdx.x == 0) blk_sum[blockIdx.x] = tot;
+}
+
+__global__ __launch_bounds__(1024) void blk_scan_kernel(const int32_t *__restrict__ in, int n,
+                                                        int32_t *__restrict__ out,
+                                                        int32_t *__restrict__ total) {
+  __shared__ int sm[1024 / 64 + 1];
+  int run = 0;
+  for (int c0 = 0; c0 < n; c0 += 1024) {
+    const int i = c0 + threadIdx.x;
+    int tot;
+    const int ex = block_excl_scan(i < n ? in[i] : 0, sm, &tot);
+    if (i < n) out[i] = run + ex;
+    run += tot;
+  }
+  if (threadIdx.x == 0 && total) *total = run;
+}
+
+__global__ __launch_bounds__(256) void tok_write_kernel(const int32_t *__restrict__ slot_pos, int T,
+                                                        int S, const int32_t *__restrict__ blk_off,
+                                                        int32_t *__restrict__ tok_ptr,
+                                                        int32_t *__restrict__ tok_pos) {
+  __shared__ int sm[256 / 64 + 1];
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  int c = 0;
+  if (t < T)
+    for (int s = 0; s < S; ++s) c += slot_pos[(size_t)t * S + s] >= 0;
+  int tot;
+  const int ex = block_excl_scan(c, sm, &tot);
+  if (t < T) {
+    int p = blk_off[blockIdx.x] + ex;
+    tok_ptr[t] = p;
+    for (int s = 0; s < S; ++s) {
+      const int v = slot_pos[(size_t)t * S + s];
+      if (v >= 0) tok_pos[p++] = v;
+    }
+    if (t == T - 1) tok_ptr[T] = p;
+  }
+}
+
+// ----------------------------------------------------------------------------------------
+// Expert-utilisation statistics. Pass 1: per block of 256 tokens, the sum over its tokens
+// of softmax_E(l)[t, e] for every expert (thread e adds its block's tokens in order).
+// Pass 2 (one block): fixed-order sums over blocks and the scalar statistics.
+__global__ __launch_bounds__(256) void stats_partial_kernel(const float *__restrict__ logits, int T,
+                                                            int E, float *__restrict__ part) {
+  __shared__ float rmax[256], rinv[256];
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  if (t < T) {
+    float m = -INFINITY;
+    for (int e = 0; e < E; ++e) m = fmaxf(m, logits[(size_t)t * E + e]);
+    float s = 0.f;
+    for (int e = 0; e < E; ++e) s += __expf(logits[(size_t)t * E + e] - m);
+    rmax[threadIdx.x] = m;
+    rinv[threadIdx.x] = 1.f / s;
+  }
+  __syncthreads();
+  const int nt = min(256, T - blockIdx.x * 256);
+  for (int e = threadIdx.x; e < E; e += 256) {
+    float a = 0.f;
+    for (int i = 0; i < nt; ++i) {
+      const int tt = blockIdx.x * 256 + i;
+      a += __expf(logits[(size_t)tt * E + e] - rmax[i]) * rinv[i];
+    }
+    part[(size_t)blockIdx.x * E + e] = a;
+  }
+}
+
+__global__ __launch_bounds__(1024) void stats_final_kernel(const float *__restrict__ part, int nblk,
+                                                           const int32_t *__restrict__ counts,
+                                                           const int32_t *__restrict__ offsets,
+                                                           int T, int E, int k, int token_choice,
+                                                           float *__restrict__ out) {
+  __shared__ float fsm[1024 / 64];
+  const int rows = offsets[E];
+  float fp = 0.f, mxc = 0.f, empty = 0.f;
+  for (int e = threadIdx.x; e < E; e += 1024) {
+    float P = 0.f;
+    for (int b = 0; b < nblk; ++b) P += part[(size_t)b * E + e];
+    P /= (float)T;
+    const float f = rows > 0 ? (float)counts[e] / (float)rows : 0.f;
+    out[e] = f;
+    out[E + e] = P;
+    fp += f * P;
+    mxc = fmaxf(mxc, (float)counts[e]);
+    empty += counts[e] == 0 ? 1.f : 0.f;
+  }
+  fp = block_sum(fp, fsm);
+  mxc = block_max(mxc, fsm);
+  empty = block_sum(empty, fsm);
+  if (threadIdx.x == 0) {
+    out[2 * E] = (float)E * fp;
+    out[2 * E + 1] = rows > 0 ? mxc / ((float)rows / (float)E) : 0.f;
+    out[2 * E + 2] = token_choice ? (float)(T * k - rows) : 0.f;
+    out[2 * E + 3] = empty;
+  }
+}
+
+// ----------------------------------------------------------------------------------------
+// host-side launchers
+
+hipError_t launch_router(int dtype, const void *x, const float *w, const float *bias,
+                         float *logits, int T, int d, int E, hipStream_t st) {
+  if (E <= 8) {
+    dim3 grid((T + 7) / 8);
+    if (dtype == 0)
+      hipLaunchKernelGGL(router_narrow_kernel<float>, grid, dim3(256), 0, st,
+                         (const float *)x, w, bias, logits, T, d, E);
+    else
+      hipLaunchKernelGGL(router_narrow_kernel<bf16_t>, grid, dim3(256), 0, st,
+                         (const bf16_t *)x, w, bias, logits, T, d, E);
+  } else {
+    dim3 grid((T + 63) / 64, (E + 127) / 128);
+    if (dtype == 0)
+      hipLaunchKernelGGL(router_wide_kernel<float>, grid, dim3(256), 0, st, (const float *)x, w,
+                         bias, logits, T, d, E);
+    else
+      hipLaunchKernelGGL(router_wide_kernel<bf16_t>, grid, dim3(256), 0, st, (const bf16_t *)x,
+                         w, bias, logits, T, d, E);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_topk(const float *logits, int T, int E, int k, int renorm, int want_key,
+                       int32_t *ids, float *gates, float *keys, hipStream_t st) {
+  int G = 64;
+  if (E <= 8) G = 8;
+  else if (E <= 16) G = 16;
+  else if (E <= 32) G = 32;
+  const int tpb = 256 / G;
+  const size_t sh = want_key ? (size_t)tpb * E * sizeof(float) : 0;
+  dim3 grid((T + tpb - 1) / tpb);
+  switch (G) {
+    case 8: hipLaunchKernelGGL(topk_kernel<8>, grid, dim3(256), sh, st, logits, T, E, k, renorm, want_key, ids, gates, keys); break;
+    case 16: hipLaunchKernelGGL(topk_kernel<16>, grid, dim3(256), sh, st, logits, T, E, k, renorm, want_key, ids, gates, keys); break;
+    case 32: hipLaunchKernelGGL(topk_kernel<32>, grid, dim3(256), sh, st, logits, T, E, k, renorm, want_key, ids, gates, keys); break;
+    default: hipLaunchKernelGGL(topk_kernel<64>, grid, dim3(256), sh, st, logits, T, E, k, renorm, want_key, ids, gates, keys); break;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_token_dispatch(const RouteScratch &s, const int32_t *ids, const float *gates,
+                                 int T, int k, int E, int C, int32_t *perm_token, float *perm_w,
+                                 uint8_t *kept, int32_t *counts, int32_t *offsets,
+                                 hipStream_t st) {
+  const int nblk = (T + 255) / 256;
+  const size_t msh = (size_t)E * 8 * sizeof(uint32_t);
+  hipLaunchKernelGGL(assign_count_kernel, dim3(nblk), dim3(256), msh, st, ids, T, k, E,
+                     s.blk_cnt);
+  const bool drop = C >= 0;
+  hipLaunchKernelGGL(assign_scan_kernel, dim3(1), dim3(1024), 0, st, s.blk_cnt, nblk, E, C,
+                     s.blk_base, drop ? s.cnt_pre : counts, drop ? s.off_pre : offsets, counts,
+                     offsets);
+  if (!drop) {
+    hipLaunchKernelGGL(assign_scatter_kernel, dim3(nblk), dim3(256), msh, st, ids, gates,
+                       (const float *)nullptr, T, k, E, offsets, s.blk_base, 0, perm_token,
+                       perm_w, (int32_t *)nullptr, (float *)nullptr, s.slot_pos, kept);
+  } else {
+    hipLaunchKernelGGL(assign_scatter_kernel, dim3(nblk), dim3(256), msh, st, ids, gates,
+                       s.keys, T, k, E, s.off_pre, s.blk_base, 1, s.cand_token, (float *)nullptr,
+                       s.cand_slot, s.cand_key, (int32_t *)nullptr, (uint8_t *)nullptr);
+    hipLaunchKernelGGL(cap_select_kernel, dim3(E), dim3(1024), 0, st, s.cand_token, s.cand_slot,
+                       s.cand_key, s.cnt_pre, s.off_pre, offsets, C, k, gates, perm_token,
+                       perm_w, s.slot_pos, kept);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_expert_choice(const RouteScratch &s, const float *logits, int T, int E, int c,
+                                int32_t *perm_token, float *perm_w, int32_t *counts,
+                                int32_t *offsets, hipStream_t st) {
+  hipLaunchKernelGGL(ec_select_kernel, dim3(E), dim3(1024), 0, st, logits, T, E, c, s.colkeys,
+                     perm_token, perm_w, s.slot_pos, counts, offsets);
+  return hipGetLastError();
+}
+
+hipError_t launch_token_csr(const RouteScratch &s, int T, int S, int32_t *tok_ptr,
+                            int32_t *tok_pos, hipStream_t st) {
+  const int nblk = (T + 255) / 256;
+  hipLaunchKernelGGL(tok_count_kernel, dim3(nblk), dim3(256), 0, st, s.slot_pos, T, S,
+                     s.tok_blk);
+  hipLaunchKernelGGL(blk_scan_kernel, dim3(1), dim3(1024), 0, st, s.tok_blk, nblk, s.tok_blk_off,
+                     (int32_t *)nullptr);
+  hipLaunchKernelGGL(tok_write_kernel, dim3(nblk), dim3(256), 0, st, s.slot_pos, T, S,
+                     s.tok_blk_off, tok_ptr, tok_pos);
+  return hipGetLastError();
+}
+
+hipError_t launch_stats(const float *logits, const int32_t *counts, const int32_t *offsets, int T,
+                        int E, int k, int token_choice, float *part, float *out, hipStream_t st) {
+  const int nblk = (T + 255) / 256;
+  hipLaunchKernelGGL(stats_partial_kernel, dim3(nblk), dim3(256), 0, st, logits, T, E, part);
+  hipLaunchKernelGGL(stats_final_kernel, dim3(1), dim3(1024), 0, st, part, nblk, counts, offsets,
+                     T, E, k, token_choice, out);
+  return hipGetLastError();
+}
+
+}  // namespace moe

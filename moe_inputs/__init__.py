@@ -55,7 +55,8 @@ class MoEConfig:
     routing: str = "token"          # "token" (token choice) or "expert" (expert choice)
     gamma: float = 0.0              # capacity factor; <= 0 means no capacity limit
     renorm_topk: bool = True
-    dtype: str = "bf16"             # "bf16" or "f32": x, expert weights and y
+    dtype: str = "bf16"             # "bf16" or "f32": x, expert weights, hidden activation
+    y_dtype: str = ""               # layer output type; "" = same as dtype
     bias: tuple = ("none",)         # ("none",) | ("normal", variance) | ("zipf", s)
     seed: int = 0
 
@@ -159,16 +160,23 @@ def _expert_stack(cfg, tid, shape, std, threads):
     return out
 
 
-def make_inputs(cfg: MoEConfig, threads: int = 8) -> MoEInputs:
-    """Generate every tensor of the workload ``cfg`` (deterministic in cfg.seed)."""
+def make_inputs(cfg: MoEConfig, threads: int = 8, cache: Optional[dict] = None) -> MoEInputs:
+    """Generate every tensor of the workload ``cfg`` (deterministic in cfg.seed).
+    ``cache`` (a dict) lets workloads with equal shapes share the expert weight stacks."""
     d, E, dff = cfg.d_model, cfg.E, cfg.d_ff
     s = cfg.seed
     x = _store(_normal(s, TID_X, 0, (cfg.T, d), 1.0), cfg.dtype)
     w_router = _normal(s, TID_WR, 0, (d, E), 1.0 / math.sqrt(d))
     bias = router_bias(cfg)
-    w_gate = _expert_stack(cfg, TID_WG, (dff, d), 1.0 / math.sqrt(d), threads)
-    w_up = _expert_stack(cfg, TID_WU, (dff, d), 1.0 / math.sqrt(d), threads)
-    w_down = _expert_stack(cfg, TID_WD, (d, dff), 1.0 / math.sqrt(dff), threads)
+    key = (s, E, d, dff, cfg.dtype)
+    if cache is not None and key in cache:
+        w_gate, w_up, w_down = cache[key]
+    else:
+        w_gate = _expert_stack(cfg, TID_WG, (dff, d), 1.0 / math.sqrt(d), threads)
+        w_up = _expert_stack(cfg, TID_WU, (dff, d), 1.0 / math.sqrt(d), threads)
+        w_down = _expert_stack(cfg, TID_WD, (d, dff), 1.0 / math.sqrt(dff), threads)
+        if cache is not None:
+            cache[key] = (w_gate, w_up, w_down)
     ws = [None, None, None]
     if cfg.d_ff_shared > 0:
         fs = cfg.d_ff_shared

@@ -319,6 +319,31 @@ def layer_forward(inp, tokens: Optional[np.ndarray] = None, logits: Optional[np.
     return y, routing
 
 
+def combine(o_rows: np.ndarray, routing: dict, T: int, o_shared: Optional[np.ndarray] = None):
+    """y[t] = sum over rows p of token t of perm_w[p] * o_rows[p] (+ o_shared[t]), float64
+    (dongbusteel page: the gate-weighted sum over the selected experts)."""
+    o = widen(o_rows)
+    y = np.zeros((T, o.shape[1]))
+    ptr, pos, w = routing["tok_ptr"], routing["tok_pos"], routing["perm_w"]
+    for t in range(T):
+        for p in pos[ptr[t]:ptr[t + 1]]:
+            y[t] += w[p] * o[p]
+    if o_shared is not None:
+        y += widen(o_shared)
+    return y
+
+
+def expert_rows_ffn(x_rows: np.ndarray, routing: dict, inp, rows: np.ndarray) -> np.ndarray:
+    """E_e(x_rows[p]) for the dispatched rows ``rows`` (e = expert owning row p), float64."""
+    offs = routing["offsets"]
+    out = np.zeros((len(rows), inp.cfg.d_model))
+    e_of = np.searchsorted(offs, rows, side="right") - 1
+    for e in np.unique(e_of):
+        sel = np.nonzero(e_of == e)[0]
+        out[sel] = swiglu_ffn(widen(x_rows[rows[sel]]), inp.w_gate[e], inp.w_up[e], inp.w_down[e])
+    return out
+
+
 def shared_expert(inp, tokens: Optional[np.ndarray] = None) -> np.ndarray:
     toks = np.arange(inp.cfg.T) if tokens is None else np.asarray(tokens)
     return swiglu_ffn(widen(inp.x[toks]), inp.ws_gate, inp.ws_up, inp.ws_down)
