@@ -8,7 +8,7 @@
 //
 // bf16 path: persistent workgroups walk a tile list built on the device from the
 // per-expert row counts (no host round trip). A tile is 256 rows x 256 columns, K in
-// steps of 64; 4 waves in a 2 x 2 layout each own 128 x 128 of the tile as 4 x 4 blocks
+// steps of 32 (four LDS stages); 4 waves in a 2 x 2 layout each own 128 x 128 of the tile as 4 x 4 blocks
 // of v_mfma_f32_32x32x16_bf16 with float32 accumulators. A and B K-slices are staged in
 // LDS straight from global memory (gfx950 global_load_lds, no register staging), two
 // stages so the next K-slice lands while the current one feeds the MFMAs, 16-byte chunks
@@ -96,17 +96,29 @@ MOE_DEV int xcd_virtual_block() {
 }
 
 // ----------------------------------------------------------------------------------------
-// bf16 MFMA kernel
-constexpr int BM = 256, BN = 256, BK = 64;
-constexpr int kLdsTile = BM * BK * 2;   // bytes of one A (or B) K-slice: 256 rows x 128 B
+// bf16 MFMA kernel, templated on the tile width BN (256 rows x BN columns, K steps of 32).
+//   BN = 256: one workgroup per CU, 4 LDS stages of 32 KB, waves own 128 x 128.
+//   BN = 128: two workgroups per CU, 3 LDS stages of 24 KB each, waves own 128 x 64; while one
+//             workgroup waits at its barrier the other keeps the MFMA pipes busy.
+constexpr int BM = 256, BK = 32;
+constexpr int kRowBytes = BK * 2;                 // 64 B: 4 chunks of 16 B
+
+template <int BN> struct Cfg {
+  static constexpr int NB = BN / 64;              // 32-column MFMA blocks per wave
+  static constexpr int NSTAGE = BN == 256 ? 4 : 3;
+  static constexpr int OCC = BN == 256 ? 1 : 2;   // workgroups per CU
+  static constexpr int A_BYTES = BM * kRowBytes, B_BYTES = BN * kRowBytes;
+  static constexpr int A_DMA = A_BYTES / 1024 / 4, B_DMA = B_BYTES / 1024 / 4;   // per wave
+  static constexpr int IN_FLIGHT = (NSTAGE - 2) * (A_DMA + B_DMA);   // copies allowed pending
+};
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) const void gbl_void_t;
 
-// LDS byte offset of 16-byte chunk `chunk` (0..7) of tile row `row`: rows of 128 B, chunks
-// XOR-swizzled by (row/2) so that the 32 rows one MFMA fragment read touches spread over
-// all banks.
-MOE_DEV int swz(int row, int chunk) { return row * 128 + ((chunk ^ ((row >> 1) & 7)) << 4); }
+// LDS byte offset of 16-byte chunk `chunk` (0..3) of tile row `row`: rows of 64 B, chunks
+// XOR-swizzled by (row/4) % 4, so that the 16 rows one quarter-wave of an MFMA fragment read
+// touches cover all 64 banks exactly once.
+MOE_DEV int swz(int row, int chunk) { return row * kRowBytes + ((chunk ^ ((row >> 2) & 3)) << 4); }
 
 // Direct global -> LDS copy of 16 bytes per lane: lane L of the wave writes LDS bytes
 // [lds_base + 16 L, +16). lds_base must be the same in every lane.
@@ -114,36 +126,55 @@ MOE_DEV void g2lds16(const void *g, char *lds_base) {
   __builtin_amdgcn_global_load_lds((gbl_void_t *)g, (lds_void_t *)lds_base, 16, 0, 0);
 }
 
-// Two pipeline stages as separate LDS objects, so loads into one stage are never mistaken
+// The pipeline stages are separate LDS objects, so loads into one stage are never mistaken
 // for writes to the stage being read.
-struct Stage { char a[kLdsTile]; char b[kLdsTile]; };
+template <int BN> struct Stage { char a[Cfg<BN>::A_BYTES]; char b[Cfg<BN>::B_BYTES]; };
 
-template <bool GATE_UP>
-MOE_DEV void mma_stage(const Stage &st, int lane, int wm, int wn, f32x16_t (&acc)[4][4]) {
+template <int BN>
+MOE_DEV void load_frags(const Stage<BN> &st, int lane, int wm, int wn, int ks, bf16x8_t (&af)[4],
+                        bf16x8_t (&bfr)[Cfg<BN>::NB]) {
+  const int chunk = ks * 2 + (lane >> 5);
 #pragma unroll
-  for (int ks = 0; ks < BK / 16; ++ks) {
-    const int chunk = ks * 2 + (lane >> 5);
-    bf16x8_t af[4], bfr[4];
+  for (int mb = 0; mb < 4; ++mb)
+    af[mb] = *reinterpret_cast<const bf16x8_t *>(st.a + swz(wm * 128 + mb * 32 + (lane & 31), chunk));
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
-      af[mb] = *reinterpret_cast<const bf16x8_t *>(st.a + swz(wm * 128 + mb * 32 + (lane & 31), chunk));
-#pragma unroll
-    for (int nb = 0; nb < 4; ++nb)
-      bfr[nb] = *reinterpret_cast<const bf16x8_t *>(st.b + swz(wn * 128 + nb * 32 + (lane & 31), chunk));
-#pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-      for (int nb = 0; nb < 4; ++nb)
-        acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mb], bfr[nb], acc[mb][nb], 0, 0, 0);
-  }
+  for (int nb = 0; nb < Cfg<BN>::NB; ++nb)
+    bfr[nb] = *reinterpret_cast<const bf16x8_t *>(st.b + swz(wn * (BN / 2) + nb * 32 + (lane & 31), chunk));
 }
 
-template <bool GATE_UP>
-__global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs args) {
-  __shared__ Stage st0, st1;
+template <int BN>
+MOE_DEV void mfma_block(const bf16x8_t (&af)[4], const bf16x8_t (&bfr)[Cfg<BN>::NB],
+                        f32x16_t (&acc)[4][Cfg<BN>::NB]) {
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < Cfg<BN>::NB; ++nb)
+      acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mb], bfr[nb], acc[mb][nb], 0, 0, 0);
+}
+
+// keep the instruction order written here (no scheduling across this point)
+MOE_DEV void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
+
+// wait until at most N of this wave's global->LDS copies are still in flight
+template <int N> MOE_DEV void wait_vm() {
+  static_assert(N == 0 || N == 6 || N == 8 || N == 12 || N == 16, "add the count");
+  if constexpr (N == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  else if constexpr (N == 6) asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
+  else if constexpr (N == 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+  else if constexpr (N == 12) asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
+  else asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+}
+
+template <bool GATE_UP, int BN>
+__global__ __launch_bounds__(256, Cfg<BN>::OCC) void gemm_bf16_kernel(GemmArgs args) {
+  using C = Cfg<BN>;
+  constexpr int NB = C::NB, NSTAGE = C::NSTAGE;
+  __shared__ Stage<BN> st0, st1, st2;
+  __shared__ __attribute__((aligned(16))) char st3_raw[NSTAGE == 4 ? sizeof(Stage<BN>) : 16];
+  Stage<BN> &st3 = *reinterpret_cast<Stage<BN> *>(st3_raw);   // used only with 4 stages
   __shared__ int tstart[kMaxGroups + 1];
   __shared__ int sm[256 / 64 + 1];
-  constexpr int BNOUT = GATE_UP ? BN / 2 : BN;
+  constexpr int BNOUT = GATE_UP ? BN / 2 : BN;   // output columns per tile (h or o)
   const int G = build_tile_table<BM, BNOUT>(args, tstart, sm);
   const int total = tstart[G];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -156,61 +187,130 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs args) {
     const int mt = (d.rows + BM - 1) / BM;
     const int n_tile = local / mt, m_tile = local % mt;
     const int m0 = m_tile * BM;
-    // Loader: wave wv fills LDS rows wv*64 .. wv*64+63 of both slices with 8 copies of
-    // 1 KB (8 rows) each; lane L fetches row r0 + L/8, physical chunk L%8, i.e. logical
-    // K-chunk (L%8) ^ ((row/2)%8). For gate/up the B rows of wave wv are all gate rows
-    // (wv even) or all up rows (wv odd): B row r holds h column n_tile*128 + (r/128)*64 + r%64.
+    // Loader: wave wv fills A rows wv*64 .. +63 and B rows wv*(BN/4) .. +BN/4-1 with copies of
+    // 1 KB (16 rows of 64 B); lane L fetches row r0 + L/4, physical chunk L%4, i.e. logical
+    // K-chunk (L%4) ^ ((row/4)%4). For gate/up the B tile holds, per wave column wn, BN/4 gate
+    // rows then the matching BN/4 up rows (h columns n_tile*BN/2 + wn*BN/4 + i), so the B rows
+    // a wave loads are all gate (wv even) or all up (wv odd).
     const int wvu = __builtin_amdgcn_readfirstlane(wv);   // wave-uniform, kept in SGPRs
     const char *Ab = (const char *)d.A;
     const char *Bb = (const char *)((GATE_UP && (wvu & 1)) ? d.B1 : d.B0);
-    uint32_t aoff[8], boff[8];   // per-lane byte offsets from the (scalar) K-slice bases
+    uint32_t aoff[C::A_DMA], boff[C::B_DMA];   // per-lane byte offsets from the slice bases
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int r = wvu * 64 + i * 8 + (lane >> 3);
-      const int c = (lane & 7) ^ ((r >> 1) & 7);
+    for (int i = 0; i < C::A_DMA; ++i) {
+      const int r = wvu * (BM / 4) + i * 16 + (lane >> 2);
+      const int c = (lane & 3) ^ ((r >> 2) & 3);
       aoff[i] = ((uint32_t)min(m0 + r, d.rows - 1) * (uint32_t)d.lda + c * 8) * 2u;
-      const int n = GATE_UP ? n_tile * (BN / 2) + (r >> 7) * 64 + (r & 63) : n_tile * BN + r;
+    }
+#pragma unroll
+    for (int i = 0; i < C::B_DMA; ++i) {
+      const int r = wvu * (BN / 4) + i * 16 + (lane >> 2);
+      const int c = (lane & 3) ^ ((r >> 2) & 3);
+      const int n = GATE_UP ? n_tile * (BN / 2) + (wvu >> 1) * (BN / 4) + (r & (BN / 4 - 1))
+                            : n_tile * BN + r;
       boff[i] = ((uint32_t)min(n, d.N - 1) * (uint32_t)d.K + c * 8) * 2u;
     }
-    char *const la0 = st0.a + wvu * 8 * 1024, *const lb0 = st0.b + wvu * 8 * 1024;
-    char *const la1 = st1.a + wvu * 8 * 1024, *const lb1 = st1.b + wvu * 8 * 1024;
-    auto issue = [&](char *la, char *lb, int k0) {
-      const char *a = Ab + (size_t)k0 * 2, *b = Bb + (size_t)k0 * 2;
+    const int aofs = wvu * C::A_DMA * 1024, bofs = wvu * C::B_DMA * 1024;
+    auto issue = [&](Stage<BN> &s, int kt) {
+      const char *a = Ab + (size_t)kt * kRowBytes, *b = Bb + (size_t)kt * kRowBytes;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        g2lds16(a + aoff[i], la + i * 1024);
-        g2lds16(b + boff[i], lb + i * 1024);
-      }
+      for (int i = 0; i < C::A_DMA; ++i) g2lds16(a + aoff[i], s.a + aofs + i * 1024);
+#pragma unroll
+      for (int i = 0; i < C::B_DMA; ++i) g2lds16(b + boff[i], s.b + bofs + i * 1024);
     };
-    f32x16_t acc[4][4];
+    f32x16_t acc[4][NB];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < NB; ++j)
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
     const int nk = d.K / BK;
-    issue(la0, lb0, 0);
-    // K loop, two slices per trip: each half reads one fixed stage while the next slice
-    // lands in the other one (an odd slice count ends with one more stage-0 step).
+    // Pipeline. Slices go global -> LDS NSTAGE-1 ahead. A slice is two k=16 sub-steps. Step kt
+    // holds the fragments of sub-step 0 of slice kt in registers on entry. Its first half
+    // issues the sub-step-0 MFMAs with the LDS reads of sub-step 1 slotted between them; then
+    // it waits for slice kt+1 and passes the barrier; its second half issues the sub-step-1
+    // MFMAs with the copy of slice kt+NSTAGE-1 (into the stage slice kt-1 used) and the LDS
+    // reads of sub-step 0 of slice kt+1 slotted between them. With one wave per SIMD, memory
+    // instructions only overlap the matrix pipe when they sit between MFMAs. Every wave has
+    // read slice kt-1 completely before it reaches the barrier of step kt, so the refill never
+    // overwrites data still to be read.
+    bf16x8_t fa0[4], fb0[NB], fa1[4], fb1[NB];
+    issue(st0, 0);
+    if (nk > 1) issue(st1, 1);
+    if (NSTAGE == 4 && nk > 2) issue(st2, 2);
+    if (nk > NSTAGE - 2) wait_vm<C::IN_FLIGHT>();
+    else wait_vm<0>();
+    __builtin_amdgcn_s_barrier();
+    load_frags<BN>(st0, lane, wm, wn, 0, fa0, fb0);
+    // steady state: the next slice exists and the refill slice exists
+    auto steady = [&](Stage<BN> &cur, Stage<BN> &nxt, Stage<BN> &refill, int kt) {
+      sched_fence();
+      load_frags<BN>(cur, lane, wm, wn, 1, fa1, fb1);
+      mfma_block<BN>(fa0, fb0, acc);
+#pragma unroll
+      for (int i = 0; i < 4 + NB; ++i) {        // 4*NB MFMAs, 4+NB LDS reads
+        __builtin_amdgcn_sched_group_barrier(0x008, (4 * NB) / (4 + NB), 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      sched_fence();
+      wait_vm<C::IN_FLIGHT - (C::A_DMA + C::B_DMA)>();
+      __builtin_amdgcn_s_barrier();
+      sched_fence();
+      // past the last slice the copy re-reads the last slice into the stage nobody reads any
+      // more: branch-free, in bounds, and the wait counts stay the same every step
+      issue(refill, min(kt + NSTAGE - 1, nk - 1));
+      load_frags<BN>(nxt, lane, wm, wn, 0, fa0, fb0);
+      mfma_block<BN>(fa1, fb1, acc);
+#pragma unroll
+      for (int i = 0; i < 4 + NB; ++i) {        // copies and reads between the MFMAs
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 1);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
+      }
+      sched_fence();
+    };
+    // any step (tail): same order, with the boundary cases
+    auto step = [&](Stage<BN> &cur, Stage<BN> &nxt, Stage<BN> &refill, int kt) {
+      load_frags<BN>(cur, lane, wm, wn, 1, fa1, fb1);
+      sched_fence();
+      mfma_block<BN>(fa0, fb0, acc);
+      sched_fence();
+      if (kt + 1 < nk) {
+        // slice kt+1 must have landed; slices kt+2 .. kt+NSTAGE-2 may still be in flight
+        if (kt + NSTAGE - 2 < nk) wait_vm<C::IN_FLIGHT - (C::A_DMA + C::B_DMA)>();
+        else wait_vm<0>();
+        __builtin_amdgcn_s_barrier();
+        if (kt + NSTAGE - 1 < nk) issue(refill, kt + NSTAGE - 1);
+        load_frags<BN>(nxt, lane, wm, wn, 0, fa0, fb0);
+      }
+      sched_fence();
+      mfma_block<BN>(fa1, fb1, acc);
+      sched_fence();
+    };
+    static_assert(NSTAGE == 4, "the unrolled loop below cycles four stages");
     int kt = 0;
-    for (; kt + 2 <= nk; kt += 2) {
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      __syncthreads();
-      issue(la1, lb1, (kt + 1) * BK);
-      mma_stage<GATE_UP>(st0, lane, wm, wn, acc);
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      __syncthreads();
-      if (kt + 2 < nk) issue(la0, lb0, (kt + 2) * BK);
-      mma_stage<GATE_UP>(st1, lane, wm, wn, acc);
+    if ((nk & 3) == 0) {
+      // all steps take the steady path (the last ones read a stale next stage they never use)
+      for (; kt < nk; kt += 4) {
+        steady(st0, st1, st3, kt);
+        steady(st1, st2, st0, kt + 1);
+        steady(st2, st3, st1, kt + 2);
+        steady(st3, st0, st2, kt + 3);
+      }
+      wait_vm<0>();
     }
-    if (kt < nk) {
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      __syncthreads();
-      mma_stage<GATE_UP>(st0, lane, wm, wn, acc);
+    for (; kt < nk; ++kt) {
+      switch (kt & 3) {
+        case 0: step(st0, st1, st3, kt); break;
+        case 1: step(st1, st2, st0, kt); break;
+        case 2: step(st2, st3, st1, kt); break;
+        default: step(st3, st0, st2, kt); break;
+      }
     }
-    __syncthreads();   // every wave is done with both stages before the next tile's loads
+    __syncthreads();   // every wave is done with every stage before the next tile's loads
     // epilogue: h in bf16 (it feeds the next bf16 GEMM), o in float32
     bf16_t *Cb = (bf16_t *)d.C;
     float *Cf = (float *)d.C;
@@ -218,13 +318,13 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs args) {
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb) {
-          const int col = n_tile * (BN / 2) + wn * 64 + nb * 32 + (lane & 31);
+        for (int nb = 0; nb < NB / 2; ++nb) {
+          const int col = n_tile * (BN / 2) + wn * (BN / 4) + nb * 32 + (lane & 31);
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const int row = m0 + wm * 128 + mb * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
             if (row < d.rows && col < d.N) {
-              const float gv = acc[mb][nb][i], uv = acc[mb][nb + 2][i];
+              const float gv = acc[mb][nb][i], uv = acc[mb][nb + NB / 2][i];
               const float h = gv / (1.0f + __expf(-gv)) * uv;
               Cb[(size_t)row * d.ldc + col] = f32_to_bf16(h);
             }
@@ -234,8 +334,8 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs args) {
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb) {
-          const int col = n_tile * BN + wn * 128 + nb * 32 + (lane & 31);
+        for (int nb = 0; nb < NB; ++nb) {
+          const int col = n_tile * BN + wn * (BN / 2) + nb * 32 + (lane & 31);
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const int row = m0 + wm * 128 + mb * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
@@ -326,26 +426,34 @@ int gemm_tiles_upper(const GemmArgs &a, int bm, int bn_out, int max_rows) {
   return (int)(t > (1 << 30) ? (1 << 30) : t);
 }
 
+#ifndef MOE_GEMM_BN
+#define MOE_GEMM_BN 256
+#endif
+
+template <int BN>
+hipError_t launch_bf16(const GemmArgs &a, bool gate_up, int max_rows, int num_cu, hipStream_t st) {
+  const int bn_out = gate_up ? BN / 2 : BN;
+  int grid = gemm_tiles_upper(a, BM, bn_out, max_rows);
+  const int cap = num_cu * Cfg<BN>::OCC;
+  if (grid > cap) grid = cap;
+  if (grid < 1) grid = 1;
+  if (gate_up)
+    hipLaunchKernelGGL((gemm_bf16_kernel<true, BN>), dim3(grid), dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL((gemm_bf16_kernel<false, BN>), dim3(grid), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_gemm(const GemmArgs &a, bool gate_up, int max_rows, int num_cu,
                        hipStream_t st) {
-  if (a.elt == 2) {
-    const int bn_out = gate_up ? BN / 2 : BN;
-    int grid = gemm_tiles_upper(a, BM, bn_out, max_rows);
-    if (grid > num_cu) grid = num_cu;
-    if (grid < 1) grid = 1;
-    if (gate_up)
-      hipLaunchKernelGGL(gemm_bf16_kernel<true>, dim3(grid), dim3(256), 0, st, a);
-    else
-      hipLaunchKernelGGL(gemm_bf16_kernel<false>, dim3(grid), dim3(256), 0, st, a);
-  } else {
-    int grid = gemm_tiles_upper(a, 64, 64, max_rows);
-    if (grid > 4 * num_cu) grid = 4 * num_cu;
-    if (grid < 1) grid = 1;
-    if (gate_up)
-      hipLaunchKernelGGL(gemm_f32_kernel<true>, dim3(grid), dim3(256), 0, st, a);
-    else
-      hipLaunchKernelGGL(gemm_f32_kernel<false>, dim3(grid), dim3(256), 0, st, a);
-  }
+  if (a.elt == 2) return launch_bf16<MOE_GEMM_BN>(a, gate_up, max_rows, num_cu, st);
+  int grid = gemm_tiles_upper(a, 64, 64, max_rows);
+  if (grid > 4 * num_cu) grid = 4 * num_cu;
+  if (grid < 1) grid = 1;
+  if (gate_up)
+    hipLaunchKernelGGL(gemm_f32_kernel<true>, dim3(grid), dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL(gemm_f32_kernel<false>, dim3(grid), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
