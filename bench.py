@@ -49,7 +49,7 @@ def algorithmic(cfg, n_kept):
     gate_up = 4.0 * d * f * n_kept + 4.0 * d * fs * T
     down = 2.0 * d * f * n_kept + 2.0 * d * fs * T
     route = T * d * elt + d * E * 4 + T * E * 4 + T * k * 8
-    dispatch = n_kept * d * elt * 2 + n_kept * 4      # each kept row read once, written once
+    dispatch = 0.0                                     # folded into the gate/up GEMM
     combine = n_kept * d * 4 + n_kept * 8 + T * d * yel + (T * d * 4 if fs else 0)
     return dict(gate_up=gate_up, down=down, route=route, dispatch=dispatch, combine=combine)
 
@@ -150,7 +150,9 @@ def main():
     stages = {}
     for i, name in enumerate(moe.STAGE_NAMES):
         ent = {"us": round(float(stage_avg[i]) * 1e3, 2)}
-        if name in ("gate_up", "down"):
+        if name == "dispatch":
+            ent["note"] = "row gather folded into the gate/up GEMM operand loads"
+        elif name in ("gate_up", "down"):
             tf = work[name] / (stage_avg[i] * 1e-3) / 1e12
             ent.update(tflops=round(tf, 1), mfma_frac=round(tf / PEAK_BF16_TFLOPS, 4))
         else:

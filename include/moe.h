@@ -166,8 +166,11 @@ moe_status moe_expert_ffn(const moe_problem *problem, const void *x_perm,
 moe_status moe_combine(const moe_problem *problem, const void *o_perm, const void *o_shared,
                        const moe_routing *routing, void *y, hipStream_t stream);
 
-/* The whole layer: moe_route, moe_dispatch, moe_expert_ffn, moe_combine on `stream`.
- * routing may be NULL (then the routing arrays live inside the workspace). */
+/* The whole layer: the results of moe_route, moe_dispatch, moe_expert_ffn and moe_combine,
+ * on `stream`. The dispatch row gather is folded into the gate/up GEMM's operand loads
+ * (routed row p is read as x[perm_token[p]]), so no x_perm is materialised; the output is
+ * bit-identical to the four separate calls. routing may be NULL (then the routing arrays
+ * live inside the workspace). */
 moe_status moe_layer_forward(const moe_problem *problem, const void *x, const float *w_router,
                              const float *bias, const void *w_gate, const void *w_up,
                              const void *w_down, const void *ws_gate, const void *ws_up,
@@ -178,7 +181,7 @@ moe_status moe_layer_forward(const moe_problem *problem, const void *x, const fl
  * `stream` before stage i starts and events[MOE_STAGE_COUNT] after the last. */
 enum {
   MOE_STAGE_ROUTE = 0,    /* router, selection, dispatch indices */
-  MOE_STAGE_DISPATCH = 1, /* row gather                          */
+  MOE_STAGE_DISPATCH = 1, /* row gather (empty: folded into the gate/up GEMM) */
   MOE_STAGE_GATE_UP = 2,  /* grouped GEMM x W_gate, x W_up + SwiGLU (routed + shared) */
   MOE_STAGE_DOWN = 3,     /* grouped GEMM h W_down (routed + shared) */
   MOE_STAGE_COMBINE = 4,  /* weighted combine                    */

@@ -29,7 +29,8 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 struct GroupDesc {
-  const void *A;      // first row of the group
+  const void *A;      // first row of the group (or the whole A when rows are mapped)
+  const int32_t *amap;  // row map of the group (rows read A[amap[r]]), or null
   const void *B0;     // [N, K] weights (gate or down)
   const void *B1;     // [N, K] up weights (gate/up only)
   void *C;            // first output row
@@ -41,13 +42,15 @@ MOE_DEV GroupDesc group_desc(const GemmArgs &a, int g) {
   if (g < a.E) {
     const int off = a.offsets[g];
     d.rows = a.counts[g];
-    d.A = (const char *)a.A + (size_t)off * a.lda * a.elt;
+    d.amap = a.a_rows ? a.a_rows + off : nullptr;
+    d.A = a.a_rows ? a.A : (const char *)a.A + (size_t)off * a.lda * a.elt;
     d.B0 = (const char *)a.B0 + (size_t)g * a.N * a.K * a.elt;
     d.B1 = a.B1 ? (const char *)a.B1 + (size_t)g * a.N * a.K * a.elt : nullptr;
     d.C = (char *)a.C + (size_t)off * a.ldc * a.c_elt;
     d.N = a.N; d.K = a.K; d.lda = a.lda; d.ldc = a.ldc;
   } else {
     d.rows = a.s_rows;
+    d.amap = nullptr;
     d.A = a.sA; d.B0 = a.sB0; d.B1 = a.sB1; d.C = a.sC;
     d.N = a.sN; d.K = a.sK; d.lda = a.s_lda; d.ldc = a.s_ldc;
   }
@@ -200,7 +203,9 @@ __global__ __launch_bounds__(256, Cfg<BN>::OCC) void gemm_bf16_kernel(GemmArgs a
     for (int i = 0; i < C::A_DMA; ++i) {
       const int r = wvu * (BM / 4) + i * 16 + (lane >> 2);
       const int c = (lane & 3) ^ ((r >> 2) & 3);
-      aoff[i] = ((uint32_t)min(m0 + r, d.rows - 1) * (uint32_t)d.lda + c * 8) * 2u;
+      int arow = min(m0 + r, d.rows - 1);
+      if (d.amap) arow = d.amap[arow];   // dispatch gather folded into the operand load
+      aoff[i] = ((uint32_t)arow * (uint32_t)d.lda + c * 8) * 2u;
     }
 #pragma unroll
     for (int i = 0; i < C::B_DMA; ++i) {
@@ -378,7 +383,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs args) {
       __syncthreads();
       for (int idx = threadIdx.x; idx < TM * TK; idx += 256) {
         const int r = idx / TK, c = idx % TK, m = m0 + r, k = k0 + c;
-        As[c][r] = (m < d.rows && k < d.K) ? A[(size_t)m * d.lda + k] : 0.f;
+        As[c][r] = (m < d.rows && k < d.K) ? A[(size_t)(d.amap ? d.amap[m] : m) * d.lda + k] : 0.f;
         const int n = n0 + r;
         const bool ok = n < d.N && k < d.K;
         Bs[0][c][r] = ok ? B0[(size_t)n * d.K + k] : 0.f;

@@ -23,11 +23,13 @@ struct RouteScratch {
   int32_t *tok_blk;     // [nblk] per-block row counts of the token CSR
   int32_t *tok_blk_off; // [nblk]
   float *stats_part;    // [nblk*E]
+  uint16_t *w3;         // [3][E_pad][d] bf16 parts of the router weight (bf16 x)
 };
 
 // Grouped GEMM: routed experts (rows from counts/offsets on the device) + optional shared.
 struct GemmArgs {
   const void *A; int lda;          // routed rows, group e starts at row offsets[e]
+  const int32_t *a_rows;           // optional row map: routed row p reads A row a_rows[p]
   const void *B0; const void *B1;  // [E, N, K] (B1: up weights for gate/up, else null)
   void *C; int ldc;
   const int32_t *counts, *offsets;
@@ -37,8 +39,9 @@ struct GemmArgs {
   int s_rows, sN, sK, s_lda, s_ldc;
 };
 
+int router_epad(int E);   // experts padded for the matrix-core router (bf16 x)
 hipError_t launch_router(int dtype, const void *x, const float *w, const float *bias,
-                         float *logits, int T, int d, int E, hipStream_t st);
+                         float *logits, int T, int d, int E, uint16_t *w3, hipStream_t st);
 hipError_t launch_topk(const float *logits, int T, int E, int k, int renorm, int want_key,
                        int32_t *ids, float *gates, float *keys, hipStream_t st);
 hipError_t launch_token_dispatch(const RouteScratch &s, const int32_t *ids, const float *gates,

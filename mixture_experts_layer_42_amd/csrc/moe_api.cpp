@@ -19,11 +19,11 @@ size_t up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 struct Layout {
   // route scratch
   size_t keys, blk_cnt, blk_base, cnt_pre, off_pre, cand_token, cand_slot, cand_key, slot_pos,
-      colkeys, tok_blk, tok_blk_off, stats_part;
+      colkeys, tok_blk, tok_blk_off, stats_part, w3;
   // routing arrays used when the caller passes no routing struct
   size_t logits, ids, topk_w, kept, counts, offsets, perm_token, perm_w, tok_ptr, tok_pos;
   // activations
-  size_t h, h_shared, x_perm, o_perm, o_shared;
+  size_t h, h_shared, o_perm, o_shared;
   size_t total;
 };
 
@@ -51,6 +51,7 @@ Layout make_layout(const moe_problem &p) {
   L.tok_blk = take(nblk * 4);
   L.tok_blk_off = take(nblk * 4);
   L.stats_part = take(nblk * E * 4);
+  L.w3 = take(p.dtype == MOE_BF16 && p.E > 8 ? 3 * (size_t)router_epad(p.E) * d * 2 : 0);
   L.logits = take(T * E * 4);
   L.ids = take(T * k * 4);
   L.topk_w = take(T * k * 4);
@@ -63,7 +64,6 @@ Layout make_layout(const moe_problem &p) {
   L.tok_pos = take(R * 4);
   L.h = take(R * dff * elt);
   L.h_shared = take(T * dfs * elt);
-  L.x_perm = take(R * d * elt);
   L.o_perm = take(R * d * 4);
   L.o_shared = take(dfs > 0 ? T * d * 4 : 0);
   L.total = o;
@@ -96,8 +96,9 @@ moe_status check_problem(const moe_problem *pp) {
   } else {
     if (p.d_model % 4) return MOE_ERR_UNSUPPORTED;
   }
-  // 32-bit element offsets inside one operand panel
-  const int64_t big = (int64_t)1 << 32;
+  // 32-bit byte offsets inside one operand panel (elements < 2^31, bf16 or fp32 panels
+  // of the sizes below stay under 4 GiB)
+  const int64_t big = (int64_t)1 << (p.dtype == MOE_BF16 ? 31 : 30);
   const int64_t wmax = (int64_t)p.d_ff * p.d_model;
   const int64_t amax = R * (int64_t)(p.d_model > p.d_ff ? p.d_model : p.d_ff);
   const int64_t smax = (int64_t)p.T * (p.d_model > p.d_ff_shared ? p.d_model : p.d_ff_shared);
@@ -157,6 +158,7 @@ RouteScratch scratch_of(const Layout &L, char *ws) {
   s.tok_blk = (int32_t *)(ws + L.tok_blk);
   s.tok_blk_off = (int32_t *)(ws + L.tok_blk_off);
   s.stats_part = (float *)(ws + L.stats_part);
+  s.w3 = (uint16_t *)(ws + L.w3);
   return s;
 }
 
@@ -191,7 +193,7 @@ hipError_t do_route(const moe_problem &p, const void *x, const float *w_router,
   hipError_t e;
   if (!(flags & MOE_ROUTE_LOGITS_IN)) {
     e = launch_router(p.dtype == MOE_BF16 ? 1 : 0, x, w_router, bias, r.logits, p.T, p.d_model,
-                      p.E, st);
+                      p.E, s.w3, st);
     if (e != hipSuccess) return e;
   }
   if (p.routing == MOE_TOKEN_CHOICE) {
@@ -219,8 +221,10 @@ hipError_t do_dispatch(const moe_problem &p, const void *x, const moe_routing &r
 
 GemmArgs gemm_args(const moe_problem &p, const moe_routing &r, bool gate_up, const void *a_rows,
                    const void *w0, const void *w1, void *c_rows, const void *s_a,
-                   const void *s_w0, const void *s_w1, void *s_c) {
+                   const void *s_w0, const void *s_w1, void *s_c,
+                   const int32_t *row_map = nullptr) {
   GemmArgs a{};
+  a.a_rows = row_map;
   a.counts = r.counts;
   a.offsets = r.offsets;
   a.E = p.E;
@@ -244,12 +248,15 @@ GemmArgs gemm_args(const moe_problem &p, const moe_routing &r, bool gate_up, con
   return a;
 }
 
+// x_perm given: routed rows are x_perm rows. x_perm null: routed row p is read as
+// x[perm_token[p]] (the dispatch gather folded into the GEMM's operand loads).
 hipError_t do_gate_up(const moe_problem &p, const void *x_perm, const moe_routing &r,
                       const void *w_gate, const void *w_up, const void *x, const void *ws_gate,
                       const void *ws_up, char *ws, hipStream_t st) {
   const Layout L = make_layout(p);
-  const GemmArgs a = gemm_args(p, r, true, x_perm, w_gate, w_up, ws + L.h, x, ws_gate, ws_up,
-                               ws + L.h_shared);
+  const GemmArgs a = gemm_args(p, r, true, x_perm ? x_perm : x, w_gate, w_up, ws + L.h, x,
+                               ws_gate, ws_up, ws + L.h_shared,
+                               x_perm ? nullptr : r.perm_token);
   return launch_gemm(a, true, (int)rows_cap(p), num_cus(), st);
 }
 
@@ -290,10 +297,9 @@ moe_status layer_forward(const moe_problem *pp, const void *x, const float *w_ro
   auto mark = [&](int i) { return ev ? hipEventRecord(ev[i], st) : hipSuccess; };
   MOE_TRY(mark(MOE_STAGE_ROUTE));
   MOE_TRY(do_route(p, x, w_router, bias, 0, r, w, st));
-  MOE_TRY(mark(MOE_STAGE_DISPATCH));
-  MOE_TRY(do_dispatch(p, x, r, w + L.x_perm, st));
+  MOE_TRY(mark(MOE_STAGE_DISPATCH));   // the row gather runs inside the gate/up GEMM
   MOE_TRY(mark(MOE_STAGE_GATE_UP));
-  MOE_TRY(do_gate_up(p, w + L.x_perm, r, w_gate, w_up, x, ws_gate, ws_up, w, st));
+  MOE_TRY(do_gate_up(p, nullptr, r, w_gate, w_up, x, ws_gate, ws_up, w, st));
   MOE_TRY(mark(MOE_STAGE_DOWN));
   MOE_TRY(do_down(p, r, w_down, ws_down, w + L.o_perm, w + L.o_shared, w, st));
   MOE_TRY(mark(MOE_STAGE_COMBINE));

@@ -207,6 +207,130 @@ __global__ __launch_bounds__(256) void router_wide_kernel(const XT *__restrict__
 }
 
 // ----------------------------------------------------------------------------------------
+// Router on the matrix cores (bf16 x). W_r (float32) is split exactly into three bf16 parts,
+// W = hi + mid + lo (hi = bf16(W), mid = bf16(W - hi), lo = W - hi - mid, which fits in bf16
+// because each step removes the leading 8 significant bits of a 24-bit value). Every
+// product of a bf16 x and a bf16 part is exact in float32, so
+//   l = x.hi + x.mid + x.lo  (float32 accumulation)
+// gives float32-accurate logits at MFMA rate. The parts are stored transposed, [3][E_pad][d],
+// so both MFMA operands stream along d like the expert GEMMs.
+typedef __bf16 rbf16x8_t __attribute__((ext_vector_type(8)));
+typedef float rf32x16_t __attribute__((ext_vector_type(16)));
+
+__global__ __launch_bounds__(256) void router_split_kernel(const float *__restrict__ w, int d,
+                                                           int E, int E_pad,
+                                                           bf16_t *__restrict__ w3) {
+  const size_t n = (size_t)E_pad * d;
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) {
+    const int e = (int)(i / d), j = (int)(i % d);
+    const float v = e < E ? w[(size_t)j * E + e] : 0.f;
+    const bf16_t hi = f32_to_bf16(v);
+    const float r1 = v - bf16_to_f32(hi);
+    const bf16_t mid = f32_to_bf16(r1);
+    const bf16_t lo = f32_to_bf16(r1 - bf16_to_f32(mid));
+    w3[i] = hi;
+    w3[n + i] = mid;
+    w3[2 * n + i] = lo;
+  }
+}
+
+// WG = 4 waves; WE waves along experts (NB blocks of 32 experts each), 4/WE along tokens
+// (32 tokens each). K steps of 64: the three W parts for the WG's experts go straight from
+// global memory into a two-stage LDS buffer (rows of 128 B, 16-byte chunks XOR-swizzled by
+// row/2; lane L of a 1 KB copy fetches the chunk that lands at byte 16 L), the next stage
+// loading while the current one feeds the MFMAs; x fragments come straight from global
+// memory one chunk ahead (each x row is read once).
+typedef __attribute__((address_space(3))) void rlds_void_t;
+typedef __attribute__((address_space(1))) const void rgbl_void_t;
+
+template <int WE, int NB>
+__global__ __launch_bounds__(256) void router_mfma_kernel(const bf16_t *__restrict__ x,
+                                                          const bf16_t *__restrict__ w3,
+                                                          const float *__restrict__ bias,
+                                                          float *__restrict__ logits, int T,
+                                                          int d, int E, int E_pad) {
+  constexpr int EPW = WE * NB * 32;           // experts per workgroup
+  constexpr int TPW = (4 / WE) * 32;          // tokens per workgroup
+  constexpr int ROWS = 3 * EPW;               // LDS rows per K chunk (128 B each)
+  constexpr int COPIES = ROWS / 8 / 4;        // 1 KB copies per wave per chunk
+  __shared__ __attribute__((aligned(16))) char wl0[ROWS * 128];
+  __shared__ __attribute__((aligned(16))) char wl1[ROWS * 128];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int wvu = __builtin_amdgcn_readfirstlane(wv);
+  const int we = wv % WE, wt = wv / WE;
+  const int t0 = blockIdx.x * TPW + wt * 32, e0 = blockIdx.y * EPW;
+  const size_t plane = (size_t)E_pad * d;
+  auto swz = [](int row, int chunk) { return row * 128 + ((chunk ^ ((row >> 1) & 7)) << 4); };
+  uint32_t woff[COPIES];   // per-lane element offsets of this wave's copies
+#pragma unroll
+  for (int i = 0; i < COPIES; ++i) {
+    const int row = (wvu * COPIES + i) * 8 + (lane >> 3);
+    const int c = (lane & 7) ^ ((row >> 1) & 7);
+    const int part = row / EPW, e = e0 + row % EPW;
+    woff[i] = (uint32_t)(part * plane + (size_t)e * d + c * 8);
+  }
+  auto stage = [&](char *buf, int k0) {
+#pragma unroll
+    for (int i = 0; i < COPIES; ++i)
+      __builtin_amdgcn_global_load_lds((rgbl_void_t *)(w3 + woff[i] + k0),
+                                       (rlds_void_t *)(buf + (wvu * COPIES + i) * 1024), 16, 0, 0);
+  };
+  rf32x16_t acc[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[nb][v] = 0.f;
+  const int tl = min(t0 + (lane & 31), T - 1);
+  const bf16_t *xr = x + (size_t)tl * d + 8 * (lane >> 5);
+  const int nk = d / 64;
+  rbf16x8_t a[4], an[4];
+  auto load_x = [&](rbf16x8_t (&dst)[4], int kc) {
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) dst[ks] = *reinterpret_cast<const rbf16x8_t *>(xr + kc * 64 + ks * 16);
+  };
+  auto compute = [&](const char *buf) {
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int chunk = ks * 2 + (lane >> 5);
+#pragma unroll
+      for (int part = 0; part < 3; ++part)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          const int row = part * EPW + we * NB * 32 + nb * 32 + (lane & 31);
+          const rbf16x8_t b = *reinterpret_cast<const rbf16x8_t *>(buf + swz(row, chunk));
+          acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks], b, acc[nb], 0, 0, 0);
+        }
+    }
+  };
+  stage(wl0, 0);
+  load_x(a, 0);
+  for (int kc = 0; kc < nk; kc += 2) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    if (kc + 1 < nk) { stage(wl1, (kc + 1) * 64); load_x(an, kc + 1); }
+    compute(wl0);
+    if (kc + 1 >= nk) break;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) a[ks] = an[ks];
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    if (kc + 2 < nk) { stage(wl0, (kc + 2) * 64); load_x(an, kc + 2); }
+    compute(wl1);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) a[ks] = an[ks];
+  }
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const int e = e0 + we * NB * 32 + nb * 32 + (lane & 31);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int t = t0 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+      if (t < T && e < E) logits[(size_t)t * E + e] = acc[nb][i] + (bias ? bias[e] : 0.f);
+    }
+  }
+}
+
+// ----------------------------------------------------------------------------------------
 // Token-choice top-k. A group of G lanes (G = power of two >= min(E, 64)) handles one
 // token; lane i of the group holds experts i, i+G, i+2G, ... Each round takes the group
 // maximum (ties: lower expert index). Gates: exp(l - max) normalised over the picks (or
@@ -643,8 +767,30 @@ __global__ __launch_bounds__(1024) void stats_final_kernel(const float *__restri
 // ----------------------------------------------------------------------------------------
 // host-side launchers
 
+int router_epad(int E) { return E <= 32 ? 32 : E <= 64 ? 64 : ((E + 127) / 128) * 128; }
+
 hipError_t launch_router(int dtype, const void *x, const float *w, const float *bias,
-                         float *logits, int T, int d, int E, hipStream_t st) {
+                         float *logits, int T, int d, int E, bf16_t *w3, hipStream_t st) {
+  if (dtype == 1 && E > 8) {
+    // bf16 activations, wide router: three-part split of W_r on the matrix cores (E <= 8
+    // stays on the narrow kernel below, whose one-token-row-per-lane-group streaming keeps
+    // every CU busy at small T)
+    const int E_pad = router_epad(E);
+    const size_t n = (size_t)E_pad * d;
+    int g = (int)((n + 255) / 256);
+    if (g > 2048) g = 2048;
+    hipLaunchKernelGGL(router_split_kernel, dim3(g), dim3(256), 0, st, w, d, E, E_pad, w3);
+    if (E_pad == 32)
+      hipLaunchKernelGGL((router_mfma_kernel<1, 1>), dim3((T + 127) / 128, 1), dim3(256), 0, st,
+                         (const bf16_t *)x, w3, bias, logits, T, d, E, E_pad);
+    else if (E_pad == 64)
+      hipLaunchKernelGGL((router_mfma_kernel<1, 2>), dim3((T + 127) / 128, 1), dim3(256), 0, st,
+                         (const bf16_t *)x, w3, bias, logits, T, d, E, E_pad);
+    else
+      hipLaunchKernelGGL((router_mfma_kernel<2, 2>), dim3((T + 63) / 64, E_pad / 128), dim3(256),
+                         0, st, (const bf16_t *)x, w3, bias, logits, T, d, E, E_pad);
+    return hipGetLastError();
+  }
   if (E <= 8) {
     dim3 grid((T + 7) / 8);
     if (dtype == 0)
