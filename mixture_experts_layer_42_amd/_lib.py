@@ -58,6 +58,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     if not os.path.exists(path):
         raise RuntimeError(f"{path} is missing: build it with "
                            "`python -m mixture_experts_layer_42_amd.build` (no fallback exists)")
+    # torch ships its own HIP runtime; load it first so that this library binds to that same
+    # runtime (a second runtime loaded beside it would not know torch's device allocations)
+    import torch  # noqa: F401
     lib = ctypes.CDLL(path)
     P, V, SZ, I = ctypes.POINTER(moe_problem), ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
     R = ctypes.POINTER(moe_routing)

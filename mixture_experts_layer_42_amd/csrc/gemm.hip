@@ -98,6 +98,24 @@ MOE_DEV int xcd_virtual_block() {
   return (b % 8) * (n / 8) + b / 8;
 }
 
+// Tail split. With P persistent workgroups and `total` tiles, the first r*P tiles (r whole
+// rounds) run whole; if the remaining L tiles fill at most half a round, each is cut into S
+// K-parts (S a power of two, S*L <= P, S <= 8, each part a multiple of 4 K-steps) so that the
+// last round takes about 1/S of a tile's time. Both the GEMM and the reduction kernel derive
+// the same plan from the device-side tile count.
+struct SplitPlan { int full, L, S; };
+
+MOE_DEV SplitPlan split_plan(int total, int P, int nk, int ok) {
+  SplitPlan sp{total, 0, 1};
+  const int r = total / P, L = total - r * P;
+  if (!ok || L == 0 || 2 * L > P) return sp;
+  int S = 1;
+  while (2 * S * L <= P && 2 * S <= 8 && nk % (8 * S) == 0) S *= 2;
+  if (S == 1) return sp;
+  sp.full = r * P; sp.L = L; sp.S = S;
+  return sp;
+}
+
 // ----------------------------------------------------------------------------------------
 // bf16 MFMA kernel, templated on the tile width BN (256 rows x BN columns, K steps of 32).
 //   BN = 256: one workgroup per CU, 4 LDS stages of 32 KB, waves own 128 x 128.
@@ -183,13 +201,23 @@ __global__ __launch_bounds__(256, Cfg<BN>::OCC) void gemm_bf16_kernel(GemmArgs a
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int wm = wv >> 1, wn = wv & 1;
 
-  for (int tile = xcd_virtual_block(); tile < total; tile += gridDim.x) {
+  const SplitPlan sp = split_plan(total, gridDim.x, args.K / BK, args.split_ok);
+  const int units = sp.full + sp.L * sp.S;
+  for (int u = xcd_virtual_block(); u < units; u += gridDim.x) {
+    int tile = u, part = 0, nparts = 1;
+    if (u >= sp.full) {
+      tile = sp.full + (u - sp.full) / sp.S;
+      part = (u - sp.full) % sp.S;
+      nparts = sp.S;
+    }
     const int g = find_group(tstart, G, tile);
     const GroupDesc d = group_desc(args, g);
     const int local = tile - tstart[g];
     const int mt = (d.rows + BM - 1) / BM;
     const int n_tile = local / mt, m_tile = local % mt;
     const int m0 = m_tile * BM;
+    const int nk = (d.K / BK) / nparts;   // K-steps of this unit
+    const int k_begin = part * nk;         // first K-step of this unit
     // Loader: wave wv fills A rows wv*64 .. +63 and B rows wv*(BN/4) .. +BN/4-1 with copies of
     // 1 KB (16 rows of 64 B); lane L fetches row r0 + L/4, physical chunk L%4, i.e. logical
     // K-chunk (L%4) ^ ((row/4)%4). For gate/up the B tile holds, per wave column wn, BN/4 gate
@@ -217,7 +245,8 @@ __global__ __launch_bounds__(256, Cfg<BN>::OCC) void gemm_bf16_kernel(GemmArgs a
     }
     const int aofs = wvu * C::A_DMA * 1024, bofs = wvu * C::B_DMA * 1024;
     auto issue = [&](Stage<BN> &s, int kt) {
-      const char *a = Ab + (size_t)kt * kRowBytes, *b = Bb + (size_t)kt * kRowBytes;
+      const char *a = Ab + (size_t)(k_begin + kt) * kRowBytes;
+      const char *b = Bb + (size_t)(k_begin + kt) * kRowBytes;
 #pragma unroll
       for (int i = 0; i < C::A_DMA; ++i) g2lds16(a + aoff[i], s.a + aofs + i * 1024);
 #pragma unroll
@@ -231,7 +260,6 @@ __global__ __launch_bounds__(256, Cfg<BN>::OCC) void gemm_bf16_kernel(GemmArgs a
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-    const int nk = d.K / BK;
     // Pipeline. Slices go global -> LDS NSTAGE-1 ahead. A slice is two k=16 sub-steps. Step kt
     // holds the fragments of sub-step 0 of slice kt in registers on entry. Its first half
     // issues the sub-step-0 MFMAs with the LDS reads of sub-step 1 slotted between them; then
@@ -249,7 +277,7 @@ __global__ __launch_bounds__(256, Cfg<BN>::OCC) void gemm_bf16_kernel(GemmArgs a
     else wait_vm<0>();
     __builtin_amdgcn_s_barrier();
     load_frags<BN>(st0, lane, wm, wn, 0, fa0, fb0);
-    // steady state: the next slice exists and the refill slice exists
+    // one K-step (slice kt); the refill index is clamped to the last slice
     auto steady = [&](Stage<BN> &cur, Stage<BN> &nxt, Stage<BN> &refill, int kt) {
       sched_fence();
       load_frags<BN>(cur, lane, wm, wn, 1, fa1, fb1);
@@ -277,76 +305,167 @@ __global__ __launch_bounds__(256, Cfg<BN>::OCC) void gemm_bf16_kernel(GemmArgs a
       }
       sched_fence();
     };
-    // any step (tail): same order, with the boundary cases
-    auto step = [&](Stage<BN> &cur, Stage<BN> &nxt, Stage<BN> &refill, int kt) {
-      load_frags<BN>(cur, lane, wm, wn, 1, fa1, fb1);
-      sched_fence();
-      mfma_block<BN>(fa0, fb0, acc);
-      sched_fence();
-      if (kt + 1 < nk) {
-        // slice kt+1 must have landed; slices kt+2 .. kt+NSTAGE-2 may still be in flight
-        if (kt + NSTAGE - 2 < nk) wait_vm<C::IN_FLIGHT - (C::A_DMA + C::B_DMA)>();
-        else wait_vm<0>();
-        __builtin_amdgcn_s_barrier();
-        if (kt + NSTAGE - 1 < nk) issue(refill, kt + NSTAGE - 1);
-        load_frags<BN>(nxt, lane, wm, wn, 0, fa0, fb0);
-      }
-      sched_fence();
-      mfma_block<BN>(fa1, fb1, acc);
-      sched_fence();
-    };
+    // Four steps per iteration cycle the four stages. The loop body is one branch-free block,
+    // so the compiler's wait counts stay exact inside it (a join would make it drain every
+    // copy in flight); the 1-3 steps of a K that is not a multiple of 4 slices follow it. The
+    // last steps read a stale next stage they never use, and their refills re-read the last
+    // slice, so every wait count holds as in the middle.
     static_assert(NSTAGE == 4, "the unrolled loop below cycles four stages");
     int kt = 0;
-    if ((nk & 3) == 0) {
-      // all steps take the steady path (the last ones read a stale next stage they never use)
-      for (; kt < nk; kt += 4) {
-        steady(st0, st1, st3, kt);
-        steady(st1, st2, st0, kt + 1);
-        steady(st2, st3, st1, kt + 2);
-        steady(st3, st0, st2, kt + 3);
-      }
-      wait_vm<0>();
+    for (; kt + 4 <= nk; kt += 4) {
+      steady(st0, st1, st3, kt);
+      steady(st1, st2, st0, kt + 1);
+      steady(st2, st3, st1, kt + 2);
+      steady(st3, st0, st2, kt + 3);
     }
-    for (; kt < nk; ++kt) {
-      switch (kt & 3) {
-        case 0: step(st0, st1, st3, kt); break;
-        case 1: step(st1, st2, st0, kt); break;
-        case 2: step(st2, st3, st1, kt); break;
-        default: step(st3, st0, st2, kt); break;
-      }
+    if (kt < nk) {
+      steady(st0, st1, st3, kt);
+      if (kt + 1 < nk) steady(st1, st2, st0, kt + 1);
+      if (kt + 2 < nk) steady(st2, st3, st1, kt + 2);
     }
+    wait_vm<0>();
     __syncthreads();   // every wave is done with every stage before the next tile's loads
-    // epilogue: h in bf16 (it feeds the next bf16 GEMM), o in float32
-    bf16_t *Cb = (bf16_t *)d.C;
-    float *Cf = (float *)d.C;
-    if (GATE_UP) {
+    if (nparts > 1) {
+      // K-part of a split tile: the raw accumulators in register order (wave, mb, nb, i,
+      // lane), so each store is 256 contiguous bytes; the reduction maps them back
+      float *Pt = args.partials + (size_t)(u - sp.full) * (BM * BN) + wv * (64 * 4 * NB * 16) + lane;
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-        for (int nb = 0; nb < NB / 2; ++nb) {
-          const int col = n_tile * (BN / 2) + wn * (BN / 4) + nb * 32 + (lane & 31);
+        for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int row = m0 + wm * 128 + mb * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-            if (row < d.rows && col < d.N) {
+          for (int i = 0; i < 16; ++i) Pt[((mb * NB + nb) * 16 + i) * 64] = acc[mb][nb][i];
+      continue;
+    }
+    // epilogue: h in bf16 (it feeds the next bf16 GEMM), o in float32. Lane (c, r4) holds
+    // column c of rows r4*4 + {0..3} + 8j of each 32 x 32 block. Stores go through a buffer
+    // resource spanning exactly the group's output rows, so the hardware drops the stores of
+    // rows past the group's end (a partial last row tile needs no per-element branch). The
+    // lane index is made opaque so the per-lane offset is rebuilt each tile rather than
+    // hoisted with 256 others.
+    int lo = lane;
+    asm volatile("" : "+v"(lo));
+    constexpr int CE = GATE_UP ? 2 : 4;   // bytes per output element
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        d.C, (short)0, (int)((uint32_t)d.rows * (uint32_t)d.ldc * CE), 0x00020000);
+    const int cw = n_tile * BNOUT + wn * (BNOUT / 2);   // first output column of this wave
+    const int nbv = (d.N - cw) >= (GATE_UP ? NB / 2 : NB) * 32 ? (GATE_UP ? NB / 2 : NB)
+                                                               : (d.N - cw) / 32;   // live blocks
+    const uint32_t rowb = (uint32_t)d.ldc * CE;
+    // running byte offset of this lane's current row, advanced row by row (kept opaque so the
+    // compiler does not expand it into one live offset per row)
+    uint32_t roff = (uint32_t)(m0 + wm * 128 + 4 * (lo >> 5)) * rowb + (uint32_t)(cw + (lo & 31)) * CE;
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+#pragma unroll
+        for (int nb = 0; nb < (GATE_UP ? NB / 2 : NB); ++nb) {
+          if (nb < nbv) {
+            if (GATE_UP) {
               const float gv = acc[mb][nb][i], uv = acc[mb][nb + NB / 2][i];
               const float h = gv / (1.0f + __expf(-gv)) * uv;
-              Cb[(size_t)row * d.ldc + col] = f32_to_bf16(h);
+              __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(h), rs, (int)(roff + nb * 32 * CE),
+                                                    0, 0);
+            } else {
+              float v = acc[mb][nb][i];
+              asm volatile("" : "+v"(v));
+              __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), rs,
+                                                    (int)(roff + nb * 32 * CE), 0, 0);
             }
           }
         }
-    } else {
+        // next row of this lane: +1 inside a group of 4, +5 after the 4th (rows 4..7 belong
+        // to the other half-wave), the last i of a block steps to the next block the same way
+        roff += ((i & 3) == 3 ? 5u : 1u) * rowb;
+        asm volatile("" : "+v"(roff));
+      }
+  }
+}
+
+// Sum of the K-parts of split tiles, in part order, then the same epilogue as a whole tile.
+// Work item: 32 rows of one split tile; each thread owns 4 adjacent output columns of a row
+// (all S part loads issued before the sums). The plan is derived from the GEMM's grid size
+// (args.grid), so any grid of this kernel sees the same split.
+constexpr int kReduceRows = 32;
+
+// Offset of tile element (tr, tc) in a partial tile stored in accumulator register order:
+// wave (tr/128)*2 + tc/128, block mb = tr%128/32, nb = tc%128/32, register
+// i = 4*(tr%32/8) + tr%4, lane = tc%32 + 32*(tr%8/4). The row and column parts add, and
+// 4 adjacent columns (tc % 4 == 0) are 4 adjacent floats.
+MOE_DEV int part_index(int tr, int tc) {
+  const int row_part = (tr >> 7) * 2 * 16384 + ((tr >> 5) & 3) * 4 * 16 * 64 +
+                       (4 * ((tr >> 3) & 3) + (tr & 3)) * 64 + 32 * ((tr >> 2) & 1);
+  const int col_part = (tc >> 7) * 16384 + ((tc >> 5) & 3) * 16 * 64 + (tc & 31);
+  return row_part + col_part;
+}
+
+template <bool GATE_UP>
+__global__ __launch_bounds__(256) void gemm_tail_reduce_kernel(GemmArgs args) {
+  constexpr int BN = 256;
+  constexpr int BNOUT = GATE_UP ? BN / 2 : BN;
+  constexpr int TPR = BNOUT / 4;        // threads per row
+  constexpr int RPP = 256 / TPR;        // rows per pass
+  constexpr int PART = BM * BN;         // floats per partial tile
+  __shared__ int tstart[kMaxGroups + 1];
+  __shared__ int sm[256 / 64 + 1];
+  const int G = build_tile_table<BM, BNOUT>(args, tstart, sm);
+  const SplitPlan sp = split_plan(tstart[G], args.grid, args.K / BK, args.split_ok);
+  const int items = sp.L * (BM / kReduceRows);
+  for (int it = blockIdx.x; it < items; it += gridDim.x) {
+    const int l = it / (BM / kReduceRows), r0 = (it % (BM / kReduceRows)) * kReduceRows;
+    const int tile = sp.full + l;
+    const int g = find_group(tstart, G, tile);
+    const GroupDesc d = group_desc(args, g);
+    const int local = tile - tstart[g];
+    const int mt = (d.rows + BM - 1) / BM;
+    const int n_tile = local / mt, m_tile = local % mt;
+    const int c = (threadIdx.x % TPR) * 4;             // first of 4 output columns in the tile
+    const int col = n_tile * BNOUT + c;
+    if (col >= d.N) continue;                         // N is a multiple of 64: whole groups of 4
+    for (int rr = threadIdx.x / TPR; rr < kReduceRows; rr += RPP) {
+      const int tr = r0 + rr, row = m_tile * BM + tr;
+      if (row >= d.rows) break;
+      const float *P0 = args.partials + (size_t)l * sp.S * PART + part_index(tr, 0);
+      if (GATE_UP) {
+        // h column c: gate sum at B-tile column (c/64)*128 + c%64, up sum 64 columns further
+        const int tc = (c >> 6) * 128 + (c & 63);
+        const int og = part_index(0, tc), ou = part_index(0, tc + 64);
+        float4 gp[8], up[8];
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-          const int col = n_tile * BN + wn * (BN / 2) + nb * 32 + (lane & 31);
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int row = m0 + wm * 128 + mb * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-            if (row < d.rows && col < d.N) Cf[(size_t)row * d.ldc + col] = acc[mb][nb][i];
+        for (int p = 0; p < 8; ++p)
+          if (p < sp.S) {
+            gp[p] = *(const float4 *)(P0 + (size_t)p * PART + og);
+            up[p] = *(const float4 *)(P0 + (size_t)p * PART + ou);
           }
+        float4 gs = gp[0], us = up[0];
+#pragma unroll
+        for (int p = 1; p < 8; ++p)
+          if (p < sp.S) {
+            gs.x += gp[p].x; gs.y += gp[p].y; gs.z += gp[p].z; gs.w += gp[p].w;
+            us.x += up[p].x; us.y += up[p].y; us.z += up[p].z; us.w += up[p].w;
+          }
+        const float gv[4] = {gs.x, gs.y, gs.z, gs.w}, uv[4] = {us.x, us.y, us.z, us.w};
+        uint32_t pk[2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const float h0 = gv[2 * j] / (1.0f + __expf(-gv[2 * j])) * uv[2 * j];
+          const float h1 = gv[2 * j + 1] / (1.0f + __expf(-gv[2 * j + 1])) * uv[2 * j + 1];
+          pk[j] = (uint32_t)f32_to_bf16(h0) |
+                  ((uint32_t)f32_to_bf16(h1) << 16);
         }
+        *(uint2 *)((bf16_t *)d.C + (size_t)row * d.ldc + col) = make_uint2(pk[0], pk[1]);
+      } else {
+        float4 pp[8];
+#pragma unroll
+        for (int p = 0; p < 8; ++p)
+          if (p < sp.S) pp[p] = *(const float4 *)(P0 + (size_t)p * PART + part_index(0, c));
+        float4 v = pp[0];
+#pragma unroll
+        for (int p = 1; p < 8; ++p)
+          if (p < sp.S) { v.x += pp[p].x; v.y += pp[p].y; v.z += pp[p].z; v.w += pp[p].w; }
+        *(float4 *)((float *)d.C + (size_t)row * d.ldc + col) = v;
+      }
     }
   }
 }
@@ -436,16 +555,28 @@ int gemm_tiles_upper(const GemmArgs &a, int bm, int bn_out, int max_rows) {
 #endif
 
 template <int BN>
-hipError_t launch_bf16(const GemmArgs &a, bool gate_up, int max_rows, int num_cu, hipStream_t st) {
+hipError_t launch_bf16(const GemmArgs &a0, bool gate_up, int max_rows, int num_cu, hipStream_t st) {
+  static_assert(BN == 256, "the tail reduction assumes 256 x 256 tiles");
+  GemmArgs a = a0;
   const int bn_out = gate_up ? BN / 2 : BN;
   int grid = gemm_tiles_upper(a, BM, bn_out, max_rows);
-  const int cap = num_cu * Cfg<BN>::OCC;
+  int cap = num_cu * Cfg<BN>::OCC;
+  if (cap > kMaxPersistent) cap = kMaxPersistent;
   if (grid > cap) grid = cap;
   if (grid < 1) grid = 1;
-  if (gate_up)
+  a.grid = grid;
+  if (!a.partials) a.split_ok = 0;
+  if (gate_up) {
     hipLaunchKernelGGL((gemm_bf16_kernel<true, BN>), dim3(grid), dim3(256), 0, st, a);
-  else
+    if (a.split_ok)   // at most grid/2 split tiles, BM/kReduceRows items each
+      hipLaunchKernelGGL(gemm_tail_reduce_kernel<true>, dim3(grid * (BM / kReduceRows) / 2 + 1),
+                         dim3(256), 0, st, a);
+  } else {
     hipLaunchKernelGGL((gemm_bf16_kernel<false, BN>), dim3(grid), dim3(256), 0, st, a);
+    if (a.split_ok)
+      hipLaunchKernelGGL(gemm_tail_reduce_kernel<false>, dim3(grid * (BM / kReduceRows) / 2 + 1),
+                         dim3(256), 0, st, a);
+  }
   return hipGetLastError();
 }
 

@@ -37,7 +37,16 @@ struct GemmArgs {
   int c_elt;                       // bytes per C element (h: elt; o: 4)
   const void *sA; const void *sB0; const void *sB1; void *sC;   // shared group
   int s_rows, sN, sK, s_lda, s_ldc;
+  // tail split: the tiles of the last, partial round of the persistent grid may run as S
+  // K-parts whose float32 partial tiles go to `partials` (room for kMaxPersistent tiles)
+  // and are summed by a second kernel; allowed when every group has the same K
+  float *partials;
+  int split_ok;
+  int grid;                         // persistent grid size (set by the launcher)
 };
+
+constexpr int kMaxPersistent = 256;   // persistent GEMM workgroups (one per CU on MI355X)
+constexpr size_t kPartialBytes = (size_t)kMaxPersistent * 256 * 256 * 4;
 
 int router_epad(int E);   // experts padded for the matrix-core router (bf16 x)
 hipError_t launch_router(int dtype, const void *x, const float *w, const float *bias,

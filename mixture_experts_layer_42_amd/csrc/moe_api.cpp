@@ -19,7 +19,7 @@ size_t up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 struct Layout {
   // route scratch
   size_t keys, blk_cnt, blk_base, cnt_pre, off_pre, cand_token, cand_slot, cand_key, slot_pos,
-      colkeys, tok_blk, tok_blk_off, stats_part, w3;
+      colkeys, tok_blk, tok_blk_off, stats_part, w3, partials;
   // routing arrays used when the caller passes no routing struct
   size_t logits, ids, topk_w, kept, counts, offsets, perm_token, perm_w, tok_ptr, tok_pos;
   // activations
@@ -52,6 +52,7 @@ Layout make_layout(const moe_problem &p) {
   L.tok_blk_off = take(nblk * 4);
   L.stats_part = take(nblk * E * 4);
   L.w3 = take(p.dtype == MOE_BF16 && p.E > 8 ? 3 * (size_t)router_epad(p.E) * d * 2 : 0);
+  L.partials = take(p.dtype == MOE_BF16 ? kPartialBytes : 0);
   L.logits = take(T * E * 4);
   L.ids = take(T * k * 4);
   L.topk_w = take(T * k * 4);
@@ -103,6 +104,10 @@ moe_status check_problem(const moe_problem *pp) {
   const int64_t amax = R * (int64_t)(p.d_model > p.d_ff ? p.d_model : p.d_ff);
   const int64_t smax = (int64_t)p.T * (p.d_model > p.d_ff_shared ? p.d_model : p.d_ff_shared);
   if (wmax >= big || amax >= big || smax >= big) return MOE_ERR_UNSUPPORTED;
+  // the bf16 GEMM stores one group's output rows (at most T of them) through a buffer
+  // resource with a 32-bit byte range: T * d_model float32 outputs must stay under 4 GiB
+  if (p.dtype == MOE_BF16 && (int64_t)p.T * p.d_model * 4 >= ((int64_t)1 << 32))
+    return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 
@@ -254,17 +259,20 @@ hipError_t do_gate_up(const moe_problem &p, const void *x_perm, const moe_routin
                       const void *w_gate, const void *w_up, const void *x, const void *ws_gate,
                       const void *ws_up, char *ws, hipStream_t st) {
   const Layout L = make_layout(p);
-  const GemmArgs a = gemm_args(p, r, true, x_perm ? x_perm : x, w_gate, w_up, ws + L.h, x,
-                               ws_gate, ws_up, ws + L.h_shared,
-                               x_perm ? nullptr : r.perm_token);
+  GemmArgs a = gemm_args(p, r, true, x_perm ? x_perm : x, w_gate, w_up, ws + L.h, x, ws_gate,
+                         ws_up, ws + L.h_shared, x_perm ? nullptr : r.perm_token);
+  a.partials = p.dtype == MOE_BF16 ? (float *)(ws + L.partials) : nullptr;
+  a.split_ok = 1;   // every group has K = d_model
   return launch_gemm(a, true, (int)rows_cap(p), num_cus(), st);
 }
 
 hipError_t do_down(const moe_problem &p, const moe_routing &r, const void *w_down,
                    const void *ws_down, void *o_perm, void *o_shared, char *ws, hipStream_t st) {
   const Layout L = make_layout(p);
-  const GemmArgs a = gemm_args(p, r, false, ws + L.h, w_down, nullptr, o_perm, ws + L.h_shared,
-                               ws_down, nullptr, o_shared);
+  GemmArgs a = gemm_args(p, r, false, ws + L.h, w_down, nullptr, o_perm, ws + L.h_shared,
+                         ws_down, nullptr, o_shared);
+  a.partials = p.dtype == MOE_BF16 ? (float *)(ws + L.partials) : nullptr;
+  a.split_ok = (p.d_ff_shared == 0 || p.d_ff_shared == p.d_ff) ? 1 : 0;   // one K for all groups
   return launch_gemm(a, false, (int)rows_cap(p), num_cus(), st);
 }
 

@@ -65,6 +65,9 @@ def ws_status(p):
     (dict(dtype=moe.MOE_F32, y_dtype=moe.MOE_F32, d_model=6), moe.MOE_ERR_UNSUPPORTED),
     (dict(dtype=moe.MOE_F32, y_dtype=moe.MOE_F32, d_model=12, d_ff=5), moe.MOE_OK),
     (dict(routing=1, T=4, k=2, E=8), moe.MOE_OK),
+    # one expert's float32 GEMM output (up to T rows of d_model) must stay under 4 GiB
+    (dict(T=1 << 18, d_model=4096, k=1), moe.MOE_ERR_UNSUPPORTED),
+    (dict(T=(1 << 18) - 64, d_model=4096, k=1), moe.MOE_OK),
 ])
 def test_problem_validation(kw, status):
     st, n = ws_status(good(**kw))

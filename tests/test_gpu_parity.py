@@ -40,6 +40,12 @@ SMALL = {
     "one-token-bf16": C0.with_(dtype="bf16", T=1, d_model=64, d_ff=64),
     "all-dropped-shared-bf16": C0.with_(dtype="bf16", T=96, d_model=64, d_ff=64, d_ff_shared=64,
                                         gamma=1e-6),
+    # routing collapse onto one expert: few tiles on a wide grid, so the grouped GEMMs cut
+    # each tile's K range into 2 to 8 parts summed in order by a second kernel
+    "collapse-ksplit-bf16": C0.with_(dtype="bf16", T=300, d_model=2048, E=32, k=1, d_ff=256,
+                                     bias=("onehot", 30.0)),
+    "collapse-ksplit-shared-bf16": C0.with_(dtype="bf16", T=200, d_model=1024, E=32, k=1,
+                                            d_ff=512, d_ff_shared=512, bias=("onehot", 30.0)),
     "no-renorm-fp32": C0.with_(k=3, renorm_topk=False),
     "k-equals-E-fp32": C0.with_(E=4, k=4, T=50),
     "zipf-drop-fp32": C0.with_(gamma=0.75, bias=("zipf", 1.2), T=160),
