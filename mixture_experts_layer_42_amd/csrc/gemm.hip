@@ -7,16 +7,18 @@
 // K-contiguous (weights in [out, in] layout), so A and B tiles stream along K.
 //
 // bf16 path: persistent workgroups walk a tile list built on the device from the
-// per-expert row counts (no host round trip). A tile is 256 rows x 256 columns, K in
-// steps of 32 (four LDS stages); 4 waves in a 2 x 2 layout each own 128 x 128 of the tile as 4 x 4 blocks
-// of v_mfma_f32_32x32x16_bf16 with float32 accumulators. A and B K-slices are staged in
-// LDS straight from global memory (gfx950 global_load_lds, no register staging), two
-// stages so the next K-slice lands while the current one feeds the MFMAs, 16-byte chunks
-// XOR-swizzled by row so the MFMA fragment reads hit distinct banks. Tiles of one expert that share a weight column are consecutive in the
-// tile list, and consecutive list entries are given to workgroups on the same XCD, so the
-// weight slice is fetched into that XCD's L2 once and reused by every row tile.
-// For gate/up the B tile interleaves 64 gate rows and the matching 64 up rows per wave,
-// so SiLU(gate) * up is formed in registers and only h is written.
+// per-expert row counts (no host round trip). A tile is 256 rows x 256 columns; K goes in
+// slices of 64 through two 64 KB LDS stages (one lands while the other feeds the MFMAs).
+// Waves (4 as 2 x 2 of 128 x 128, or 8 as 2 x 4 of 128 x 64) compute with
+// v_mfma_f32_32x32x16_bf16 into float32 accumulators. Slices are copied from global memory
+// straight into LDS (gfx950 global_load_lds, no register staging); each 1 KB copy covers 8
+// rows x 128 B, i.e. whole 128-byte lines, which streams about twice as fast as half-line
+// rows. 16-byte chunks are XOR-swizzled by row so the MFMA fragment reads hit distinct banks.
+// Tiles of one expert that share a weight column are consecutive in the tile list, and
+// consecutive list entries are given to workgroups on the same XCD, so the weight slice is
+// fetched into that XCD's L2 once and reused by every row tile. For gate/up the B tile
+// interleaves per wave column the gate rows and the matching up rows, so SiLU(gate) * up is
+// formed in registers and only h is written.
 //
 // float32 path (used when the problem dtype is float32): a plain LDS-tiled SIMT GEMM over
 // the same tile list.
@@ -100,7 +102,7 @@ MOE_DEV int xcd_virtual_block() {
 
 // Tail split. With P persistent workgroups and `total` tiles, the first r*P tiles (r whole
 // rounds) run whole; if the remaining L tiles fill at most half a round, each is cut into S
-// K-parts (S a power of two, S*L <= P, S <= 8, each part a multiple of 4 K-steps) so that the
+// K-parts (S a power of two, S*L <= P, S <= 8, each part at least 4 K-slices) so that the
 // last round takes about 1/S of a tile's time. Both the GEMM and the reduction kernel derive
 // the same plan from the device-side tile count.
 struct SplitPlan { int full, L, S; };
@@ -110,36 +112,41 @@ MOE_DEV SplitPlan split_plan(int total, int P, int nk, int ok) {
   const int r = total / P, L = total - r * P;
   if (!ok || L == 0 || 2 * L > P) return sp;
   int S = 1;
-  while (2 * S * L <= P && 2 * S <= 8 && nk % (8 * S) == 0) S *= 2;
+  while (2 * S * L <= P && 2 * S <= 8 && nk % (2 * S) == 0 && nk / (2 * S) >= 4) S *= 2;
   if (S == 1) return sp;
   sp.full = r * P; sp.L = L; sp.S = S;
   return sp;
 }
 
 // ----------------------------------------------------------------------------------------
-// bf16 MFMA kernel, templated on the tile width BN (256 rows x BN columns, K steps of 32).
-//   BN = 256: one workgroup per CU, 4 LDS stages of 32 KB, waves own 128 x 128.
-//   BN = 128: two workgroups per CU, 3 LDS stages of 24 KB each, waves own 128 x 64; while one
-//             workgroup waits at its barrier the other keeps the MFMA pipes busy.
-constexpr int BM = 256, BK = 32;
-constexpr int kRowBytes = BK * 2;                 // 64 B: 4 chunks of 16 B
+// bf16 MFMA kernel. A tile is 256 rows x 256 B-columns, K in slices of 64 staged through two
+// 64 KB LDS buffers. W waves share it: W = 4 as 2 x 2 waves of 128 x 128 (one wave per
+// SIMD, 256 accumulators each), W = 8 as 2 x 4 waves of 128 x 64 (two waves per SIMD, so
+// one wave's LDS reads and barrier waits overlap the other's MFMAs).
+constexpr int BM = 256, BN = 256, BK = 64, NSTAGE = 2;
+constexpr int kRowBytes = BK * 2;                 // 128 B: 8 chunks of 16 B
+constexpr int kSub = BK / 16;                     // k=16 MFMA sub-steps per slice
+constexpr int kMaxWaves = 8;
 
-template <int BN> struct Cfg {
-  static constexpr int NB = BN / 64;              // 32-column MFMA blocks per wave
-  static constexpr int NSTAGE = BN == 256 ? 4 : 3;
-  static constexpr int OCC = BN == 256 ? 1 : 2;   // workgroups per CU
+template <int W> struct Cfg {
+  static constexpr int WN = W / 2;                // wave columns (two wave rows of 128)
+  static constexpr int WCOLS = BN / WN;           // B columns per wave
+  static constexpr int NB = WCOLS / 32;           // 32-column MFMA blocks per wave
   static constexpr int A_BYTES = BM * kRowBytes, B_BYTES = BN * kRowBytes;
-  static constexpr int A_DMA = A_BYTES / 1024 / 4, B_DMA = B_BYTES / 1024 / 4;   // per wave
-  static constexpr int IN_FLIGHT = (NSTAGE - 2) * (A_DMA + B_DMA);   // copies allowed pending
+  static constexpr int A_DMA = A_BYTES / 1024 / W, B_DMA = B_BYTES / 1024 / W;   // per wave
+  static constexpr int DMA = A_DMA + B_DMA;       // 1 KB copies per wave per slice
+  static constexpr int PART_WAVE = 4 * NB * 16 * 64;     // floats of one wave's accumulators
 };
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) const void gbl_void_t;
 
-// LDS byte offset of 16-byte chunk `chunk` (0..3) of tile row `row`: rows of 64 B, chunks
-// XOR-swizzled by (row/4) % 4, so that the 16 rows one quarter-wave of an MFMA fragment read
-// touches cover all 64 banks exactly once.
-MOE_DEV int swz(int row, int chunk) { return row * kRowBytes + ((chunk ^ ((row >> 2) & 3)) << 4); }
+// LDS byte offset of 16-byte chunk `chunk` (0..7) of tile row `row`: rows of 128 B, chunks
+// XOR-swizzled by (row/2) % 8, so that the 16 rows a quarter-wave of an MFMA fragment read
+// touches (same logical chunk) cover all 64 banks exactly once.
+MOE_DEV int swz(int row, int chunk) {
+  return row * kRowBytes + ((chunk ^ ((row >> 1) & 7)) << 4);
+}
 
 // Direct global -> LDS copy of 16 bytes per lane: lane L of the wave writes LDS bytes
 // [lds_base + 16 L, +16). lds_base must be the same in every lane.
@@ -149,57 +156,59 @@ MOE_DEV void g2lds16(const void *g, char *lds_base) {
 
 // The pipeline stages are separate LDS objects, so loads into one stage are never mistaken
 // for writes to the stage being read.
-template <int BN> struct Stage { char a[Cfg<BN>::A_BYTES]; char b[Cfg<BN>::B_BYTES]; };
+struct Stage { char a[BM * kRowBytes]; char b[BN * kRowBytes]; };
 
-template <int BN>
-MOE_DEV void load_frags(const Stage<BN> &st, int lane, int wm, int wn, int ks, bf16x8_t (&af)[4],
-                        bf16x8_t (&bfr)[Cfg<BN>::NB]) {
+// fragments of sub-step ks (k = 16 ks .. 16 ks + 15 of the slice)
+template <int W>
+MOE_DEV void load_frags(const Stage &st, int lane, int wm, int wn, int ks, bf16x8_t (&af)[4],
+                        bf16x8_t (&bfr)[Cfg<W>::NB]) {
   const int chunk = ks * 2 + (lane >> 5);
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb)
     af[mb] = *reinterpret_cast<const bf16x8_t *>(st.a + swz(wm * 128 + mb * 32 + (lane & 31), chunk));
 #pragma unroll
-  for (int nb = 0; nb < Cfg<BN>::NB; ++nb)
-    bfr[nb] = *reinterpret_cast<const bf16x8_t *>(st.b + swz(wn * (BN / 2) + nb * 32 + (lane & 31), chunk));
+  for (int nb = 0; nb < Cfg<W>::NB; ++nb)
+    bfr[nb] = *reinterpret_cast<const bf16x8_t *>(
+        st.b + swz(wn * Cfg<W>::WCOLS + nb * 32 + (lane & 31), chunk));
 }
 
-template <int BN>
-MOE_DEV void mfma_block(const bf16x8_t (&af)[4], const bf16x8_t (&bfr)[Cfg<BN>::NB],
-                        f32x16_t (&acc)[4][Cfg<BN>::NB]) {
+template <int W>
+MOE_DEV void mfma_block(const bf16x8_t (&af)[4], const bf16x8_t (&bfr)[Cfg<W>::NB],
+                        f32x16_t (&acc)[4][Cfg<W>::NB]) {
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-    for (int nb = 0; nb < Cfg<BN>::NB; ++nb)
+    for (int nb = 0; nb < Cfg<W>::NB; ++nb)
       acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mb], bfr[nb], acc[mb][nb], 0, 0, 0);
 }
 
 // keep the instruction order written here (no scheduling across this point)
 MOE_DEV void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
 
-// wait until at most N of this wave's global->LDS copies are still in flight
-template <int N> MOE_DEV void wait_vm() {
-  static_assert(N == 0 || N == 6 || N == 8 || N == 12 || N == 16, "add the count");
-  if constexpr (N == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  else if constexpr (N == 6) asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
-  else if constexpr (N == 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-  else if constexpr (N == 12) asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
-  else asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+// Offset of tile element (tr, tc) (tc a B-tile column) in a partial tile stored in
+// accumulator register order: wave (tr/128)*WN + tc/WCOLS, then block (mb, nb) =
+// (tr%128/32, tc%WCOLS/32), register i = 4*(tr%32/8) + tr%4, lane = tc%32 + 32*(tr%8/4).
+// The row and column parts add, and 4 adjacent columns (tc % 4 == 0) are 4 adjacent floats.
+template <int W> MOE_DEV int part_index(int tr, int tc) {
+  using C = Cfg<W>;
+  const int row_part = (tr >> 7) * C::WN * C::PART_WAVE + ((tr >> 5) & 3) * C::NB * 16 * 64 +
+                       (4 * ((tr >> 3) & 3) + (tr & 3)) * 64 + 32 * ((tr >> 2) & 1);
+  const int col_part = (tc / C::WCOLS) * C::PART_WAVE + ((tc % C::WCOLS) >> 5) * 16 * 64 + (tc & 31);
+  return row_part + col_part;
 }
 
-template <bool GATE_UP, int BN>
-__global__ __launch_bounds__(256, Cfg<BN>::OCC) void gemm_bf16_kernel(GemmArgs args) {
-  using C = Cfg<BN>;
-  constexpr int NB = C::NB, NSTAGE = C::NSTAGE;
-  __shared__ Stage<BN> st0, st1, st2;
-  __shared__ __attribute__((aligned(16))) char st3_raw[NSTAGE == 4 ? sizeof(Stage<BN>) : 16];
-  Stage<BN> &st3 = *reinterpret_cast<Stage<BN> *>(st3_raw);   // used only with 4 stages
+template <bool GATE_UP, int W>
+__global__ __launch_bounds__(64 * W, 1) void gemm_bf16_kernel(GemmArgs args) {
+  using C = Cfg<W>;
+  constexpr int NB = C::NB;
+  __shared__ Stage st0, st1;
   __shared__ int tstart[kMaxGroups + 1];
-  __shared__ int sm[256 / 64 + 1];
+  __shared__ int sm[kMaxWaves + 1];
   constexpr int BNOUT = GATE_UP ? BN / 2 : BN;   // output columns per tile (h or o)
   const int G = build_tile_table<BM, BNOUT>(args, tstart, sm);
   const int total = tstart[G];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int wm = wv >> 1, wn = wv & 1;
+  const int wm = wv / C::WN, wn = wv % C::WN;
 
   const SplitPlan sp = split_plan(total, gridDim.x, args.K / BK, args.split_ok);
   const int units = sp.full + sp.L * sp.S;
@@ -218,33 +227,34 @@ __global__ __launch_bounds__(256, Cfg<BN>::OCC) void gemm_bf16_kernel(GemmArgs a
     const int m0 = m_tile * BM;
     const int nk = (d.K / BK) / nparts;   // K-steps of this unit
     const int k_begin = part * nk;         // first K-step of this unit
-    // Loader: wave wv fills A rows wv*64 .. +63 and B rows wv*(BN/4) .. +BN/4-1 with copies of
-    // 1 KB (16 rows of 64 B); lane L fetches row r0 + L/4, physical chunk L%4, i.e. logical
-    // K-chunk (L%4) ^ ((row/4)%4). For gate/up the B tile holds, per wave column wn, BN/4 gate
-    // rows then the matching BN/4 up rows (h columns n_tile*BN/2 + wn*BN/4 + i), so the B rows
-    // a wave loads are all gate (wv even) or all up (wv odd).
+    // Loader: wave wv fills A rows wv*BM/W .. and B rows wv*BN/W .. with copies of 1 KB
+    // (8 rows of 128 B); lane L fetches row r0 + L/8, physical chunk L%8, i.e. logical
+    // K-chunk (L%8) ^ ((row/2)%8). For gate/up the B tile holds, per wave column wn,
+    // WCOLS/2 gate rows then the matching WCOLS/2 up rows (h columns n_tile*128 +
+    // wn*WCOLS/2 + j), so the B rows a wave loads are all gate (wv even) or all up (wv odd).
     const int wvu = __builtin_amdgcn_readfirstlane(wv);   // wave-uniform, kept in SGPRs
     const char *Ab = (const char *)d.A;
     const char *Bb = (const char *)((GATE_UP && (wvu & 1)) ? d.B1 : d.B0);
     uint32_t aoff[C::A_DMA], boff[C::B_DMA];   // per-lane byte offsets from the slice bases
 #pragma unroll
     for (int i = 0; i < C::A_DMA; ++i) {
-      const int r = wvu * (BM / 4) + i * 16 + (lane >> 2);
-      const int c = (lane & 3) ^ ((r >> 2) & 3);
+      const int r = wvu * (BM / W) + i * 8 + (lane >> 3);
+      const int c = (lane & 7) ^ ((r >> 1) & 7);
       int arow = min(m0 + r, d.rows - 1);
       if (d.amap) arow = d.amap[arow];   // dispatch gather folded into the operand load
       aoff[i] = ((uint32_t)arow * (uint32_t)d.lda + c * 8) * 2u;
     }
 #pragma unroll
     for (int i = 0; i < C::B_DMA; ++i) {
-      const int r = wvu * (BN / 4) + i * 16 + (lane >> 2);
-      const int c = (lane & 3) ^ ((r >> 2) & 3);
-      const int n = GATE_UP ? n_tile * (BN / 2) + (wvu >> 1) * (BN / 4) + (r & (BN / 4 - 1))
+      const int r = wvu * (BN / W) + i * 8 + (lane >> 3);
+      const int c = (lane & 7) ^ ((r >> 1) & 7);
+      const int n = GATE_UP ? n_tile * (BN / 2) + (wvu >> 1) * (C::WCOLS / 2) +
+                                  (r & (C::WCOLS / 2 - 1))
                             : n_tile * BN + r;
       boff[i] = ((uint32_t)min(n, d.N - 1) * (uint32_t)d.K + c * 8) * 2u;
     }
     const int aofs = wvu * C::A_DMA * 1024, bofs = wvu * C::B_DMA * 1024;
-    auto issue = [&](Stage<BN> &s, int kt) {
+    auto issue = [&](Stage &s, int kt) {
       const char *a = Ab + (size_t)(k_begin + kt) * kRowBytes;
       const char *b = Bb + (size_t)(k_begin + kt) * kRowBytes;
 #pragma unroll
@@ -260,75 +270,67 @@ __global__ __launch_bounds__(256, Cfg<BN>::OCC) void gemm_bf16_kernel(GemmArgs a
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-    // Pipeline. Slices go global -> LDS NSTAGE-1 ahead. A slice is two k=16 sub-steps. Step kt
-    // holds the fragments of sub-step 0 of slice kt in registers on entry. Its first half
-    // issues the sub-step-0 MFMAs with the LDS reads of sub-step 1 slotted between them; then
-    // it waits for slice kt+1 and passes the barrier; its second half issues the sub-step-1
-    // MFMAs with the copy of slice kt+NSTAGE-1 (into the stage slice kt-1 used) and the LDS
-    // reads of sub-step 0 of slice kt+1 slotted between them. With one wave per SIMD, memory
-    // instructions only overlap the matrix pipe when they sit between MFMAs. Every wave has
-    // read slice kt-1 completely before it reaches the barrier of step kt, so the refill never
-    // overwrites data still to be read.
+    // Pipeline. Slice s lives in stage s % 2. Step kt waits until slice kt has landed,
+    // passes the barrier (every wave has its last fragments of slice kt-1 in registers by
+    // then, so that stage is free), issues the copy of slice kt+1 into it, and runs the
+    // MFMAs: those of the last sub-step of slice kt-1, then sub-steps 0..2 of slice kt, each
+    // with the LDS reads of the next sub-step (and, in the first, the copies) slotted
+    // between them. The last sub-step of slice kt runs after the next barrier. Fragments
+    // alternate between two register sets (even and odd sub-steps).
     bf16x8_t fa0[4], fb0[NB], fa1[4], fb1[NB];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) fa1[i] = bf16x8_t{};   // "slice -1": contributes 0 * 0
+#pragma unroll
+    for (int i = 0; i < NB; ++i) fb1[i] = bf16x8_t{};
     issue(st0, 0);
-    if (nk > 1) issue(st1, 1);
-    if (NSTAGE == 4 && nk > 2) issue(st2, 2);
-    if (nk > NSTAGE - 2) wait_vm<C::IN_FLIGHT>();
-    else wait_vm<0>();
-    __builtin_amdgcn_s_barrier();
-    load_frags<BN>(st0, lane, wm, wn, 0, fa0, fb0);
-    // one K-step (slice kt); the refill index is clamped to the last slice
-    auto steady = [&](Stage<BN> &cur, Stage<BN> &nxt, Stage<BN> &refill, int kt) {
-      sched_fence();
-      load_frags<BN>(cur, lane, wm, wn, 1, fa1, fb1);
-      mfma_block<BN>(fa0, fb0, acc);
+    // MFMAs of (fa, fb) with the fragment reads of the next sub-step between them
+    auto sub = [&](const bf16x8_t (&fa)[4], const bf16x8_t (&fb)[NB], const Stage &cur, int ks,
+                   bf16x8_t (&na)[4], bf16x8_t (&nb)[NB]) {
+      load_frags<W>(cur, lane, wm, wn, ks, na, nb);
+      mfma_block<W>(fa, fb, acc);
 #pragma unroll
-      for (int i = 0; i < 4 + NB; ++i) {        // 4*NB MFMAs, 4+NB LDS reads
-        __builtin_amdgcn_sched_group_barrier(0x008, (4 * NB) / (4 + NB), 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      }
-      sched_fence();
-      wait_vm<C::IN_FLIGHT - (C::A_DMA + C::B_DMA)>();
-      __builtin_amdgcn_s_barrier();
-      sched_fence();
-      // past the last slice the copy re-reads the last slice into the stage nobody reads any
-      // more: branch-free, in bounds, and the wait counts stay the same every step
-      issue(refill, min(kt + NSTAGE - 1, nk - 1));
-      load_frags<BN>(nxt, lane, wm, wn, 0, fa0, fb0);
-      mfma_block<BN>(fa1, fb1, acc);
-#pragma unroll
-      for (int i = 0; i < 4 + NB; ++i) {        // copies and reads between the MFMAs
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
-        __builtin_amdgcn_sched_group_barrier(0x020, 1, 1);
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
+      for (int i = 0; i < 4 * NB; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (i < 4 + NB) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       }
       sched_fence();
     };
-    // Four steps per iteration cycle the four stages. The loop body is one branch-free block,
-    // so the compiler's wait counts stay exact inside it (a join would make it drain every
-    // copy in flight); the 1-3 steps of a K that is not a multiple of 4 slices follow it. The
-    // last steps read a stale next stage they never use, and their refills re-read the last
-    // slice, so every wait count holds as in the middle.
-    static_assert(NSTAGE == 4, "the unrolled loop below cycles four stages");
+    auto step = [&](Stage &cur, Stage &refill, int kt) {
+      sched_fence();
+      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");   // slice kt has landed
+      __builtin_amdgcn_s_barrier();
+      sched_fence();
+      issue(refill, min(kt + 1, nk - 1));   // past the end: re-read the last slice
+      load_frags<W>(cur, lane, wm, wn, 0, fa0, fb0);
+      mfma_block<W>(fa1, fb1, acc);          // last sub-step of slice kt-1
+#pragma unroll
+      for (int i = 0; i < 4 * NB; ++i) {     // copies and reads between the MFMAs
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x020, C::DMA / (4 * NB), 0);
+        if (i < 4 + NB) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      sched_fence();
+      sub(fa0, fb0, cur, 1, fa1, fb1);
+      sub(fa1, fb1, cur, 2, fa0, fb0);
+      sub(fa0, fb0, cur, 3, fa1, fb1);
+    };
+    static_assert(kSub == 4 && NSTAGE == 2, "the step above runs four sub-steps, two stages");
+    static_assert(C::DMA % (4 * NB) == 0, "copies spread evenly over the first MFMAs");
+    // Two steps per iteration alternate the stages. The loop body is one branch-free block,
+    // so the compiler's wait counts stay exact inside it; an odd last step follows it.
     int kt = 0;
-    for (; kt + 4 <= nk; kt += 4) {
-      steady(st0, st1, st3, kt);
-      steady(st1, st2, st0, kt + 1);
-      steady(st2, st3, st1, kt + 2);
-      steady(st3, st0, st2, kt + 3);
+    for (; kt + 2 <= nk; kt += 2) {
+      step(st0, st1, kt);
+      step(st1, st0, kt + 1);
     }
-    if (kt < nk) {
-      steady(st0, st1, st3, kt);
-      if (kt + 1 < nk) steady(st1, st2, st0, kt + 1);
-      if (kt + 2 < nk) steady(st2, st3, st1, kt + 2);
-    }
-    wait_vm<0>();
+    if (kt < nk) step(st0, st1, kt);
+    mfma_block<W>(fa1, fb1, acc);   // last sub-step of the last slice
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the surplus copy of the last step
     __syncthreads();   // every wave is done with every stage before the next tile's loads
     if (nparts > 1) {
       // K-part of a split tile: the raw accumulators in register order (wave, mb, nb, i,
       // lane), so each store is 256 contiguous bytes; the reduction maps them back
-      float *Pt = args.partials + (size_t)(u - sp.full) * (BM * BN) + wv * (64 * 4 * NB * 16) + lane;
+      float *Pt = args.partials + (size_t)(u - sp.full) * (BM * BN) + wv * C::PART_WAVE + lane;
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
@@ -346,11 +348,11 @@ __global__ __launch_bounds__(256, Cfg<BN>::OCC) void gemm_bf16_kernel(GemmArgs a
     int lo = lane;
     asm volatile("" : "+v"(lo));
     constexpr int CE = GATE_UP ? 2 : 4;   // bytes per output element
+    constexpr int OB = GATE_UP ? NB / 2 : NB;   // output blocks per wave row
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
         d.C, (short)0, (int)((uint32_t)d.rows * (uint32_t)d.ldc * CE), 0x00020000);
-    const int cw = n_tile * BNOUT + wn * (BNOUT / 2);   // first output column of this wave
-    const int nbv = (d.N - cw) >= (GATE_UP ? NB / 2 : NB) * 32 ? (GATE_UP ? NB / 2 : NB)
-                                                               : (d.N - cw) / 32;   // live blocks
+    const int cw = n_tile * BNOUT + wn * (OB * 32);   // first output column of this wave
+    const int nbv = (d.N - cw) >= OB * 32 ? OB : (d.N - cw) / 32;   // live blocks
     const uint32_t rowb = (uint32_t)d.ldc * CE;
     // running byte offset of this lane's current row, advanced row by row (kept opaque so the
     // compiler does not expand it into one live offset per row)
@@ -360,10 +362,10 @@ __global__ __launch_bounds__(256, Cfg<BN>::OCC) void gemm_bf16_kernel(GemmArgs a
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
 #pragma unroll
-        for (int nb = 0; nb < (GATE_UP ? NB / 2 : NB); ++nb) {
+        for (int nb = 0; nb < OB; ++nb) {
           if (nb < nbv) {
             if (GATE_UP) {
-              const float gv = acc[mb][nb][i], uv = acc[mb][nb + NB / 2][i];
+              const float gv = acc[mb][nb][i], uv = acc[mb][nb + OB][i];
               const float h = gv / (1.0f + __expf(-gv)) * uv;
               __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(h), rs, (int)(roff + nb * 32 * CE),
                                                     0, 0);
@@ -389,26 +391,15 @@ __global__ __launch_bounds__(256, Cfg<BN>::OCC) void gemm_bf16_kernel(GemmArgs a
 // (args.grid), so any grid of this kernel sees the same split.
 constexpr int kReduceRows = 32;
 
-// Offset of tile element (tr, tc) in a partial tile stored in accumulator register order:
-// wave (tr/128)*2 + tc/128, block mb = tr%128/32, nb = tc%128/32, register
-// i = 4*(tr%32/8) + tr%4, lane = tc%32 + 32*(tr%8/4). The row and column parts add, and
-// 4 adjacent columns (tc % 4 == 0) are 4 adjacent floats.
-MOE_DEV int part_index(int tr, int tc) {
-  const int row_part = (tr >> 7) * 2 * 16384 + ((tr >> 5) & 3) * 4 * 16 * 64 +
-                       (4 * ((tr >> 3) & 3) + (tr & 3)) * 64 + 32 * ((tr >> 2) & 1);
-  const int col_part = (tc >> 7) * 16384 + ((tc >> 5) & 3) * 16 * 64 + (tc & 31);
-  return row_part + col_part;
-}
-
-template <bool GATE_UP>
+template <bool GATE_UP, int W>
 __global__ __launch_bounds__(256) void gemm_tail_reduce_kernel(GemmArgs args) {
-  constexpr int BN = 256;
+  using C = Cfg<W>;
   constexpr int BNOUT = GATE_UP ? BN / 2 : BN;
   constexpr int TPR = BNOUT / 4;        // threads per row
   constexpr int RPP = 256 / TPR;        // rows per pass
   constexpr int PART = BM * BN;         // floats per partial tile
   __shared__ int tstart[kMaxGroups + 1];
-  __shared__ int sm[256 / 64 + 1];
+  __shared__ int sm[kMaxWaves + 1];
   const int G = build_tile_table<BM, BNOUT>(args, tstart, sm);
   const SplitPlan sp = split_plan(tstart[G], args.grid, args.K / BK, args.split_ok);
   const int items = sp.L * (BM / kReduceRows);
@@ -426,11 +417,12 @@ __global__ __launch_bounds__(256) void gemm_tail_reduce_kernel(GemmArgs args) {
     for (int rr = threadIdx.x / TPR; rr < kReduceRows; rr += RPP) {
       const int tr = r0 + rr, row = m_tile * BM + tr;
       if (row >= d.rows) break;
-      const float *P0 = args.partials + (size_t)l * sp.S * PART + part_index(tr, 0);
+      const float *P0 = args.partials + (size_t)l * sp.S * PART + part_index<W>(tr, 0);
       if (GATE_UP) {
-        // h column c: gate sum at B-tile column (c/64)*128 + c%64, up sum 64 columns further
-        const int tc = (c >> 6) * 128 + (c & 63);
-        const int og = part_index(0, tc), ou = part_index(0, tc + 64);
+        // h column c: gate sum at B-tile column (c / (WCOLS/2)) * WCOLS + c % (WCOLS/2), up
+        // sum WCOLS/2 columns further
+        const int tc = (c / (C::WCOLS / 2)) * C::WCOLS + c % (C::WCOLS / 2);
+        const int og = part_index<W>(0, tc), ou = part_index<W>(0, tc + C::WCOLS / 2);
         float4 gp[8], up[8];
 #pragma unroll
         for (int p = 0; p < 8; ++p)
@@ -451,15 +443,14 @@ __global__ __launch_bounds__(256) void gemm_tail_reduce_kernel(GemmArgs args) {
         for (int j = 0; j < 2; ++j) {
           const float h0 = gv[2 * j] / (1.0f + __expf(-gv[2 * j])) * uv[2 * j];
           const float h1 = gv[2 * j + 1] / (1.0f + __expf(-gv[2 * j + 1])) * uv[2 * j + 1];
-          pk[j] = (uint32_t)f32_to_bf16(h0) |
-                  ((uint32_t)f32_to_bf16(h1) << 16);
+          pk[j] = (uint32_t)f32_to_bf16(h0) | ((uint32_t)f32_to_bf16(h1) << 16);
         }
         *(uint2 *)((bf16_t *)d.C + (size_t)row * d.ldc + col) = make_uint2(pk[0], pk[1]);
       } else {
         float4 pp[8];
 #pragma unroll
         for (int p = 0; p < 8; ++p)
-          if (p < sp.S) pp[p] = *(const float4 *)(P0 + (size_t)p * PART + part_index(0, c));
+          if (p < sp.S) pp[p] = *(const float4 *)(P0 + (size_t)p * PART + part_index<W>(0, c));
         float4 v = pp[0];
 #pragma unroll
         for (int p = 1; p < 8; ++p)
@@ -479,7 +470,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs args) {
   __shared__ float As[TK][TM + 4];
   __shared__ float Bs[2][TK][TN + 4];
   __shared__ int tstart[kMaxGroups + 1];
-  __shared__ int sm[256 / 64 + 1];
+  __shared__ int sm[kMaxWaves + 1];
   const int G = build_tile_table<TM, TN>(args, tstart, sm);
   const int total = tstart[G];
   const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
@@ -550,39 +541,38 @@ int gemm_tiles_upper(const GemmArgs &a, int bm, int bn_out, int max_rows) {
   return (int)(t > (1 << 30) ? (1 << 30) : t);
 }
 
-#ifndef MOE_GEMM_BN
-#define MOE_GEMM_BN 256
+#ifndef MOE_GEMM_WAVES
+#define MOE_GEMM_WAVES 8
 #endif
 
-template <int BN>
+template <int W>
 hipError_t launch_bf16(const GemmArgs &a0, bool gate_up, int max_rows, int num_cu, hipStream_t st) {
-  static_assert(BN == 256, "the tail reduction assumes 256 x 256 tiles");
   GemmArgs a = a0;
   const int bn_out = gate_up ? BN / 2 : BN;
   int grid = gemm_tiles_upper(a, BM, bn_out, max_rows);
-  int cap = num_cu * Cfg<BN>::OCC;
+  int cap = num_cu;   // one workgroup per CU (the four LDS stages take 128 KB)
   if (cap > kMaxPersistent) cap = kMaxPersistent;
   if (grid > cap) grid = cap;
   if (grid < 1) grid = 1;
   a.grid = grid;
   if (!a.partials) a.split_ok = 0;
+  // at most grid/2 split tiles, BM/kReduceRows reduction items each
+  const int rgrid = grid * (BM / kReduceRows) / 2 + 1;
   if (gate_up) {
-    hipLaunchKernelGGL((gemm_bf16_kernel<true, BN>), dim3(grid), dim3(256), 0, st, a);
-    if (a.split_ok)   // at most grid/2 split tiles, BM/kReduceRows items each
-      hipLaunchKernelGGL(gemm_tail_reduce_kernel<true>, dim3(grid * (BM / kReduceRows) / 2 + 1),
-                         dim3(256), 0, st, a);
-  } else {
-    hipLaunchKernelGGL((gemm_bf16_kernel<false, BN>), dim3(grid), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((gemm_bf16_kernel<true, W>), dim3(grid), dim3(64 * W), 0, st, a);
     if (a.split_ok)
-      hipLaunchKernelGGL(gemm_tail_reduce_kernel<false>, dim3(grid * (BM / kReduceRows) / 2 + 1),
-                         dim3(256), 0, st, a);
+      hipLaunchKernelGGL((gemm_tail_reduce_kernel<true, W>), dim3(rgrid), dim3(256), 0, st, a);
+  } else {
+    hipLaunchKernelGGL((gemm_bf16_kernel<false, W>), dim3(grid), dim3(64 * W), 0, st, a);
+    if (a.split_ok)
+      hipLaunchKernelGGL((gemm_tail_reduce_kernel<false, W>), dim3(rgrid), dim3(256), 0, st, a);
   }
   return hipGetLastError();
 }
 
 hipError_t launch_gemm(const GemmArgs &a, bool gate_up, int max_rows, int num_cu,
                        hipStream_t st) {
-  if (a.elt == 2) return launch_bf16<MOE_GEMM_BN>(a, gate_up, max_rows, num_cu, st);
+  if (a.elt == 2) return launch_bf16<MOE_GEMM_WAVES>(a, gate_up, max_rows, num_cu, st);
   int grid = gemm_tiles_upper(a, 64, 64, max_rows);
   if (grid > 4 * num_cu) grid = 4 * num_cu;
   if (grid < 1) grid = 1;
