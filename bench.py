@@ -55,6 +55,20 @@ def algorithmic(cfg, n_kept):
     return dict(gate_up=gate_up, down=down, route=route, dispatch=dispatch, combine=combine)
 
 
+def gemm_hbm_bytes(cfg, counts):
+    """Bytes each grouped GEMM must move at least: the weights of every expert with rows
+    (and the shared expert), the rows it reads and the rows it writes, each once."""
+    import numpy as np
+    d, f, fs, T = cfg.d_model, cfg.d_ff, cfg.d_ff_shared, cfg.T
+    elt = 2 if cfg.dtype == "bf16" else 4
+    used = int(np.count_nonzero(counts))
+    rows = int(np.sum(counts))
+    gate_up = (used * 2 * f * d + 2 * fs * d) * elt + (rows + (T if fs else 0)) * d * elt \
+        + (rows * f + T * fs) * elt
+    down = (used * f * d + fs * d) * elt + (rows * f + T * fs) * elt + (rows + (T if fs else 0)) * d * 4
+    return dict(gate_up=float(gate_up), down=float(down))
+
+
 def cpu_baseline(inp, sample_tokens=0, target_s=20.0):
     """Time the CPU oracle (float64 numpy) on the first N tokens of the workload; routing is
     always computed over all T tokens, as the method requires. Unless N is given, a 256-token
@@ -177,6 +191,7 @@ def main():
     stage_avg = stage_ms.mean(axis=0)
     n_kept = int(rb.offsets[-1].item())
     work = algorithmic(cfg, n_kept)
+    gemm_bytes = gemm_hbm_bytes(cfg, rb.counts.cpu().numpy())
     ms_per_step = total_ms / args.steps
     value = cfg.T / (ms_per_step * 1e-3)
 
@@ -198,6 +213,10 @@ def main():
         elif name in ("gate_up", "down"):
             tf = work[name] / (stage_avg[i] * 1e-3) / 1e12
             ent.update(tflops=round(tf, 1), mfma_frac=round(tf / PEAK_BF16_TFLOPS, 4))
+            # the HBM view (the bound when few rows reach each expert): weights of the
+            # experts that received rows, plus the activations read and written once
+            gbs = gemm_bytes[name] / (stage_avg[i] * 1e-3) / 1e9
+            ent.update(gbs=round(gbs, 1), hbm_frac=round(gbs / PEAK_HBM_GBS, 4))
         else:
             gbs = work[name] / (stage_avg[i] * 1e-3) / 1e9
             ent.update(gbs=round(gbs, 1), hbm_frac=round(gbs / PEAK_HBM_GBS, 4))

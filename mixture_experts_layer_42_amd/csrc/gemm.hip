@@ -462,6 +462,237 @@ __global__ __launch_bounds__(256) void gemm_tail_reduce_kernel(GemmArgs args) {
 }
 
 // ----------------------------------------------------------------------------------------
+// Skinny path: groups of at most 64 rows (decode-shaped batches). Every weight element is
+// read once, so the GEMM is bound by streaming the weights from HBM; a 256-row tile would
+// spend its MFMAs on padding. A unit is 32*MB rows x 256 B-columns x one K part of a group;
+// 4 waves own 64 B-columns each (for gate/up 32 gate and the matching 32 up columns), K in
+// slices of 64 through three LDS stages. With S > 1 K parts, each unit writes float32 sums
+// to the partial buffer and gemm_skinny_reduce_kernel adds the parts in order.
+struct SkinnyPlan { int mb, S, nt, snt, pitch; };
+
+SkinnyPlan skinny_plan(const GemmArgs &a, bool gate_up) {
+  SkinnyPlan sp{0, 1, 0, 0, 0};
+  if (a.elt != 2 || a.max_group_rows > kSkinnyRows) return sp;
+  sp.mb = a.max_group_rows <= 32 ? 1 : 2;
+  const int bno = gate_up ? BN / 2 : BN;   // output columns per unit
+  sp.nt = (a.N + bno - 1) / bno;
+  sp.snt = a.s_rows > 0 ? (a.sN + bno - 1) / bno : 0;
+  const int used = a.E < a.rcap ? a.E : a.rcap;   // groups that can receive rows
+  const int tiles = used * sp.nt + sp.snt;
+  const int nk = a.K / BK, snk = a.s_rows > 0 ? a.sK / BK : nk;
+  int S = 1;
+  while (S < 16 && tiles * S < 1024 && nk % (2 * S) == 0 && snk % (2 * S) == 0 &&
+         nk / (2 * S) >= 2 && snk / (2 * S) >= 2)
+    S *= 2;
+  sp.S = S;
+  const int nmax = a.s_rows > 0 && a.sN > a.N ? a.sN : a.N;
+  sp.pitch = (gate_up ? 2 : 1) * nmax;
+  return sp;
+}
+
+size_t skinny_partial_bytes(const GemmArgs &a, bool gate_up) {
+  const SkinnyPlan sp = skinny_plan(a, gate_up);
+  if (sp.mb == 0 || sp.S == 1) return 0;
+  return (size_t)sp.S * (size_t)(a.rcap + a.s_rows) * sp.pitch * 4;
+}
+
+template <int N> MOE_DEV void wait_vm_n() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
+
+template <int MB> struct SkStage { char a[32 * MB * kRowBytes]; char b[BN * kRowBytes]; };
+
+template <bool GATE_UP, int MB>
+__global__ __launch_bounds__(256, 1) void gemm_skinny_kernel(GemmArgs args) {
+  constexpr int SBM = 32 * MB;
+  constexpr int DMA = MB + 8;   // 1 KB copies per wave per slice: A MB, B 8
+  constexpr int BNOUT = GATE_UP ? BN / 2 : BN;
+  __shared__ SkStage<MB> st0, st1, st2;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int wvu = __builtin_amdgcn_readfirstlane(wv);
+  const int G = args.E + (args.s_rows > 0 ? 1 : 0);
+  const int S = args.sk_S;
+  const int ntmax = args.s_rows > 0 && args.sN > args.N ? (args.sN + BNOUT - 1) / BNOUT
+                                                         : (args.N + BNOUT - 1) / BNOUT;
+  const int units = G * ntmax * S;
+  for (int u = blockIdx.x; u < units; u += gridDim.x) {
+    const int g = u / (ntmax * S), n_tile = (u / S) % ntmax, part = u % S;
+    const GroupDesc d = group_desc(args, g);
+    if (d.rows == 0 || n_tile * BNOUT >= d.N) continue;   // uniform over the workgroup
+    const int nk = (d.K / BK) / S, k_begin = part * nk;
+    const char *Ab = (const char *)d.A;
+    uint32_t aoff[MB], boff[8];
+#pragma unroll
+    for (int i = 0; i < MB; ++i) {
+      const int r = (wvu * MB + i) * 8 + (lane >> 3);
+      const int c = (lane & 7) ^ ((r >> 1) & 7);
+      int arow = min(r, d.rows - 1);
+      if (d.amap) arow = d.amap[arow];
+      aoff[i] = ((uint32_t)arow * (uint32_t)d.lda + c * 8) * 2u;
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int r = wvu * 64 + i * 8 + (lane >> 3);
+      const int c = (lane & 7) ^ ((r >> 1) & 7);
+      const int n = GATE_UP ? n_tile * BNOUT + wvu * 32 + (i & 3) * 8 + (lane >> 3)
+                            : n_tile * BN + r;
+      boff[i] = ((uint32_t)min(n, d.N - 1) * (uint32_t)d.K + c * 8) * 2u;
+    }
+    const char *Bg = (const char *)d.B0;
+    const char *Bu = (const char *)(GATE_UP ? d.B1 : d.B0);
+    auto issue = [&](SkStage<MB> &s, int kt) {
+      const size_t ko = (size_t)(k_begin + kt) * kRowBytes;
+#pragma unroll
+      for (int i = 0; i < MB; ++i) g2lds16(Ab + ko + aoff[i], s.a + (wvu * MB + i) * 1024);
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        g2lds16((GATE_UP && i >= 4 ? Bu : Bg) + ko + boff[i], s.b + (wvu * 8 + i) * 1024);
+    };
+    f32x16_t acc[MB][2];
+#pragma unroll
+    for (int m = 0; m < MB; ++m)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[m][j][v] = 0.f;
+    issue(st0, 0);
+    issue(st1, min(1, nk - 1));
+    auto step = [&](const SkStage<MB> &cur, SkStage<MB> &refill, int kt) {
+      sched_fence();
+      wait_vm_n<DMA>();                            // slice kt has landed (kt+1 may not)
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      sched_fence();
+      issue(refill, min(kt + 2, nk - 1));           // past the end: re-read the last slice
+#pragma unroll
+      for (int ks = 0; ks < kSub; ++ks) {
+        const int chunk = ks * 2 + (lane >> 5);
+        bf16x8_t fa[MB], fb[2];
+#pragma unroll
+        for (int m = 0; m < MB; ++m)
+          fa[m] = *reinterpret_cast<const bf16x8_t *>(cur.a + swz(m * 32 + (lane & 31), chunk));
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          fb[j] = *reinterpret_cast<const bf16x8_t *>(cur.b + swz(wv * 64 + j * 32 + (lane & 31), chunk));
+#pragma unroll
+        for (int m = 0; m < MB; ++m)
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+            acc[m][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[m], fb[j], acc[m][j], 0, 0, 0);
+      }
+      sched_fence();
+    };
+    int kt = 0;
+    for (; kt + 3 <= nk; kt += 3) {
+      step(st0, st2, kt);
+      step(st1, st0, kt + 1);
+      step(st2, st1, kt + 2);
+    }
+    if (kt < nk) {
+      step(st0, st2, kt);
+      if (kt + 1 < nk) step(st1, st0, kt + 1);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();   // every wave is done with every stage before the next unit's copies
+    // lane (c, r4) of block (m, j) holds column c of rows m*32 + r4*4 + {0..3} + 8q
+    if (S == 1) {
+      constexpr int CE = GATE_UP ? 2 : 4;
+      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+          d.C, (short)0, (int)((uint32_t)d.rows * (uint32_t)d.ldc * CE), 0x00020000);
+#pragma unroll
+      for (int j = 0; j < (GATE_UP ? 1 : 2); ++j) {
+        const int col = GATE_UP ? n_tile * BNOUT + wv * 32 + (lane & 31)
+                                : n_tile * BN + wv * 64 + j * 32 + (lane & 31);
+        if (col - (lane & 31) >= d.N) continue;   // whole 32-column block past N
+#pragma unroll
+        for (int m = 0; m < MB; ++m)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int row = m * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+            const uint32_t off = ((uint32_t)row * d.ldc + col) * CE;
+            if (GATE_UP) {
+              const float gv = acc[m][0][i], uv = acc[m][1][i];
+              __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(gv / (1.0f + __expf(-gv)) * uv),
+                                                    rs, (int)off, 0, 0);
+            } else {
+              __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[m][j][i]), rs, (int)off,
+                                                    0, 0);
+            }
+          }
+      }
+    } else {
+      const int prow0 = g < args.E ? args.offsets[g] : args.rcap;
+      float *P = args.partials + ((size_t)part * (args.rcap + args.s_rows) + prow0) * args.sk_pitch;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        // gate/up: gate sums in columns [0, pitch/2), up sums in [pitch/2, pitch)
+        const int col = GATE_UP ? (j ? args.sk_pitch / 2 : 0) + n_tile * BNOUT + wv * 32 + (lane & 31)
+                                : n_tile * BN + wv * 64 + j * 32 + (lane & 31);
+        const int ncol = GATE_UP ? n_tile * BNOUT + wv * 32 : n_tile * BN + wv * 64 + j * 32;
+        if (ncol >= d.N) continue;
+#pragma unroll
+        for (int m = 0; m < MB; ++m)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int row = m * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+            if (row < d.rows) P[(size_t)row * args.sk_pitch + col] = acc[m][j][i];
+          }
+      }
+    }
+  }
+}
+
+// Sum of the skinny path's K parts, in part order, then the same epilogue. One item = 4
+// adjacent output columns of one row (routed rows below rcap, shared rows from rcap on).
+template <bool GATE_UP>
+__global__ __launch_bounds__(256) void gemm_skinny_reduce_kernel(GemmArgs args) {
+  const int S = args.sk_S, pitch = args.sk_pitch;
+  const int rows_total = args.rcap + args.s_rows;
+  const int q = GATE_UP ? pitch / 2 / 4 : pitch / 4;   // column quads per row
+  const int routed = args.offsets[args.E];
+  const size_t part = (size_t)rows_total * pitch;
+  for (int it = blockIdx.x * blockDim.x + threadIdx.x; it < rows_total * q;
+       it += gridDim.x * blockDim.x) {
+    const int prow = it / q, c = (it % q) * 4;
+    char *C;
+    int ldc, N;
+    if (prow < args.rcap) {
+      if (prow >= routed) continue;
+      C = (char *)args.C + (size_t)prow * args.ldc * args.c_elt; ldc = args.ldc; N = args.N;
+    } else {
+      C = (char *)args.sC + (size_t)(prow - args.rcap) * args.s_ldc * args.c_elt;
+      ldc = args.s_ldc; N = args.sN;
+    }
+    (void)ldc;
+    if (c >= N) continue;
+    const float *P = args.partials + (size_t)prow * pitch + c;
+    if (GATE_UP) {
+      float4 gs = make_float4(0.f, 0.f, 0.f, 0.f), us = gs;
+      for (int p = 0; p < S; ++p) {
+        const float4 gp = *(const float4 *)(P + p * part);
+        const float4 up = *(const float4 *)(P + p * part + pitch / 2);
+        gs.x += gp.x; gs.y += gp.y; gs.z += gp.z; gs.w += gp.w;
+        us.x += up.x; us.y += up.y; us.z += up.z; us.w += up.w;
+      }
+      const float gv[4] = {gs.x, gs.y, gs.z, gs.w}, uv[4] = {us.x, us.y, us.z, us.w};
+      uint32_t pk[2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const float h0 = gv[2 * j] / (1.0f + __expf(-gv[2 * j])) * uv[2 * j];
+        const float h1 = gv[2 * j + 1] / (1.0f + __expf(-gv[2 * j + 1])) * uv[2 * j + 1];
+        pk[j] = (uint32_t)f32_to_bf16(h0) | ((uint32_t)f32_to_bf16(h1) << 16);
+      }
+      *(uint2 *)((bf16_t *)C + c) = make_uint2(pk[0], pk[1]);
+    } else {
+      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+      for (int p = 0; p < S; ++p) {
+        const float4 pp = *(const float4 *)(P + p * part);
+        v.x += pp.x; v.y += pp.y; v.z += pp.z; v.w += pp.w;
+      }
+      *(float4 *)((float *)C + c) = v;
+    }
+  }
+}
+
+// ----------------------------------------------------------------------------------------
 // float32 SIMT kernel: 64 x 64 output tile, K step 16, 256 threads with 4 x 4 outputs each
 // (gate/up keeps a gate and an up accumulator per output).
 template <bool GATE_UP>
@@ -570,9 +801,48 @@ hipError_t launch_bf16(const GemmArgs &a0, bool gate_up, int max_rows, int num_c
   return hipGetLastError();
 }
 
+hipError_t launch_skinny(const GemmArgs &a0, bool gate_up, const SkinnyPlan &sp, int num_cu,
+                         hipStream_t st) {
+  GemmArgs a = a0;
+  a.sk_S = sp.S;
+  a.sk_pitch = sp.pitch;
+  if (sp.S > 1 && !a.partials) return hipErrorInvalidValue;
+  const int G = a.E + (a.s_rows > 0 ? 1 : 0);
+  const int ntmax = sp.snt > sp.nt ? sp.snt : sp.nt;
+  int grid = G * ntmax * sp.S;
+  if (grid > num_cu) grid = num_cu;
+  if (grid < 1) grid = 1;
+  if (gate_up) {
+    if (sp.mb == 1)
+      hipLaunchKernelGGL((gemm_skinny_kernel<true, 1>), dim3(grid), dim3(256), 0, st, a);
+    else
+      hipLaunchKernelGGL((gemm_skinny_kernel<true, 2>), dim3(grid), dim3(256), 0, st, a);
+  } else {
+    if (sp.mb == 1)
+      hipLaunchKernelGGL((gemm_skinny_kernel<false, 1>), dim3(grid), dim3(256), 0, st, a);
+    else
+      hipLaunchKernelGGL((gemm_skinny_kernel<false, 2>), dim3(grid), dim3(256), 0, st, a);
+  }
+  if (sp.S > 1) {
+    const long items = (long)(a.rcap + a.s_rows) * (gate_up ? sp.pitch / 2 : sp.pitch) / 4;
+    long rg = (items + 255) / 256;
+    if (rg > 4 * num_cu) rg = 4 * num_cu;
+    if (rg < 1) rg = 1;
+    if (gate_up)
+      hipLaunchKernelGGL(gemm_skinny_reduce_kernel<true>, dim3(rg), dim3(256), 0, st, a);
+    else
+      hipLaunchKernelGGL(gemm_skinny_reduce_kernel<false>, dim3(rg), dim3(256), 0, st, a);
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_gemm(const GemmArgs &a, bool gate_up, int max_rows, int num_cu,
                        hipStream_t st) {
-  if (a.elt == 2) return launch_bf16<MOE_GEMM_WAVES>(a, gate_up, max_rows, num_cu, st);
+  if (a.elt == 2) {
+    const SkinnyPlan sp = skinny_plan(a, gate_up);
+    if (sp.mb) return launch_skinny(a, gate_up, sp, num_cu, st);
+    return launch_bf16<MOE_GEMM_WAVES>(a, gate_up, max_rows, num_cu, st);
+  }
   int grid = gemm_tiles_upper(a, 64, 64, max_rows);
   if (grid > 4 * num_cu) grid = 4 * num_cu;
   if (grid < 1) grid = 1;

@@ -43,10 +43,20 @@ struct GemmArgs {
   float *partials;
   int split_ok;
   int grid;                         // persistent grid size (set by the launcher)
+  // few rows per group (decode-shaped batches): every group holds at most max_group_rows
+  // rows; when that is <= kSkinnyRows a 32/64-row tile streams the weights once, its K range
+  // cut into sk_S parts whose float32 sums (rows of sk_pitch floats, routed rows first, then
+  // the shared rows at row rcap) go to `partials`
+  int max_group_rows;
+  int rcap;                         // routed row capacity (T*k)
+  int sk_S, sk_pitch;               // set by the launcher
 };
 
 constexpr int kMaxPersistent = 256;   // persistent GEMM workgroups (one per CU on MI355X)
 constexpr size_t kPartialBytes = (size_t)kMaxPersistent * 256 * 256 * 4;
+constexpr int kSkinnyRows = 64;       // groups of at most this many rows take the skinny path
+// float32 partial-sum bytes the skinny path needs for a GEMM (0 if it does not apply)
+size_t skinny_partial_bytes(const GemmArgs &a, bool gate_up);
 
 int router_epad(int E);   // experts padded for the matrix-core router (bf16 x)
 hipError_t launch_router(int dtype, const void *x, const float *w, const float *bias,

@@ -31,6 +31,43 @@ int elt_of(const moe_problem &p) { return p.dtype == MOE_BF16 ? 2 : 4; }
 int64_t rows_cap(const moe_problem &p) { return (int64_t)p.T * p.k; }
 int slot_width(const moe_problem &p) { return p.routing == MOE_EXPERT_CHOICE ? p.E : p.k; }
 
+// sizes of one grouped GEMM of the problem (no pointers)
+GemmArgs gemm_shape(const moe_problem &p, bool gate_up) {
+  GemmArgs a{};
+  a.E = p.E;
+  a.elt = elt_of(p);
+  a.c_elt = gate_up ? a.elt : 4;
+  if (gate_up) {
+    a.N = p.d_ff; a.K = p.d_model; a.lda = p.d_model; a.ldc = p.d_ff;
+  } else {
+    a.N = p.d_model; a.K = p.d_ff; a.lda = p.d_ff; a.ldc = p.d_model;
+  }
+  if (p.d_ff_shared > 0) {
+    a.s_rows = p.T;
+    if (gate_up) {
+      a.sN = p.d_ff_shared; a.sK = p.d_model; a.s_lda = p.d_model; a.s_ldc = p.d_ff_shared;
+    } else {
+      a.sN = p.d_model; a.sK = p.d_ff_shared; a.s_lda = p.d_ff_shared; a.s_ldc = p.d_model;
+    }
+  }
+  // rows one group can hold: a token picks an expert at most once (token choice), an
+  // expert takes c <= T tokens (expert choice), the shared expert takes all T
+  a.max_group_rows = p.T;
+  a.rcap = (int)rows_cap(p);
+  return a;
+}
+
+// float32 partial sums of the bf16 GEMMs: the last-round tail split, or the skinny path's
+// K-parts, whichever needs more
+size_t partial_bytes(const moe_problem &p) {
+  size_t b = kPartialBytes;
+  for (int gu = 0; gu < 2; ++gu) {
+    const size_t s = skinny_partial_bytes(gemm_shape(p, gu == 1), gu == 1);
+    if (s > b) b = s;
+  }
+  return b;
+}
+
 Layout make_layout(const moe_problem &p) {
   Layout L{};
   const size_t T = p.T, E = p.E, k = p.k, R = rows_cap(p), d = p.d_model, dff = p.d_ff,
@@ -52,7 +89,7 @@ Layout make_layout(const moe_problem &p) {
   L.tok_blk_off = take(nblk * 4);
   L.stats_part = take(nblk * E * 4);
   L.w3 = take(p.dtype == MOE_BF16 && p.E > 8 ? 3 * (size_t)router_epad(p.E) * d * 2 : 0);
-  L.partials = take(p.dtype == MOE_BF16 ? kPartialBytes : 0);
+  L.partials = take(p.dtype == MOE_BF16 ? partial_bytes(p) : 0);
   L.logits = take(T * E * 4);
   L.ids = take(T * k * 4);
   L.topk_w = take(T * k * 4);
@@ -228,28 +265,12 @@ GemmArgs gemm_args(const moe_problem &p, const moe_routing &r, bool gate_up, con
                    const void *w0, const void *w1, void *c_rows, const void *s_a,
                    const void *s_w0, const void *s_w1, void *s_c,
                    const int32_t *row_map = nullptr) {
-  GemmArgs a{};
+  GemmArgs a = gemm_shape(p, gate_up);
   a.a_rows = row_map;
   a.counts = r.counts;
   a.offsets = r.offsets;
-  a.E = p.E;
-  a.elt = elt_of(p);
-  a.c_elt = gate_up ? a.elt : 4;
   a.A = a_rows; a.B0 = w0; a.B1 = w1; a.C = c_rows;
-  if (gate_up) {
-    a.N = p.d_ff; a.K = p.d_model; a.lda = p.d_model; a.ldc = p.d_ff;
-  } else {
-    a.N = p.d_model; a.K = p.d_ff; a.lda = p.d_ff; a.ldc = p.d_model;
-  }
-  if (p.d_ff_shared > 0) {
-    a.sA = s_a; a.sB0 = s_w0; a.sB1 = s_w1; a.sC = s_c;
-    a.s_rows = p.T;
-    if (gate_up) {
-      a.sN = p.d_ff_shared; a.sK = p.d_model; a.s_lda = p.d_model; a.s_ldc = p.d_ff_shared;
-    } else {
-      a.sN = p.d_model; a.sK = p.d_ff_shared; a.s_lda = p.d_ff_shared; a.s_ldc = p.d_model;
-    }
-  }
+  if (p.d_ff_shared > 0) { a.sA = s_a; a.sB0 = s_w0; a.sB1 = s_w1; a.sC = s_c; }
   return a;
 }
 

@@ -46,6 +46,13 @@ SMALL = {
                                      bias=("onehot", 30.0)),
     "collapse-ksplit-shared-bf16": C0.with_(dtype="bf16", T=200, d_model=1024, E=32, k=1,
                                             d_ff=512, d_ff_shared=512, bias=("onehot", 30.0)),
+    # decode-shaped batches (at most 64 rows per expert): the skinny GEMM path, its K
+    # parts summed by the reduction kernel; 32-row and 64-row tiles, with a shared expert
+    # whose K differs from the routed experts'
+    "decode-T8-bf16": C0.with_(dtype="bf16", T=8, d_model=512, E=8, k=2, d_ff=1024),
+    "decode-T48-shared-bf16": C0.with_(dtype="bf16", T=48, d_model=256, E=16, k=1, d_ff=512,
+                                       d_ff_shared=256, gamma=1.0, bias=("zipf", 1.2)),
+    "decode-T1-E64-bf16": C0.with_(dtype="bf16", T=1, d_model=1024, E=64, k=4, d_ff=512),
     "no-renorm-fp32": C0.with_(k=3, renorm_topk=False),
     "k-equals-E-fp32": C0.with_(E=4, k=4, T=50),
     "zipf-drop-fp32": C0.with_(gamma=0.75, bias=("zipf", 1.2), T=160),
@@ -300,3 +307,29 @@ def test_full_size_layer(cid):
     say(f"[full] cfg{cid}: max|dy|/RMS per-token/global: f32 y {p32:.4f}/{g32:.4f}  bf16 y "
         f"{pl:.4f}/{gl:.4f} (oracle-logit path {ps:.4f}/{gs:.4f}); exact answer rounded to "
         f"bf16: {e_round:.4f}")
+
+
+@pytest.mark.parametrize("T", [1, 8, 64])
+def test_decode_shaped_layer(T):
+    """The Mixtral-shaped layer with a decode-sized batch (T tokens, every expert's rows fit
+    the skinny GEMM path): y of every token against the oracle, through moe_layer_forward
+    (row gather folded into the GEMM) and through the separate steps (x_perm copied)."""
+    cfg = mi.CONFIGS[1].with_(T=T)
+    say(f"[decode] T={T}: generating inputs")
+    inp = inputs_for(cfg)
+    dev = dev_weights(inp)
+    l = oracle.router_logits(inp.x, inp.w_router, inp.bias)
+    ro = oracle.route(cfg, logits=l)
+    say(f"[decode] T={T}: oracle FFN on all tokens")
+    y_ref, _ = oracle.layer_forward(inp, routing=ro)
+    steps = run_steps(cfg, dev, logits_in=l)
+    _compare_routing(cfg, steps["rb"], ro, exact_logits=l)
+    check_y(cfg, host_f32(steps["y"]), y_ref)
+    cfg32 = cfg.with_(y_dtype="f32")
+    y32, rb = run_layer(cfg32, dev)
+    g = rb.host()
+    d_o, d_g = _decisions(ro, T), _decisions(g, T)
+    ok = np.array([d_o[t] == d_g[t] for t in range(T)])
+    assert ok.sum() >= T - 1
+    p32, g32 = check_y(cfg32, host_f32(y32)[ok], y_ref[ok])
+    say(f"[decode] T={T}: max|dy|/RMS per-token/global {p32:.4f}/{g32:.4f}")
