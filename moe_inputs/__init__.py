@@ -54,6 +54,8 @@ class MoEConfig:
     d_ff_shared: int = 0
     routing: str = "token"          # "token" (token choice) or "expert" (expert choice)
     gamma: float = 0.0              # capacity factor; <= 0 means no capacity limit
+    expand_m: int = 0               # expanded drop: m extra candidate experts per token
+    cap_groups: int = 0             # capacity per group of E/cap_groups experts (0: per expert)
     renorm_topk: bool = True
     dtype: str = "bf16"             # "bf16" or "f32": x, expert weights, hidden activation
     y_dtype: str = ""               # layer output type; "" = same as dtype

@@ -31,6 +31,22 @@ is a fixed float32 encoding (the routing-score spec below). Steps:
                     pairs weigh 0 and are not renormalised (Capacity-Aware
                     Inference summary, Methodology, Token Drop: capacity
                     C = gamma * N-bar, lowest gating scores dropped)
+     expanded drop  (same summary, Methodology, Expanded Drop: m further experts of
+                    the device join each token's candidates, so that tokens an
+                    overloaded expert drops move to experts with room; on one
+                    device every expert is local, so the m are the token's next m
+                    experts by logit) token drop over the top-k pairs first; a
+                    token that lost d of them offers its m extra candidates, each
+                    expert admits the offered pairs that fit its leftover capacity
+                    by (p32 desc, token asc), and the token keeps its first d
+                    admitted ones in slot order. An extra pair weighs p_te over the
+                    softmax mass of the token's top-k, like the top-k gates
+     group capacity (same summary, Methodology, device-level variant: capacity is
+                    counted per device, so an expert may go past its own share
+                    while its device has room) the E experts form D groups of E/D
+                    consecutive experts; a group with more than
+                    C_D = floor(gamma * T*k/D) candidate pairs keeps the C_D best by
+                    (p32 desc, token asc, slot asc)
   dispatch   kept (token, expert) pairs grouped by expert, ascending token
              inside each expert (a stable sort by expert id)
   expert     E_e(v) = W_down_e ( silu(W_gate_e v) * (W_up_e v) ),  silu(z) = z/(1+exp(-z))
@@ -50,7 +66,9 @@ evaluated as 1 + (r + r*(r*P(r))) with P(r) = 1/2! + r/3! + ... + r^5/7! in Horn
 form (adding the 1 last keeps the result monotone in x), then scaling by 2**n
 built in the exponent field; rexp(x) = +0 for x < -87.
 
-Pins (tests/test_oracle_*.py): brute-force enumeration for every selection form,
+Pins (tests/test_oracle_*.py): hand-derived examples (tests/golden/), brute-force
+enumeration for every selection form (subset dominance for the group capacity), the
+reductions of the capacity variants to the token drop (m = 0; groups of one expert),
 a dense evaluation of the definition, closed forms (k = E gives the plain
 softmax mixture; E = k = 1 gives a textbook SwiGLU FFN through torch.nn.functional),
 invariants fixed by the pages (exactly k per token, exactly c per expert,
@@ -211,6 +229,75 @@ def capacity_drop(ids: np.ndarray, p32: np.ndarray, C: int, E: int) -> np.ndarra
     return kept
 
 
+def expanded_drop(ids_ext: np.ndarray, p32: np.ndarray, C: int, k: int) -> np.ndarray:
+    """Expanded drop (Capacity-Aware Inference summary, Methodology, Expanded Drop).
+    ids_ext [T, k+m]: each token's top-(k+m) experts, slots >= k being the m extra
+    candidates. Returns kept [T, k+m]:
+      1. the top-k pairs go through the token drop with capacity C;
+      2. a token that lost d >= 1 top-k pairs offers its extra candidates; expert e, with
+         L_e = C - (its kept top-k pairs) places left, admits the L_e offered pairs with
+         the highest (p32, then lower token);
+      3. each such token keeps its first d admitted extra pairs in slot order."""
+    T, km = ids_ext.shape
+    E = p32.shape[1]
+    kept = np.zeros((T, km), dtype=np.uint8)
+    kept[:, :k] = capacity_drop(ids_ext[:, :k], p32, C, E)
+    need = k - kept[:, :k].sum(axis=1).astype(np.int64)
+    admitted = np.zeros((T, km), dtype=np.uint8)
+    for e in range(E):
+        left = C - int(np.count_nonzero((ids_ext[:, :k] == e) & (kept[:, :k] == 1)))
+        tt, jj = np.nonzero(ids_ext[:, k:] == e)     # offered pairs, ascending token
+        jj = jj + k
+        offer = need[tt] > 0
+        tt, jj = tt[offer], jj[offer]
+        if left <= 0 or tt.size == 0:
+            continue
+        order = np.argsort(-p32[tt, e], kind="stable")[:left]
+        admitted[tt[order], jj[order]] = 1
+    for t in np.nonzero(need > 0)[0]:
+        took = 0
+        for j in range(k, km):
+            if admitted[t, j] and took < need[t]:
+                kept[t, j] = 1
+                took += 1
+    return kept
+
+
+def expanded_gates(logits: np.ndarray, ids_ext: np.ndarray, k: int, renorm: bool = True):
+    """Weight of every candidate slot: the full softmax probability, divided by the softmax
+    mass of the token's top-k picks when ``renorm`` (so the top-k gates are the usual
+    renormalised ones and an extra expert that replaces a dropped pick enters with its own
+    probability on the same scale)."""
+    p = softmax_rows(logits)
+    g = np.take_along_axis(p, ids_ext.astype(np.int64), axis=1)
+    if renorm:
+        g = g / g[:, :k].sum(axis=1, keepdims=True)
+    return g
+
+
+def group_capacity(T: int, k: int, D: int, gamma: float) -> int:
+    """C_D = gamma * T*k/D: the token-drop capacity of one device holding E/D experts
+    (Capacity-Aware Inference summary, Methodology, device-level variant), floored."""
+    return int(math.floor(float(gamma) * (float(T) * float(k) / float(D))))
+
+
+def group_capacity_drop(ids: np.ndarray, p32: np.ndarray, C_D: int, E: int, D: int) -> np.ndarray:
+    """kept[t,j] = 1 unless the group of expert ids[t,j] (experts g*E/D .. (g+1)*E/D - 1)
+    has more than C_D candidate pairs and (t, j) is not among its C_D best by (p32 desc,
+    token asc, slot asc)."""
+    T, k = ids.shape
+    gs = E // D
+    kept = np.ones((T, k), dtype=np.uint8)
+    for g in range(D):
+        tt, jj = np.nonzero(ids // gs == g)      # token-major, slot ascending
+        if tt.size <= C_D:
+            continue
+        key = p32[tt, ids[tt, jj]]
+        order = np.argsort(-key, kind="stable")
+        kept[tt[order[C_D:]], jj[order[C_D:]]] = 0
+    return kept
+
+
 # ----------------------------------------------------------------------------- dispatch
 
 def dispatch(pair_token: np.ndarray, pair_expert: np.ndarray, pair_weight: np.ndarray, T: int, E: int):
@@ -256,13 +343,28 @@ def route(cfg, x=None, w_router=None, bias=None, logits=None) -> dict:
         out.update(sel=sel, sel_w=wts, c=expert_choice_capacity(T, k, E))
         out.update(dispatch(tt, ee, wts[tt, ee], T, E))
         return out
-    ids = topk_select(logits, k)
-    g = topk_gates(logits, ids, bool(cfg.renorm_topk))
+    m = int(getattr(cfg, "expand_m", 0) or 0)
+    D = int(getattr(cfg, "cap_groups", 0) or 0)
+    if (m or D) and not cfg.gamma > 0:
+        raise ValueError("expanded drop and group capacity need a capacity (gamma > 0)")
+    if m and D:
+        raise ValueError("expanded drop and group capacity are separate variants")
+    if k + m > E or (D and E % D):
+        raise ValueError("need k + m <= E and D dividing E")
+    ids = topk_select(logits, k + m)
+    if m:
+        g = expanded_gates(logits, ids, k, bool(cfg.renorm_topk))
+    else:
+        g = topk_gates(logits, ids, bool(cfg.renorm_topk))
     kept = np.ones((T, k), dtype=np.uint8)
     if cfg.gamma > 0:
-        C = capacity(T, k, E, cfg.gamma)
         p32 = routing_score32(logits)
-        kept = capacity_drop(ids, p32, C, E)
+        if D:
+            C = group_capacity(T, k, D, cfg.gamma)
+            kept = group_capacity_drop(ids, p32, C, E, D)
+        else:
+            C = capacity(T, k, E, cfg.gamma)
+            kept = expanded_drop(ids, p32, C, k) if m else capacity_drop(ids, p32, C, E)
         out.update(C=C, p32=p32)
     w = np.where(kept == 1, g, 0.0)
     tt, jj = np.nonzero(kept)                          # token-major, slot ascending
