@@ -33,6 +33,9 @@ def parse():
     ap.add_argument("--config", type=int, default=1)
     ap.add_argument("--tokens", type=int, default=0, help="override T (decode-shaped runs)")
     ap.add_argument("--y-dtype", default="", choices=["", "bf16", "f32"])
+    ap.add_argument("--gamma", type=float, default=None, help="override the capacity factor")
+    ap.add_argument("--expand-m", type=int, default=0, help="Expanded Drop: extra candidates")
+    ap.add_argument("--cap-groups", type=int, default=0, help="capacity per group of E/D experts")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=0,
                     help="tokens in the oracle sample (default: about 15 s of oracle work)")
@@ -146,6 +149,10 @@ def main():
         cfg = cfg.with_(T=args.tokens)
     if args.y_dtype:
         cfg = cfg.with_(y_dtype=args.y_dtype)
+    if args.gamma is not None:
+        cfg = cfg.with_(gamma=args.gamma)
+    if args.expand_m or args.cap_groups:
+        cfg = cfg.with_(expand_m=args.expand_m, cap_groups=args.cap_groups)
     print(f"[bench] generating {cfg.name} T={cfg.T}", file=sys.stderr, flush=True)
     inp = mi.make_inputs(cfg, threads=16)
     dev = {n: moe.device_tensor(getattr(inp, n)) for n in
@@ -236,13 +243,17 @@ def main():
         "data": "synthetic (seeded random inputs and random-init weights of the stated shape)",
         "config": {"workload": f"{cfg.name}: T={cfg.T} d_model={cfg.d_model} E={cfg.E} k={cfg.k} "
                                f"d_ff={cfg.d_ff} d_ff_shared={cfg.d_ff_shared} routing={cfg.routing} "
-                               f"gamma={cfg.gamma} {cfg.dtype} weights/activations, fp32 router, "
+                               f"gamma={cfg.gamma}"
+                               + (f" expand_m={cfg.expand_m}" if cfg.expand_m else "")
+                               + (f" cap_groups={cfg.cap_groups}" if cfg.cap_groups else "")
+                               + f" {cfg.dtype} weights/activations, fp32 router, "
                                f"y {cfg.y_dtype or cfg.dtype}",
                    "tokens": cfg.T, "rows_kept": n_kept, "parallelism": "single GPU"},
         "roofline": {"kernel": "grouped gate/up GEMM + SwiGLU (gemm_bf16_kernel<true, 8>)",
                      "bound": "mfma", "achieved": round(gu_tf, 1), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(gu_tf / PEAK_BF16_TFLOPS, 4),
-                     "traffic": recorded_traffic(cfg.name) if not args.tokens else None},
+                     "traffic": None if (args.tokens or args.gamma is not None or args.expand_m
+                                         or args.cap_groups) else recorded_traffic(cfg.name)},
         "grouped_gemm_mfma_util": round(gemm_tf / PEAK_BF16_TFLOPS, 4),
         "stages": stages,
         "host_s": round(host_s, 4),

@@ -74,6 +74,19 @@ typedef enum {
  *   C = floor(gamma * T*k/E) candidates keeps the C with the highest routing score
  *   (ties: lower token index); dropped pairs weigh 0, kept gates are not
  *   renormalised again (Capacity-Aware Inference summary, Token Drop).
+ *   Two variants of the capacity rule (same summary, Methodology), both with gamma > 0:
+ *   - expand_m = m > 0, Expanded Drop: each token also ranks its next m experts by
+ *     logit (slots k .. k+m-1). After the token drop of the top-k pairs, a token that
+ *     lost d picks offers its m extra candidates; expert e admits offered pairs into
+ *     its C - (kept top-k pairs) remaining places by the same routing score (ties:
+ *     lower token), and the token keeps its first d admitted extra pairs in slot
+ *     order. An extra pair weighs its softmax probability over the softmax mass of
+ *     the token's top-k (the scale of the top-k gates). Needs k + m <= E.
+ *   - cap_groups = D > 0, device-level capacity: the E experts form D groups of E/D
+ *     consecutive experts (one group per device of an expert-parallel layout); a group
+ *     with more than C_D = floor(gamma * T*k/D) candidate pairs keeps the C_D best by
+ *     routing score (ties: lower token, then lower slot), whatever their expert.
+ *     Needs D dividing E and k <= 16; not combined with expand_m.
  * MOE_EXPERT_CHOICE: each expert keeps the c = floor(k*T/E) tokens with the
  *   largest logit in its column (ties: lower token index); weight = softmax over
  *   all T tokens of that column; a token may get 0..E experts (hrletsgo page,
@@ -94,14 +107,18 @@ typedef struct {
   int32_t dtype;                  /* moe_dtype of x, expert weights, x_perm and the hidden h   */
   int32_t y_dtype;                /* moe_dtype of y; MOE_F32 allowed for either dtype, MOE_BF16
                                      only when dtype is MOE_BF16                               */
+  int32_t expand_m;               /* Expanded Drop: extra candidate experts per token; 0 = off  */
+  int32_t cap_groups;             /* capacity per group of E/cap_groups experts; 0 = per expert */
 } moe_problem;
 
 /* Routing result, all device pointers owned by the caller.
  *  logits     [T, E]   float32; input when MOE_ROUTE_LOGITS_IN, else output
- *  topk_ids   [T, k]   int32, token choice: picks in descending logit order (NULL allowed
- *                      for expert choice, required for token choice)
- *  topk_w     [T, k]   float32, token choice: gate of each pick before any drop
- *  kept       [T, k]   uint8, token choice: 1 kept / 0 dropped by capacity (may be NULL)
+ *  topk_ids   [T, S]   int32, token choice: picks in descending logit order (NULL allowed
+ *                      for expert choice, required for token choice); S = k + expand_m
+ *                      (slots k.. hold the Expanded Drop's extra candidates)
+ *  topk_w     [T, S]   float32, token choice: gate of each pick before any drop
+ *  kept       [T, S]   uint8, token choice: 1 kept / 0 dropped by capacity (may be NULL,
+ *                      except with expand_m > 0 or cap_groups > 0)
  *  counts     [E]      int32, rows per expert after selection
  *  offsets    [E+1]    int32, exclusive prefix sum of counts; offsets[E] = rows in use
  *  perm_token [R]      int32, dispatched row p holds token perm_token[p]; rows are grouped

@@ -36,7 +36,8 @@ class moe_problem(ctypes.Structure):
                 ("k", ctypes.c_int32), ("d_ff", ctypes.c_int32), ("d_ff_shared", ctypes.c_int32),
                 ("routing", ctypes.c_int32), ("gamma", ctypes.c_float),
                 ("renorm_topk", ctypes.c_int32), ("dtype", ctypes.c_int32),
-                ("y_dtype", ctypes.c_int32)]
+                ("y_dtype", ctypes.c_int32), ("expand_m", ctypes.c_int32),
+                ("cap_groups", ctypes.c_int32)]
 
 
 class moe_routing(ctypes.Structure):
@@ -113,9 +114,10 @@ def _check(status: int, where: str):
 
 
 def make_problem(T, d_model, E, k, d_ff, d_ff_shared=0, routing=MOE_TOKEN_CHOICE, gamma=0.0,
-                 renorm_topk=1, dtype=MOE_BF16, y_dtype=None) -> moe_problem:
+                 renorm_topk=1, dtype=MOE_BF16, y_dtype=None, expand_m=0,
+                 cap_groups=0) -> moe_problem:
     return moe_problem(T, d_model, E, k, d_ff, d_ff_shared, routing, gamma, renorm_topk, dtype,
-                       dtype if y_dtype is None else y_dtype)
+                       dtype if y_dtype is None else y_dtype, expand_m, cap_groups)
 
 
 def make_routing(**ptrs) -> moe_routing:

@@ -10,13 +10,15 @@ from ._lib import (MOE_BF16, MOE_EXPERT_CHOICE, MOE_F32, MOE_TOKEN_CHOICE, make_
 def problem_of(cfg):
     """moe_problem from any object with the fields T, d_model, E, k, d_ff, d_ff_shared,
     routing ("token"/"expert"), gamma, renorm_topk, dtype ("bf16"/"f32") and optionally
-    y_dtype ("bf16"/"f32"/"" = same as dtype)."""
+    y_dtype ("bf16"/"f32"/"" = same as dtype), expand_m and cap_groups (default 0)."""
     y_dt = getattr(cfg, "y_dtype", "") or cfg.dtype
     return make_problem(cfg.T, cfg.d_model, cfg.E, cfg.k, cfg.d_ff, cfg.d_ff_shared,
                         MOE_EXPERT_CHOICE if cfg.routing == "expert" else MOE_TOKEN_CHOICE,
                         float(cfg.gamma), int(bool(cfg.renorm_topk)),
                         MOE_BF16 if cfg.dtype == "bf16" else MOE_F32,
-                        MOE_BF16 if y_dt == "bf16" else MOE_F32)
+                        MOE_BF16 if y_dt == "bf16" else MOE_F32,
+                        int(getattr(cfg, "expand_m", 0) or 0),
+                        int(getattr(cfg, "cap_groups", 0) or 0))
 
 
 def device_tensor(a, device="cuda"):
@@ -35,12 +37,13 @@ class RoutingBuffers:
     def __init__(self, problem, device="cuda"):
         import torch
         T, E, k = problem.T, problem.E, problem.k
+        S = k + problem.expand_m          # slots per token (extra Expanded Drop candidates)
         R = T * k
         i32, f32 = torch.int32, torch.float32
         self.logits = torch.empty(T, E, dtype=f32, device=device)
-        self.topk_ids = torch.empty(T, k, dtype=i32, device=device)
-        self.topk_w = torch.empty(T, k, dtype=f32, device=device)
-        self.kept = torch.empty(T, k, dtype=torch.uint8, device=device)
+        self.topk_ids = torch.empty(T, S, dtype=i32, device=device)
+        self.topk_w = torch.empty(T, S, dtype=f32, device=device)
+        self.kept = torch.empty(T, S, dtype=torch.uint8, device=device)
         self.counts = torch.empty(E, dtype=i32, device=device)
         self.offsets = torch.empty(E + 1, dtype=i32, device=device)
         self.perm_token = torch.empty(R, dtype=i32, device=device)

@@ -10,15 +10,15 @@ constexpr int kMaxGroups = kMaxExperts + 1;   // routed experts + one shared exp
 
 // Workspace regions used by the routing kernels.
 struct RouteScratch {
-  float *keys;          // [T*k] routing score of each pick (capacity drop)
+  float *keys;          // [T*S] routing score of each pick (capacity drop)
   int32_t *blk_cnt;     // [nblk*E] per-block per-expert counts
   int32_t *blk_base;    // [nblk*E] exclusive scan over blocks
   int32_t *cnt_pre;     // [E] candidates per expert (before the capacity drop)
   int32_t *off_pre;     // [E+1]
-  int32_t *cand_token;  // [R] candidates grouped by expert
-  int32_t *cand_slot;   // [R]
-  float *cand_key;      // [R]
-  int32_t *slot_pos;    // [T*S] row of (token, slot) or -1; S = k (token choice) or E
+  int32_t *cand_token;  // [T*S] candidates grouped by expert (or expert group)
+  int32_t *cand_slot;   // [T*S]
+  float *cand_key;      // [T*S]
+  int32_t *slot_pos;    // [T*S] row of (token, slot) or -1; S = k + m (token choice) or E
   uint32_t *colkeys;    // [E*T] expert-choice column keys
   int32_t *tok_blk;     // [nblk] per-block row counts of the token CSR
   int32_t *tok_blk_off; // [nblk]
@@ -61,12 +61,20 @@ size_t skinny_partial_bytes(const GemmArgs &a, bool gate_up);
 int router_epad(int E);   // experts padded for the matrix-core router (bf16 x)
 hipError_t launch_router(int dtype, const void *x, const float *w, const float *bias,
                          float *logits, int T, int d, int E, uint16_t *w3, hipStream_t st);
-hipError_t launch_topk(const float *logits, int T, int E, int k, int renorm, int want_key,
-                       int32_t *ids, float *gates, float *keys, hipStream_t st);
+hipError_t launch_topk(const float *logits, int T, int E, int k, int kden, int renorm,
+                       int want_key, int32_t *ids, float *gates, float *keys, hipStream_t st);
 hipError_t launch_token_dispatch(const RouteScratch &s, const int32_t *ids, const float *gates,
                                  int T, int k, int E, int C, int32_t *perm_token, float *perm_w,
                                  uint8_t *kept, int32_t *counts, int32_t *offsets,
                                  hipStream_t st);
+hipError_t launch_group_capacity(const RouteScratch &s, const int32_t *ids, const float *gates,
+                                 int T, int k, int E, int D, int C_D, int32_t *perm_token,
+                                 float *perm_w, uint8_t *kept, int32_t *counts, int32_t *offsets,
+                                 hipStream_t st);
+hipError_t launch_expanded_drop(const RouteScratch &s, const int32_t *ids, const float *gates,
+                                int T, int k, int m, int E, int C, int32_t *perm_token,
+                                float *perm_w, uint8_t *kept, int32_t *counts, int32_t *offsets,
+                                hipStream_t st);
 hipError_t launch_expert_choice(const RouteScratch &s, const float *logits, int T, int E, int c,
                                 int32_t *perm_token, float *perm_w, int32_t *counts,
                                 int32_t *offsets, hipStream_t st);

@@ -29,7 +29,9 @@ struct Layout {
 
 int elt_of(const moe_problem &p) { return p.dtype == MOE_BF16 ? 2 : 4; }
 int64_t rows_cap(const moe_problem &p) { return (int64_t)p.T * p.k; }
-int slot_width(const moe_problem &p) { return p.routing == MOE_EXPERT_CHOICE ? p.E : p.k; }
+int slot_width(const moe_problem &p) {
+  return p.routing == MOE_EXPERT_CHOICE ? p.E : p.k + p.expand_m;
+}
 
 // sizes of one grouped GEMM of the problem (no pointers)
 GemmArgs gemm_shape(const moe_problem &p, bool gate_up) {
@@ -75,14 +77,14 @@ Layout make_layout(const moe_problem &p) {
   const size_t nblk = (T + 255) / 256;
   size_t o = 0;
   auto take = [&](size_t bytes) { size_t at = o; o += up(bytes); return at; };
-  L.keys = take(T * k * 4);
+  L.keys = take(T * S * 4);
   L.blk_cnt = take(nblk * E * 4);
   L.blk_base = take(nblk * E * 4);
   L.cnt_pre = take(E * 4);
   L.off_pre = take((E + 1) * 4);
-  L.cand_token = take(R * 4);
-  L.cand_slot = take(R * 4);
-  L.cand_key = take(R * 4);
+  L.cand_token = take(T * S * 4);
+  L.cand_slot = take(T * S * 4);
+  L.cand_key = take(T * S * 4);
   L.slot_pos = take(T * S * 4);
   L.colkeys = take(p.routing == MOE_EXPERT_CHOICE ? E * T * 4 : 0);
   L.tok_blk = take(nblk * 4);
@@ -91,9 +93,9 @@ Layout make_layout(const moe_problem &p) {
   L.w3 = take(p.dtype == MOE_BF16 && p.E > 8 ? 3 * (size_t)router_epad(p.E) * d * 2 : 0);
   L.partials = take(p.dtype == MOE_BF16 ? partial_bytes(p) : 0);
   L.logits = take(T * E * 4);
-  L.ids = take(T * k * 4);
-  L.topk_w = take(T * k * 4);
-  L.kept = take(T * k);
+  L.ids = take(T * S * 4);
+  L.topk_w = take(T * S * 4);
+  L.kept = take(T * S);
   L.counts = take(E * 4);
   L.offsets = take((E + 1) * 4);
   L.perm_token = take(R * 4);
@@ -124,11 +126,19 @@ moe_status check_problem(const moe_problem *pp) {
   if (p.dtype == MOE_F32 && p.y_dtype != MOE_F32) return MOE_ERR_INVALID_ARG;
   if (p.renorm_topk != 0 && p.renorm_topk != 1) return MOE_ERR_INVALID_ARG;
   if (std::isnan(p.gamma) || std::isinf(p.gamma)) return MOE_ERR_INVALID_ARG;
+  if (p.expand_m < 0 || p.cap_groups < 0) return MOE_ERR_INVALID_ARG;
+  if (p.expand_m > 0 || p.cap_groups > 0) {
+    if (p.routing != MOE_TOKEN_CHOICE || !(p.gamma > 0.f) || (p.expand_m > 0 && p.cap_groups > 0))
+      return MOE_ERR_INVALID_ARG;
+    if ((int64_t)p.k + p.expand_m > p.E) return MOE_ERR_INVALID_ARG;
+    if (p.cap_groups > 0 && p.E % p.cap_groups != 0) return MOE_ERR_INVALID_ARG;
+  }
   if (p.routing == MOE_EXPERT_CHOICE && ((int64_t)p.k * p.T < p.E || p.gamma > 0.f))
     return MOE_ERR_INVALID_ARG;
   const int64_t R = rows_cap(p);
   if (R > INT32_MAX || (int64_t)p.T * p.E > INT32_MAX) return MOE_ERR_INVALID_ARG;
   if (p.E > kMaxExperts) return MOE_ERR_UNSUPPORTED;
+  if (p.cap_groups > 0 && p.k > 16) return MOE_ERR_UNSUPPORTED;   // picks per token in a group
   if (p.dtype == MOE_BF16) {
     if (p.d_model % 64 || p.d_ff % 64 || p.d_ff_shared % 64) return MOE_ERR_UNSUPPORTED;
   } else {
@@ -162,6 +172,8 @@ moe_status check_routing_out(const moe_problem &p, const moe_routing *r) {
   if (p.routing == MOE_TOKEN_CHOICE && (!ptr_ok(r->topk_ids) || !ptr_ok(r->topk_w)))
     return MOE_ERR_INVALID_ARG;
   if (!opt_ptr_ok(r->kept)) return MOE_ERR_INVALID_ARG;
+  // the capacity variants keep their intermediate decisions in `kept`
+  if ((p.expand_m > 0 || p.cap_groups > 0) && !r->kept) return MOE_ERR_INVALID_ARG;
   return MOE_OK;
 }
 
@@ -225,6 +237,12 @@ int capacity_of(const moe_problem &p) {
   return (int)std::floor((double)p.gamma * nbar);
 }
 
+// C_D = floor(gamma * T*k/D): the token-drop capacity of a device that holds E/D experts
+int group_capacity_of(const moe_problem &p) {
+  const double per_group = (double)p.T * (double)p.k / (double)p.cap_groups;
+  return (int)std::floor((double)p.gamma * per_group);
+}
+
 // ---- the four steps, without validation --------------------------------------------------
 
 hipError_t do_route(const moe_problem &p, const void *x, const float *w_router,
@@ -240,11 +258,19 @@ hipError_t do_route(const moe_problem &p, const void *x, const float *w_router,
   }
   if (p.routing == MOE_TOKEN_CHOICE) {
     const int C = capacity_of(p);
-    e = launch_topk(r.logits, p.T, p.E, p.k, p.renorm_topk, C >= 0 ? 1 : 0, r.topk_ids, r.topk_w,
-                    s.keys, st);
+    e = launch_topk(r.logits, p.T, p.E, p.k + p.expand_m, p.k, p.renorm_topk, C >= 0 ? 1 : 0,
+                    r.topk_ids, r.topk_w, s.keys, st);
     if (e != hipSuccess) return e;
-    e = launch_token_dispatch(s, r.topk_ids, r.topk_w, p.T, p.k, p.E, C, r.perm_token, r.perm_w,
-                              r.kept, r.counts, r.offsets, st);
+    if (p.cap_groups > 0)
+      e = launch_group_capacity(s, r.topk_ids, r.topk_w, p.T, p.k, p.E, p.cap_groups,
+                                group_capacity_of(p), r.perm_token, r.perm_w, r.kept, r.counts,
+                                r.offsets, st);
+    else if (p.expand_m > 0)
+      e = launch_expanded_drop(s, r.topk_ids, r.topk_w, p.T, p.k, p.expand_m, p.E, C,
+                               r.perm_token, r.perm_w, r.kept, r.counts, r.offsets, st);
+    else
+      e = launch_token_dispatch(s, r.topk_ids, r.topk_w, p.T, p.k, p.E, C, r.perm_token,
+                                r.perm_w, r.kept, r.counts, r.offsets, st);
     if (e != hipSuccess) return e;
   } else {
     const int c = (int)(((int64_t)p.k * p.T) / p.E);

@@ -338,7 +338,7 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(const bf16_t *__restri
 // q_e = rexp_spec(l_e - max), S = q_0 + q_1 + ... left to right, p32 = q_e / S.
 template <int G>
 __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ logits, int T, int E,
-                                                   int k, int renorm, int want_key,
+                                                   int k, int kden, int renorm, int want_key,
                                                    int32_t *__restrict__ ids,
                                                    float *__restrict__ gates,
                                                    float *__restrict__ keys) {
@@ -376,7 +376,7 @@ __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ log
     if (r == 0) mx = bv;
     if ((be % G) == gl) taken |= 1u << (be / G);
     const float q = expf(bv - mx);
-    qsum += q;
+    if (r < kden) qsum += q;   // renormalisation mass: the first kden picks
     if (gl == 0 && live) {
       ids[(size_t)t * k + r] = be;
       gates[(size_t)t * k + r] = q;   // numerator for now
@@ -417,39 +417,58 @@ __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ log
 }
 
 // ----------------------------------------------------------------------------------------
-// Dispatch histogram. Block b owns tokens [256b, 256b+256). For every expert a 256-bit
-// mask marks the block's tokens that chose it (LDS atomicOr of distinct bits, order free);
-// popcounts give the block's per-expert counts and, in the scatter, each pair's rank.
-MOE_DEV void build_masks(uint32_t *mask, const int32_t *ids, const uint8_t *kept, int T, int k,
-                         int E) {
-  for (int i = threadIdx.x; i < E * 8; i += blockDim.x) mask[i] = 0u;
+// Dispatch histogram. Block b owns tokens [256b, 256b+256). Each token has a row of S slots
+// (expert ids); the pairs taken are the slots in [j0, j1), minus those with kept == 0 when a
+// kept array is given, and a pair's bucket is its expert / gs (gs = 1: one bucket per
+// expert; gs = E/D: one per group of experts). A token can have up to `mult` pairs in one
+// bucket. For every bucket and c < mult a 256-bit mask marks the block's tokens with more
+// than c pairs in it (LDS atomicOr of distinct bits, order free), so popcounts give the
+// block's per-bucket counts and, in the scatter, each pair's rank: pairs of lower tokens
+// first, a token's own pairs in slot order.
+struct PairSel {
+  const uint8_t *kept;
+  int S, j0, j1, gs, mult;
+};
+
+constexpr int kMaxSlots = 16;   // pairs of one token in one bucket are tracked up to k <= 16
+
+MOE_DEV void build_masks(uint32_t *mask, const int32_t *ids, const PairSel &f, int T, int B) {
+  for (int i = threadIdx.x; i < B * f.mult * 8; i += blockDim.x) mask[i] = 0u;
   __syncthreads();
   const int t = blockIdx.x * 256 + threadIdx.x;
   if (t < T) {
-    for (int j = 0; j < k; ++j) {
-      if (kept && !kept[(size_t)t * k + j]) continue;
-      const int e = ids[(size_t)t * k + j];
-      atomicOr(&mask[e * 8 + (threadIdx.x >> 5)], 1u << (threadIdx.x & 31));
+    int seen[kMaxSlots];
+    int ns = 0;
+    for (int j = f.j0; j < f.j1; ++j) {
+      if (f.kept && !f.kept[(size_t)t * f.S + j]) continue;
+      const int b = ids[(size_t)t * f.S + j] / f.gs;
+      int c = 0;
+      if (f.mult > 1) {
+        for (int q = 0; q < ns; ++q) c += seen[q] == b;
+        seen[ns++] = b;
+      }
+      atomicOr(&mask[(b * f.mult + c) * 8 + (threadIdx.x >> 5)], 1u << (threadIdx.x & 31));
     }
   }
   __syncthreads();
 }
 
 __global__ __launch_bounds__(256) void assign_count_kernel(const int32_t *__restrict__ ids, int T,
-                                                           int k, int E,
+                                                           PairSel f, int B,
                                                            int32_t *__restrict__ blk_cnt) {
   extern __shared__ uint32_t mask[];
-  build_masks(mask, ids, nullptr, T, k, E);
-  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+  build_masks(mask, ids, f, T, B);
+  for (int b = threadIdx.x; b < B; b += blockDim.x) {
     int c = 0;
+    for (int m = 0; m < f.mult; ++m)
 #pragma unroll
-    for (int w = 0; w < 8; ++w) c += __popc(mask[e * 8 + w]);
-    blk_cnt[(size_t)blockIdx.x * E + e] = c;
+      for (int w = 0; w < 8; ++w) c += __popc(mask[(b * f.mult + m) * 8 + w]);
+    blk_cnt[(size_t)blockIdx.x * B + b] = c;
   }
 }
 
-// Column scans of the block counts (one thread per expert, blocks in order), expert
-// totals, exclusive scan over experts. With a capacity C >= 0 the kept counts are
+// Column scans of the block counts (one thread per bucket, blocks in order), bucket
+// totals, exclusive scan over buckets. With a capacity C >= 0 the kept counts are
 // min(count, C) and a second offset table is produced for them.
 __global__ __launch_bounds__(1024) void assign_scan_kernel(const int32_t *__restrict__ blk_cnt,
                                                            int nblk, int E, int C,
@@ -481,35 +500,77 @@ __global__ __launch_bounds__(1024) void assign_scan_kernel(const int32_t *__rest
   }
 }
 
-// Stable scatter: pair (t, j) of expert e goes to off[e] + blk_base[b][e] + (number of the
-// block's tokens before t that chose e). Without capacity the final arrays are written;
-// with capacity the candidate arrays (token, slot, key) that cap_select reads.
+// Stable scatter: pair (t, j) of bucket b goes to off[b] + blk_base[blk][b] + (its rank in
+// the block). Candidate mode writes (token, slot, key) lists for cap_select; final mode
+// writes the dispatch arrays, and marks the slots in [j0, j1) that were not taken with -1.
 __global__ __launch_bounds__(256) void assign_scatter_kernel(
     const int32_t *__restrict__ ids, const float *__restrict__ gates,
-    const float *__restrict__ keys, int T, int k, int E, const int32_t *__restrict__ off,
+    const float *__restrict__ keys, int T, PairSel f, int B, const int32_t *__restrict__ off,
     const int32_t *__restrict__ blk_base, int candidates, int32_t *__restrict__ out_token,
     float *__restrict__ out_w, int32_t *__restrict__ out_slot, float *__restrict__ out_key,
-    int32_t *__restrict__ slot_pos, uint8_t *__restrict__ kept) {
+    int32_t *__restrict__ slot_pos, uint8_t *__restrict__ kept_out) {
   extern __shared__ uint32_t mask[];
-  build_masks(mask, ids, nullptr, T, k, E);
+  build_masks(mask, ids, f, T, B);
   const int t = blockIdx.x * 256 + threadIdx.x;
   if (t >= T) return;
   const int word = threadIdx.x >> 5, bit = threadIdx.x & 31;
-  for (int j = 0; j < k; ++j) {
-    const int e = ids[(size_t)t * k + j];
-    int rank = __popc(mask[e * 8 + word] & ((1u << bit) - 1u));
-    for (int w = 0; w < word; ++w) rank += __popc(mask[e * 8 + w]);
-    const int pos = off[e] + blk_base[(size_t)blockIdx.x * E + e] + rank;
+  int seen[kMaxSlots];
+  int ns = 0;
+  for (int j = f.j0; j < f.j1; ++j) {
+    const size_t ij = (size_t)t * f.S + j;
+    if (f.kept && !f.kept[ij]) {
+      if (!candidates) slot_pos[ij] = -1;
+      continue;
+    }
+    const int b = ids[ij] / f.gs;
+    int c = 0;
+    if (f.mult > 1) {
+      for (int q = 0; q < ns; ++q) c += seen[q] == b;
+      seen[ns++] = b;
+    }
+    int rank = c;
+    for (int m = 0; m < f.mult; ++m) {
+      const uint32_t *mk = mask + (b * f.mult + m) * 8;
+      rank += __popc(mk[word] & ((1u << bit) - 1u));
+      for (int w = 0; w < word; ++w) rank += __popc(mk[w]);
+    }
+    const int pos = off[b] + blk_base[(size_t)blockIdx.x * B + b] + rank;
     if (candidates) {
       out_token[pos] = t;
       out_slot[pos] = j;
-      out_key[pos] = keys[(size_t)t * k + j];
+      out_key[pos] = keys[ij];
     } else {
       out_token[pos] = t;
-      out_w[pos] = gates[(size_t)t * k + j];
-      slot_pos[(size_t)t * k + j] = pos;
-      if (kept) kept[(size_t)t * k + j] = 1;
+      out_w[pos] = gates[ij];
+      slot_pos[ij] = pos;
+      if (kept_out) kept_out[ij] = 1;
     }
+  }
+}
+
+// Expanded drop, between its two selections: a token that lost some of its first k picks
+// offers its extra candidates (kept[j >= k] = 1 marks the offer) ...
+__global__ __launch_bounds__(256) void expand_offer_kernel(uint8_t *__restrict__ kept, int T,
+                                                           int k, int S) {
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  if (t >= T) return;
+  int have = 0;
+  for (int j = 0; j < k; ++j) have += kept[(size_t)t * S + j];
+  for (int j = k; j < S; ++j) kept[(size_t)t * S + j] = have < k ? 1 : 0;
+}
+
+// ... and after the admission (kept[j >= k] = admitted) keeps its first admitted extra
+// pairs in slot order, as many as it lost.
+__global__ __launch_bounds__(256) void expand_keep_kernel(uint8_t *__restrict__ kept, int T,
+                                                          int k, int S) {
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  if (t >= T) return;
+  int have = 0;
+  for (int j = 0; j < k; ++j) have += kept[(size_t)t * S + j];
+  for (int j = k; j < S; ++j) {
+    uint8_t &v = kept[(size_t)t * S + j];
+    if (v && have < k) ++have;
+    else v = 0;
   }
 }
 
@@ -547,25 +608,30 @@ MOE_DEV SelectResult block_radix_select(GetKey get, int n, int want, int *hist, 
   return SelectResult{prefix, want};
 }
 
-// Capacity-aware token drop, one workgroup per expert. The candidates of expert e sit in
-// ascending token order at [off_pre[e], off_pre[e] + cnt); if more than C, the C with the
-// largest (key, then lower token) stay. Survivors keep their order and go to off_fin[e] + rank.
+// Capacity selection, one workgroup per bucket. The candidates of bucket e sit in their
+// rank order (ascending token, then slot) at [off_pre[e], off_pre[e] + cnt); if more than
+// the bucket's capacity (C, minus used[e] places already taken when `used` is given), the
+// ones with the largest (key, then earlier rank) stay. Final mode (perm_token given):
+// survivors keep their order and go to off_fin[e] + rank, dropped slots get -1. Flag mode:
+// only kept[t, j] = survived.
 __global__ __launch_bounds__(1024) void cap_select_kernel(
     const int32_t *__restrict__ cand_token, const int32_t *__restrict__ cand_slot,
     const float *__restrict__ cand_key, const int32_t *__restrict__ cnt_pre,
-    const int32_t *__restrict__ off_pre, const int32_t *__restrict__ off_fin, int C, int k,
-    const float *__restrict__ gates, int32_t *__restrict__ perm_token,
-    float *__restrict__ perm_w, int32_t *__restrict__ slot_pos, uint8_t *__restrict__ kept) {
+    const int32_t *__restrict__ off_pre, const int32_t *__restrict__ off_fin, int C,
+    const int32_t *__restrict__ used, int S, const float *__restrict__ gates,
+    int32_t *__restrict__ perm_token, float *__restrict__ perm_w, int32_t *__restrict__ slot_pos,
+    uint8_t *__restrict__ kept) {
   __shared__ int hist[256];
   __shared__ int sm[1024 / 64 + 1];
   const int e = blockIdx.x;
-  const int n = cnt_pre[e], base = off_pre[e], obase = off_fin[e];
-  // C == 0 keeps nothing: a threshold above every finite key
+  const int n = cnt_pre[e], base = off_pre[e];
+  const int cap = used ? max(C - used[e], 0) : C;
+  // capacity 0 keeps nothing: a threshold above every finite key
   SelectResult sr{0xffffffffu, 0};
-  const bool drop = n > C;
-  if (drop && C > 0) {
+  const bool drop = n > cap;
+  if (drop && cap > 0) {
     auto get = [&](int i) { return float_key(cand_key[base + i]); };
-    sr = block_radix_select(get, n, C, hist, sm);
+    sr = block_radix_select(get, n, cap, hist, sm);
   }
   int run_eq = 0, run_sel = 0;
   for (int c0 = 0; c0 < n; c0 += blockDim.x) {
@@ -582,15 +648,18 @@ __global__ __launch_bounds__(1024) void cap_select_kernel(
     run_sel += tot;
     if (in) {
       const int t = cand_token[base + i], j = cand_slot[base + i];
-      if (self) {
-        const int q = obase + rank;
-        perm_token[q] = t;
-        perm_w[q] = gates[(size_t)t * k + j];
-        slot_pos[(size_t)t * k + j] = q;
-      } else {
-        slot_pos[(size_t)t * k + j] = -1;
+      const size_t ij = (size_t)t * S + j;
+      if (perm_token) {
+        if (self) {
+          const int q = off_fin[e] + rank;
+          perm_token[q] = t;
+          perm_w[q] = gates[ij];
+          slot_pos[ij] = q;
+        } else {
+          slot_pos[ij] = -1;
+        }
       }
-      if (kept) kept[(size_t)t * k + j] = (uint8_t)self;
+      if (kept) kept[ij] = (uint8_t)self;
     }
   }
 }
@@ -811,8 +880,8 @@ hipError_t launch_router(int dtype, const void *x, const float *w, const float *
   return hipGetLastError();
 }
 
-hipError_t launch_topk(const float *logits, int T, int E, int k, int renorm, int want_key,
-                       int32_t *ids, float *gates, float *keys, hipStream_t st) {
+hipError_t launch_topk(const float *logits, int T, int E, int k, int kden, int renorm,
+                       int want_key, int32_t *ids, float *gates, float *keys, hipStream_t st) {
   int G = 64;
   if (E <= 8) G = 8;
   else if (E <= 16) G = 16;
@@ -820,39 +889,115 @@ hipError_t launch_topk(const float *logits, int T, int E, int k, int renorm, int
   const int tpb = 256 / G;
   const size_t sh = want_key ? (size_t)tpb * E * sizeof(float) : 0;
   dim3 grid((T + tpb - 1) / tpb);
+#define MOE_TOPK(GG) hipLaunchKernelGGL(topk_kernel<GG>, grid, dim3(256), sh, st, logits, T, E, k, \
+                                        kden, renorm, want_key, ids, gates, keys)
   switch (G) {
-    case 8: hipLaunchKernelGGL(topk_kernel<8>, grid, dim3(256), sh, st, logits, T, E, k, renorm, want_key, ids, gates, keys); break;
-    case 16: hipLaunchKernelGGL(topk_kernel<16>, grid, dim3(256), sh, st, logits, T, E, k, renorm, want_key, ids, gates, keys); break;
-    case 32: hipLaunchKernelGGL(topk_kernel<32>, grid, dim3(256), sh, st, logits, T, E, k, renorm, want_key, ids, gates, keys); break;
-    default: hipLaunchKernelGGL(topk_kernel<64>, grid, dim3(256), sh, st, logits, T, E, k, renorm, want_key, ids, gates, keys); break;
+    case 8: MOE_TOPK(8); break;
+    case 16: MOE_TOPK(16); break;
+    case 32: MOE_TOPK(32); break;
+    default: MOE_TOPK(64); break;
   }
+#undef MOE_TOPK
   return hipGetLastError();
 }
+
+namespace {
+
+// histogram + scan + scatter of the pairs `f` selects into B buckets. Candidate mode:
+// per-bucket candidate lists in s.cand_* with counts s.cnt_pre and offsets s.off_pre.
+// Final mode: counts/offsets and the dispatch arrays.
+void assign_pairs(const RouteScratch &s, const int32_t *ids, const float *gates, int T,
+                  const PairSel &f, int B, bool candidates, int32_t *perm_token, float *perm_w,
+                  uint8_t *kept_out, int32_t *counts, int32_t *offsets, hipStream_t st) {
+  const int nblk = (T + 255) / 256;
+  const size_t msh = (size_t)B * f.mult * 8 * sizeof(uint32_t);
+  hipLaunchKernelGGL(assign_count_kernel, dim3(nblk), dim3(256), msh, st, ids, T, f, B, s.blk_cnt);
+  int32_t *cnt = candidates ? s.cnt_pre : counts, *off = candidates ? s.off_pre : offsets;
+  hipLaunchKernelGGL(assign_scan_kernel, dim3(1), dim3(1024), 0, st, s.blk_cnt, nblk, B, -1,
+                     s.blk_base, cnt, off, (int32_t *)nullptr, (int32_t *)nullptr);
+  if (candidates)
+    hipLaunchKernelGGL(assign_scatter_kernel, dim3(nblk), dim3(256), msh, st, ids, gates, s.keys,
+                       T, f, B, off, s.blk_base, 1, s.cand_token, (float *)nullptr, s.cand_slot,
+                       s.cand_key, (int32_t *)nullptr, (uint8_t *)nullptr);
+  else
+    hipLaunchKernelGGL(assign_scatter_kernel, dim3(nblk), dim3(256), msh, st, ids, gates,
+                       (const float *)nullptr, T, f, B, off, s.blk_base, 0, perm_token, perm_w,
+                       (int32_t *)nullptr, (float *)nullptr, s.slot_pos, kept_out);
+}
+
+}  // namespace
 
 hipError_t launch_token_dispatch(const RouteScratch &s, const int32_t *ids, const float *gates,
                                  int T, int k, int E, int C, int32_t *perm_token, float *perm_w,
                                  uint8_t *kept, int32_t *counts, int32_t *offsets,
                                  hipStream_t st) {
   const int nblk = (T + 255) / 256;
-  const size_t msh = (size_t)E * 8 * sizeof(uint32_t);
-  hipLaunchKernelGGL(assign_count_kernel, dim3(nblk), dim3(256), msh, st, ids, T, k, E,
-                     s.blk_cnt);
-  const bool drop = C >= 0;
-  hipLaunchKernelGGL(assign_scan_kernel, dim3(1), dim3(1024), 0, st, s.blk_cnt, nblk, E, C,
-                     s.blk_base, drop ? s.cnt_pre : counts, drop ? s.off_pre : offsets, counts,
-                     offsets);
-  if (!drop) {
-    hipLaunchKernelGGL(assign_scatter_kernel, dim3(nblk), dim3(256), msh, st, ids, gates,
-                       (const float *)nullptr, T, k, E, offsets, s.blk_base, 0, perm_token,
-                       perm_w, (int32_t *)nullptr, (float *)nullptr, s.slot_pos, kept);
-  } else {
-    hipLaunchKernelGGL(assign_scatter_kernel, dim3(nblk), dim3(256), msh, st, ids, gates,
-                       s.keys, T, k, E, s.off_pre, s.blk_base, 1, s.cand_token, (float *)nullptr,
-                       s.cand_slot, s.cand_key, (int32_t *)nullptr, (uint8_t *)nullptr);
-    hipLaunchKernelGGL(cap_select_kernel, dim3(E), dim3(1024), 0, st, s.cand_token, s.cand_slot,
-                       s.cand_key, s.cnt_pre, s.off_pre, offsets, C, k, gates, perm_token,
-                       perm_w, s.slot_pos, kept);
+  const PairSel all{nullptr, k, 0, k, 1, 1};
+  if (C < 0) {
+    assign_pairs(s, ids, gates, T, all, E, false, perm_token, perm_w, kept, counts, offsets, st);
+    return hipGetLastError();
   }
+  const size_t msh = (size_t)E * 8 * sizeof(uint32_t);
+  hipLaunchKernelGGL(assign_count_kernel, dim3(nblk), dim3(256), msh, st, ids, T, all, E,
+                     s.blk_cnt);
+  hipLaunchKernelGGL(assign_scan_kernel, dim3(1), dim3(1024), 0, st, s.blk_cnt, nblk, E, C,
+                     s.blk_base, s.cnt_pre, s.off_pre, counts, offsets);
+  hipLaunchKernelGGL(assign_scatter_kernel, dim3(nblk), dim3(256), msh, st, ids, gates, s.keys, T,
+                     all, E, s.off_pre, s.blk_base, 1, s.cand_token, (float *)nullptr,
+                     s.cand_slot, s.cand_key, (int32_t *)nullptr, (uint8_t *)nullptr);
+  hipLaunchKernelGGL(cap_select_kernel, dim3(E), dim3(1024), 0, st, s.cand_token, s.cand_slot,
+                     s.cand_key, s.cnt_pre, s.off_pre, offsets, C, (const int32_t *)nullptr, k,
+                     gates, perm_token, perm_w, s.slot_pos, kept);
+  return hipGetLastError();
+}
+
+hipError_t launch_group_capacity(const RouteScratch &s, const int32_t *ids, const float *gates,
+                                 int T, int k, int E, int D, int C_D, int32_t *perm_token,
+                                 float *perm_w, uint8_t *kept, int32_t *counts, int32_t *offsets,
+                                 hipStream_t st) {
+  const int gs = E / D;
+  // candidates per group (a token may have up to min(k, E/D) pairs in one group)
+  const PairSel grp{nullptr, k, 0, k, gs, k < gs ? k : gs};
+  assign_pairs(s, ids, gates, T, grp, D, true, nullptr, nullptr, nullptr, nullptr, nullptr, st);
+  hipLaunchKernelGGL(cap_select_kernel, dim3(D), dim3(1024), 0, st, s.cand_token, s.cand_slot,
+                     s.cand_key, s.cnt_pre, s.off_pre, s.off_pre, C_D, (const int32_t *)nullptr,
+                     k, gates, (int32_t *)nullptr, (float *)nullptr, (int32_t *)nullptr, kept);
+  // dispatch of the kept pairs per expert
+  const PairSel fin{kept, k, 0, k, 1, 1};
+  assign_pairs(s, ids, gates, T, fin, E, false, perm_token, perm_w, nullptr, counts, offsets, st);
+  return hipGetLastError();
+}
+
+hipError_t launch_expanded_drop(const RouteScratch &s, const int32_t *ids, const float *gates,
+                                int T, int k, int m, int E, int C, int32_t *perm_token,
+                                float *perm_w, uint8_t *kept, int32_t *counts, int32_t *offsets,
+                                hipStream_t st) {
+  const int S = k + m, nblk = (T + 255) / 256;
+  const size_t msh = (size_t)E * 8 * sizeof(uint32_t);
+  // 1. token drop over the first k slots (flags); counts <- kept top-k pairs per expert
+  const PairSel top{nullptr, S, 0, k, 1, 1};
+  hipLaunchKernelGGL(assign_count_kernel, dim3(nblk), dim3(256), msh, st, ids, T, top, E,
+                     s.blk_cnt);
+  hipLaunchKernelGGL(assign_scan_kernel, dim3(1), dim3(1024), 0, st, s.blk_cnt, nblk, E, C,
+                     s.blk_base, s.cnt_pre, s.off_pre, counts, offsets);
+  hipLaunchKernelGGL(assign_scatter_kernel, dim3(nblk), dim3(256), msh, st, ids, gates, s.keys, T,
+                     top, E, s.off_pre, s.blk_base, 1, s.cand_token, (float *)nullptr,
+                     s.cand_slot, s.cand_key, (int32_t *)nullptr, (uint8_t *)nullptr);
+  hipLaunchKernelGGL(cap_select_kernel, dim3(E), dim3(1024), 0, st, s.cand_token, s.cand_slot,
+                     s.cand_key, s.cnt_pre, s.off_pre, s.off_pre, C, (const int32_t *)nullptr, S,
+                     gates, (int32_t *)nullptr, (float *)nullptr, (int32_t *)nullptr, kept);
+  // 2. offers of the tokens that lost picks, admitted into each expert's leftover places
+  hipLaunchKernelGGL(expand_offer_kernel, dim3(nblk), dim3(256), 0, st, kept, T, k, S);
+  const PairSel ext{kept, S, k, S, 1, 1};
+  assign_pairs(s, ids, gates, T, ext, E, true, nullptr, nullptr, nullptr, nullptr, nullptr, st);
+  hipLaunchKernelGGL(cap_select_kernel, dim3(E), dim3(1024), 0, st, s.cand_token, s.cand_slot,
+                     s.cand_key, s.cnt_pre, s.off_pre, s.off_pre, C, counts, S, gates,
+                     (int32_t *)nullptr, (float *)nullptr, (int32_t *)nullptr, kept);
+  // 3. each token keeps as many admitted extra pairs as it lost, in slot order
+  hipLaunchKernelGGL(expand_keep_kernel, dim3(nblk), dim3(256), 0, st, kept, T, k, S);
+  // 4. dispatch of all kept pairs per expert
+  const PairSel fin{kept, S, 0, S, 1, 1};
+  assign_pairs(s, ids, gates, T, fin, E, false, perm_token, perm_w, nullptr, counts, offsets, st);
   return hipGetLastError();
 }
 

@@ -36,7 +36,8 @@ def test_library_exports_every_declared_symbol():
 
 def good(**kw):
     base = dict(T=64, d_model=128, E=8, k=2, d_ff=256, d_ff_shared=0, routing=0, gamma=0.0,
-                renorm_topk=1, dtype=moe.MOE_BF16, y_dtype=moe.MOE_BF16)
+                renorm_topk=1, dtype=moe.MOE_BF16, y_dtype=moe.MOE_BF16, expand_m=0,
+                cap_groups=0)
     base.update(kw)
     return moe.moe_problem(*[base[f] for f, _ in moe.moe_problem._fields_])
 
@@ -65,6 +66,16 @@ def ws_status(p):
     (dict(dtype=moe.MOE_F32, y_dtype=moe.MOE_F32, d_model=6), moe.MOE_ERR_UNSUPPORTED),
     (dict(dtype=moe.MOE_F32, y_dtype=moe.MOE_F32, d_model=12, d_ff=5), moe.MOE_OK),
     (dict(routing=1, T=4, k=2, E=8), moe.MOE_OK),
+    # capacity variants: need token choice and gamma > 0, k + m <= E, D dividing E, not both
+    (dict(expand_m=2, gamma=1.0), moe.MOE_OK), (dict(cap_groups=4, gamma=1.0), moe.MOE_OK),
+    (dict(expand_m=-1), moe.MOE_ERR_INVALID_ARG), (dict(cap_groups=-2), moe.MOE_ERR_INVALID_ARG),
+    (dict(expand_m=2), moe.MOE_ERR_INVALID_ARG), (dict(cap_groups=2), moe.MOE_ERR_INVALID_ARG),
+    (dict(expand_m=7, gamma=1.0), moe.MOE_ERR_INVALID_ARG),
+    (dict(cap_groups=3, gamma=1.0), moe.MOE_ERR_INVALID_ARG),
+    (dict(expand_m=1, cap_groups=2, gamma=1.0), moe.MOE_ERR_INVALID_ARG),
+    (dict(routing=1, expand_m=1, gamma=1.0), moe.MOE_ERR_INVALID_ARG),
+    (dict(E=64, k=17, cap_groups=2, gamma=1.0), moe.MOE_ERR_UNSUPPORTED),
+    (dict(E=64, k=17, expand_m=20, gamma=1.0), moe.MOE_OK),
     # one expert's float32 GEMM output (up to T rows of d_model) must stay under 4 GiB
     (dict(T=1 << 18, d_model=4096, k=1), moe.MOE_ERR_UNSUPPORTED),
     (dict(T=(1 << 18) - 64, d_model=4096, k=1), moe.MOE_OK),
@@ -74,6 +85,13 @@ def test_problem_validation(kw, status):
     assert st == status, moe.status_str(st)
     if status == moe.MOE_OK:
         assert n > 0 and n % 256 == 0
+
+
+def test_variants_need_the_kept_array():
+    p = good(expand_m=1, gamma=1.0)
+    assert call_route(p, r=routing_struct(kept=None), nbytes=1 << 40) == moe.MOE_ERR_INVALID_ARG
+    p = good(cap_groups=2, gamma=1.0)
+    assert call_route(p, r=routing_struct(kept=None), nbytes=1 << 40) == moe.MOE_ERR_INVALID_ARG
 
 
 def test_workspace_grows_with_rows():

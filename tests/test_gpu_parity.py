@@ -53,6 +53,16 @@ SMALL = {
     "decode-T48-shared-bf16": C0.with_(dtype="bf16", T=48, d_model=256, E=16, k=1, d_ff=512,
                                        d_ff_shared=256, gamma=1.0, bias=("zipf", 1.2)),
     "decode-T1-E64-bf16": C0.with_(dtype="bf16", T=1, d_model=1024, E=64, k=4, d_ff=512),
+    # capacity variants: Expanded Drop (m extra candidates re-home dropped pairs) and
+    # capacity per group of experts, under skewed routers
+    "expanded-drop-bf16": C0.with_(dtype="bf16", T=500, d_model=128, E=8, k=2, d_ff=192,
+                                   gamma=0.75, expand_m=2, bias=("zipf", 1.2)),
+    "expanded-drop-E64-fp32": C0.with_(T=300, E=64, k=4, expand_m=4, gamma=1.0,
+                                       bias=("normal", 1.0)),
+    "group-capacity-bf16": C0.with_(dtype="bf16", T=400, E=16, k=4, d_ff=192, cap_groups=4,
+                                    gamma=0.75, bias=("zipf", 1.2)),
+    "group-capacity-one-group-fp32": C0.with_(T=200, cap_groups=1, gamma=0.5,
+                                              bias=("normal", 0.5)),
     "no-renorm-fp32": C0.with_(k=3, renorm_topk=False),
     "k-equals-E-fp32": C0.with_(E=4, k=4, T=50),
     "zipf-drop-fp32": C0.with_(gamma=0.75, bias=("zipf", 1.2), T=160),
@@ -125,6 +135,9 @@ TIE_CASES = [
     dict(T=300, E=8, k=2, gamma=8.0), dict(T=2500, E=8, k=2, routing="expert"),
     dict(T=77, E=6, k=5, routing="expert"), dict(T=300, E=128, k=8, routing="expert"),
     dict(T=64, E=64, k=64, routing="expert"),
+    dict(T=999, E=16, k=2, gamma=0.75, expand_m=3), dict(T=300, E=32, k=4, gamma=0.5, expand_m=8),
+    dict(T=1000, E=8, k=2, gamma=0.5, cap_groups=2), dict(T=500, E=64, k=8, gamma=1.25, cap_groups=8),
+    dict(T=333, E=16, k=4, gamma=0.25, cap_groups=1),
 ]
 
 
