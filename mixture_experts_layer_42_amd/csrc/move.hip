@@ -30,7 +30,11 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(const uint4 *__restric
 
 // y[t] = sum_{i in [tok_ptr[t], tok_ptr[t+1])} perm_w[tok_pos[i]] * o[tok_pos[i]] (+ o_shared[t]),
 // float32 sum in CSR order (the shared row added last), one rounding into y. One wave per
-// token, 4 columns (16 bytes of o) per lane access.
+// token: the token's row indices and weights sit one per lane and are broadcast; each step
+// issues the loads of two rows x CH column chunks (16 bytes of o per lane per chunk) before
+// the multiply-adds, so several rows' loads are in flight at once. A missing second row of a
+// pair reads the first row again with weight 0, which leaves the sum unchanged
+// (fma(0, v, acc) = acc for finite v), so the result equals the row-by-row sum.
 template <typename TY>
 __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ o,
                                                       const float *__restrict__ o_shared,
@@ -38,31 +42,64 @@ __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ 
                                                       const int32_t *__restrict__ tok_pos,
                                                       const float *__restrict__ perm_w,
                                                       TY *__restrict__ y, int Tn, int d) {
+  constexpr int CH = 4;   // 256-column chunks per step
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= Tn) return;
-  const int b = tok_ptr[t], e = tok_ptr[t + 1];
-  for (int c0 = lane * 4; c0 < d; c0 += 256) {
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int i = b; i < e; ++i) {
-      const int p = tok_pos[i];
-      const float w = perm_w[p];
-      const float4 v = *reinterpret_cast<const float4 *>(o + (size_t)p * d + c0);
-      acc.x = fmaf(w, v.x, acc.x); acc.y = fmaf(w, v.y, acc.y);
-      acc.z = fmaf(w, v.z, acc.z); acc.w = fmaf(w, v.w, acc.w);
+  const int b = tok_ptr[t], n = tok_ptr[t + 1] - b;
+  for (int cb = 0; cb < d; cb += 256 * CH) {   // uniform over the wave (the shuffles below)
+    const int c0 = cb + lane * 4;
+    float4 acc[CH];
+#pragma unroll
+    for (int u = 0; u < CH; ++u) acc[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int rb = 0; rb < n; rb += 64) {   // rows in blocks of 64, one per lane
+    const int m = min(64, n - rb);
+    const int my_p = lane < m ? tok_pos[b + rb + lane] : 0;
+    const float my_w = lane < m ? perm_w[my_p] : 0.f;
+    for (int j = 0; j < m; j += 2) {
+      const int p0 = __shfl(my_p, j, 64);
+      const float w0 = __shfl(my_w, j, 64);
+      const bool two = j + 1 < m;
+      const int p1 = two ? __shfl(my_p, j + 1, 64) : p0;
+      const float w1 = two ? __shfl(my_w, j + 1, 64) : 0.f;
+      float4 v0[CH], v1[CH];
+#pragma unroll
+      for (int u = 0; u < CH; ++u) {
+        const int c = c0 + u * 256;
+        if (c < d) {
+          v0[u] = *reinterpret_cast<const float4 *>(o + (size_t)p0 * d + c);
+          v1[u] = *reinterpret_cast<const float4 *>(o + (size_t)p1 * d + c);
+        } else {
+          v0[u] = v1[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < CH; ++u) {
+        acc[u].x = fmaf(w0, v0[u].x, acc[u].x); acc[u].y = fmaf(w0, v0[u].y, acc[u].y);
+        acc[u].z = fmaf(w0, v0[u].z, acc[u].z); acc[u].w = fmaf(w0, v0[u].w, acc[u].w);
+        acc[u].x = fmaf(w1, v1[u].x, acc[u].x); acc[u].y = fmaf(w1, v1[u].y, acc[u].y);
+        acc[u].z = fmaf(w1, v1[u].z, acc[u].z); acc[u].w = fmaf(w1, v1[u].w, acc[u].w);
+      }
     }
-    if (o_shared) {
-      const float4 v = *reinterpret_cast<const float4 *>(o_shared + (size_t)t * d + c0);
-      acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
     }
-    TY *yp = y + (size_t)t * d + c0;
-    if constexpr (sizeof(TY) == 2) {
-      uint2 pk;
-      pk.x = (uint32_t)f32_to_bf16(acc.x) | ((uint32_t)f32_to_bf16(acc.y) << 16);
-      pk.y = (uint32_t)f32_to_bf16(acc.z) | ((uint32_t)f32_to_bf16(acc.w) << 16);
-      *reinterpret_cast<uint2 *>(yp) = pk;
-    } else {
-      *reinterpret_cast<float4 *>(yp) = acc;
+#pragma unroll
+    for (int u = 0; u < CH; ++u) {
+      const int c = c0 + u * 256;
+      if (c >= d) break;
+      float4 a = acc[u];
+      if (o_shared) {
+        const float4 v = *reinterpret_cast<const float4 *>(o_shared + (size_t)t * d + c);
+        a.x += v.x; a.y += v.y; a.z += v.z; a.w += v.w;
+      }
+      TY *yp = y + (size_t)t * d + c;
+      if constexpr (sizeof(TY) == 2) {
+        uint2 pk;
+        pk.x = (uint32_t)f32_to_bf16(a.x) | ((uint32_t)f32_to_bf16(a.y) << 16);
+        pk.y = (uint32_t)f32_to_bf16(a.z) | ((uint32_t)f32_to_bf16(a.w) << 16);
+        *reinterpret_cast<uint2 *>(yp) = pk;
+      } else {
+        *reinterpret_cast<float4 *>(yp) = a;
+      }
     }
   }
 }
