@@ -82,6 +82,34 @@ MOE_DEV int block_excl_scan(int v, int *smem, int *total) {
   return res;
 }
 
+// N independent exclusive scans over the block at once (thread order), two barriers in
+// all. smem: (blockDim.x/64) * N + N ints. total[c] gets the block total of column c.
+template <int N>
+MOE_DEV void block_excl_scan_vec(int (&v)[N], int *smem, int (&total)[N]) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  int inc[N];
+#pragma unroll
+  for (int c = 0; c < N; ++c) inc[c] = wave_incl_scan(v[c]);
+  if (lane == 63)
+#pragma unroll
+    for (int c = 0; c < N; ++c) smem[wid * N + c] = inc[c];
+  __syncthreads();
+  if (threadIdx.x < N) {
+    const int c = threadIdx.x;
+    int run = 0;
+    for (int w = 0; w < nw; ++w) { const int t = smem[w * N + c]; smem[w * N + c] = run; run += t; }
+    smem[nw * N + c] = run;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int c = 0; c < N; ++c) {
+    const int ex = smem[wid * N + c] + inc[c] - v[c];
+    total[c] = smem[nw * N + c];
+    v[c] = ex;
+  }
+  __syncthreads();
+}
+
 MOE_DEV float block_sum(float v, float *smem) {   // smem: blockDim.x/64 floats; contains barriers
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, nw = blockDim.x >> 6;
   v = wave_sum(v);

@@ -18,6 +18,7 @@ struct RouteScratch {
   int32_t *cand_token;  // [T*S] candidates grouped by expert (or expert group)
   int32_t *cand_slot;   // [T*S]
   float *cand_key;      // [T*S]
+  float *cand_w;        // [T*S] gate of each candidate
   int32_t *slot_pos;    // [T*S] row of (token, slot) or -1; S = k + m (token choice) or E
   uint32_t *colkeys;    // [E*T] expert-choice column keys
   int32_t *tok_blk;     // [nblk] per-block row counts of the token CSR

@@ -18,7 +18,8 @@ size_t up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct Layout {
   // route scratch
-  size_t keys, blk_cnt, blk_base, cnt_pre, off_pre, cand_token, cand_slot, cand_key, slot_pos,
+  size_t keys, blk_cnt, blk_base, cnt_pre, off_pre, cand_token, cand_slot, cand_key, cand_w,
+      slot_pos,
       colkeys, tok_blk, tok_blk_off, stats_part, w3, partials;
   // routing arrays used when the caller passes no routing struct
   size_t logits, ids, topk_w, kept, counts, offsets, perm_token, perm_w, tok_ptr, tok_pos;
@@ -85,6 +86,7 @@ Layout make_layout(const moe_problem &p) {
   L.cand_token = take(T * S * 4);
   L.cand_slot = take(T * S * 4);
   L.cand_key = take(T * S * 4);
+  L.cand_w = take(T * S * 4);
   L.slot_pos = take(T * S * 4);
   L.colkeys = take(p.routing == MOE_EXPERT_CHOICE ? E * T * 4 : 0);
   L.tok_blk = take(nblk * 4);
@@ -207,6 +209,7 @@ RouteScratch scratch_of(const Layout &L, char *ws) {
   s.cand_token = (int32_t *)(ws + L.cand_token);
   s.cand_slot = (int32_t *)(ws + L.cand_slot);
   s.cand_key = (float *)(ws + L.cand_key);
+  s.cand_w = (float *)(ws + L.cand_w);
   s.slot_pos = (int32_t *)(ws + L.slot_pos);
   s.colkeys = (uint32_t *)(ws + L.colkeys);
   s.tok_blk = (int32_t *)(ws + L.tok_blk);

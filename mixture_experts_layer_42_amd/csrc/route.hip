@@ -12,6 +12,8 @@
 //                   (ascending token inside an expert), CSR token -> rows
 // Integer decisions never depend on summation order or atomics: histograms are
 // built from bit masks and popcounts, positions from prefix scans.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -336,7 +338,7 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(const bf16_t *__restri
 // maximum (ties: lower expert index). Gates: exp(l - max) normalised over the picks (or
 // over all E). With a capacity limit the float32 routing score of each pick is written:
 // q_e = rexp_spec(l_e - max), S = q_0 + q_1 + ... left to right, p32 = q_e / S.
-template <int G>
+template <int G, int MAXPL>
 __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ logits, int T, int E,
                                                    int k, int kden, int renorm, int want_key,
                                                    int32_t *__restrict__ ids,
@@ -346,8 +348,7 @@ __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ log
   const int gl = threadIdx.x % G, gi = threadIdx.x / G;
   const int t = blockIdx.x * (256 / G) + gi;
   const bool live = t < T;
-  const int npl = (E + G - 1) / G;
-  constexpr int MAXPL = (G < 64) ? 1 : kMaxExperts / 64;   // E <= G for G < 64
+  const int npl = (E + G - 1) / G;   // logits per lane (<= MAXPL)
   float lv[MAXPL];
   uint32_t taken = 0u;
 #pragma unroll
@@ -481,7 +482,18 @@ __global__ __launch_bounds__(1024) void assign_scan_kernel(const int32_t *__rest
   const int e = threadIdx.x;
   int run = 0;
   if (e < E) {
-    for (int b = 0; b < nblk; ++b) {
+    int b = 0;
+    for (; b + 8 <= nblk; b += 8) {   // eight independent loads in flight, then the scan
+      int c[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) c[i] = blk_cnt[(size_t)(b + i) * E + e];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        blk_base[(size_t)(b + i) * E + e] = run;
+        run += c[i];
+      }
+    }
+    for (; b < nblk; ++b) {
       const int c = blk_cnt[(size_t)b * E + e];
       blk_base[(size_t)b * E + e] = run;
       run += c;
@@ -539,6 +551,7 @@ __global__ __launch_bounds__(256) void assign_scatter_kernel(
       out_token[pos] = t;
       out_slot[pos] = j;
       out_key[pos] = keys[ij];
+      if (out_w) out_w[pos] = gates[ij];   // the pair's gate rides along with its key
     } else {
       out_token[pos] = t;
       out_w[pos] = gates[ij];
@@ -578,23 +591,65 @@ __global__ __launch_bounds__(256) void expand_keep_kernel(uint8_t *__restrict__ 
 // Block-wide radix selection (1024 threads): among n uint32 keys, find the want-th largest
 // value tau and how many keys equal to tau are needed (need_eq) so that
 // {u > tau} + (first need_eq of {u == tau}) is exactly the top `want`. Histograms of one
-// byte per pass (LDS integer adds: the counts do not depend on order).
+// byte per pass (LDS integer adds: the counts do not depend on order), one per wave so that
+// the many keys sharing a leading byte (scores of similar size) do not all queue on one LDS
+// word; the 16 wave histograms are summed bin by bin.
 struct SelectResult { uint32_t tau; int need_eq; };
+constexpr int kSelWaves = 16;   // waves of a 1024-thread selection block
+
+// bin counts of the pass into hist[wave][bin] -> returns the total of bin 255-b to thread b
+MOE_DEV int sum_wave_hists(const int *hist, int b) {
+  int h = 0;
+  if (b < 256)
+#pragma unroll
+    for (int w = 0; w < kSelWaves; ++w) h += hist[w * 256 + 255 - b];
+  return h;
+}
 
 template <typename GetKey>
 MOE_DEV SelectResult block_radix_select(GetKey get, int n, int want, int *hist, int *sm) {
   uint32_t prefix = 0u, pmask = 0u;
+  int *wh = hist + (threadIdx.x >> 6) * 256;
   for (int shift = 24; shift >= 0; shift -= 8) {
-    for (int i = threadIdx.x; i < 256; i += blockDim.x) hist[i] = 0;
+    for (int i = threadIdx.x; i < kSelWaves * 256; i += blockDim.x) hist[i] = 0;
     __syncthreads();
     for (int i = threadIdx.x; i < n; i += blockDim.x) {
       const uint32_t u = get(i);
-      if ((u & pmask) == prefix) atomicAdd(&hist[(u >> shift) & 255u], 1);
+      if ((u & pmask) == prefix) atomicAdd(&wh[(u >> shift) & 255u], 1);
     }
     __syncthreads();
     // thread b looks at bin 255-b: inclusive scan from the top bin down
     const int b = threadIdx.x;
-    const int h = (b < 256) ? hist[255 - b] : 0;
+    const int h = sum_wave_hists(hist, b);
+    int tot;
+    const int ex = block_excl_scan(h, sm, &tot);
+    __shared__ int pick[2];
+    if (b < 256 && ex < want && want <= ex + h) { pick[0] = 255 - b; pick[1] = want - ex; }
+    __syncthreads();
+    prefix |= ((uint32_t)pick[0]) << shift;
+    pmask |= 255u << shift;
+    want = pick[1];
+    __syncthreads();
+  }
+  return SelectResult{prefix, want};
+}
+
+// The same selection over keys held in registers: thread tid owns keys tid + 1024 j.
+template <int KPT>
+MOE_DEV SelectResult block_radix_select_regs(const uint32_t (&u)[KPT], int n, int want, int *hist,
+                                             int *sm) {
+  uint32_t prefix = 0u, pmask = 0u;
+  int *wh = hist + (threadIdx.x >> 6) * 256;
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    for (int i = threadIdx.x; i < kSelWaves * 256; i += blockDim.x) hist[i] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < KPT; ++j)
+      if (threadIdx.x + j * 1024 < n && (u[j] & pmask) == prefix)
+        atomicAdd(&wh[(u[j] >> shift) & 255u], 1);
+    __syncthreads();
+    const int b = threadIdx.x;
+    const int h = sum_wave_hists(hist, b);
     int tot;
     const int ex = block_excl_scan(h, sm, &tot);
     __shared__ int pick[2];
@@ -609,26 +664,83 @@ MOE_DEV SelectResult block_radix_select(GetKey get, int n, int want, int *hist, 
 }
 
 // Capacity selection, one workgroup per bucket. The candidates of bucket e sit in their
-// rank order (ascending token, then slot) at [off_pre[e], off_pre[e] + cnt); if more than
-// the bucket's capacity (C, minus used[e] places already taken when `used` is given), the
-// ones with the largest (key, then earlier rank) stay. Final mode (perm_token given):
-// survivors keep their order and go to off_fin[e] + rank, dropped slots get -1. Flag mode:
-// only kept[t, j] = survived.
+// rank order (ascending token, then slot) at [off_pre[e], off_pre[e] + cnt), each with its
+// key and gate; if more than the bucket's capacity (C, minus used[e] places already taken
+// when `used` is given), the ones with the largest (key, then earlier rank) stay. Final mode
+// (perm_token given): survivors keep their order and go to off_fin[e] + rank, dropped slots
+// get -1. Flag mode: only kept[t, j] = survived.
 __global__ __launch_bounds__(1024) void cap_select_kernel(
     const int32_t *__restrict__ cand_token, const int32_t *__restrict__ cand_slot,
-    const float *__restrict__ cand_key, const int32_t *__restrict__ cnt_pre,
-    const int32_t *__restrict__ off_pre, const int32_t *__restrict__ off_fin, int C,
-    const int32_t *__restrict__ used, int S, const float *__restrict__ gates,
+    const float *__restrict__ cand_key, const float *__restrict__ cand_w,
+    const int32_t *__restrict__ cnt_pre, const int32_t *__restrict__ off_pre,
+    const int32_t *__restrict__ off_fin, int C, const int32_t *__restrict__ used, int S,
     int32_t *__restrict__ perm_token, float *__restrict__ perm_w, int32_t *__restrict__ slot_pos,
     uint8_t *__restrict__ kept) {
-  __shared__ int hist[256];
-  __shared__ int sm[1024 / 64 + 1];
+  constexpr int KPT = 16;   // keys per thread kept in registers (n <= 16384)
+  __shared__ int hist[kSelWaves * 256];
+  __shared__ int sm[kSelWaves * KPT + KPT];
   const int e = blockIdx.x;
   const int n = cnt_pre[e], base = off_pre[e];
   const int cap = used ? max(C - used[e], 0) : C;
   // capacity 0 keeps nothing: a threshold above every finite key
   SelectResult sr{0xffffffffu, 0};
   const bool drop = n > cap;
+  auto emit = [&](int i, bool self, int rank) {
+    const int t = cand_token[base + i], j = cand_slot[base + i];
+    const size_t ij = (size_t)t * S + j;
+    if (perm_token) {
+      if (self) {
+        const int q = off_fin[e] + rank;
+        perm_token[q] = t;
+        perm_w[q] = cand_w[base + i];
+        slot_pos[ij] = q;
+      } else {
+        slot_pos[ij] = -1;
+      }
+    }
+    if (kept) kept[ij] = (uint8_t)self;
+  };
+  // thread tid owns candidates tid + 1024 c (chunk c): keys in registers; the ranks of each
+  // chunk come from one vector scan over the block, chunks in order
+  auto in_regs = [&](auto kpt) {
+    constexpr int K = decltype(kpt)::value;
+    uint32_t u[K];
+#pragma unroll
+    for (int c = 0; c < K; ++c) {
+      const int i = threadIdx.x + c * 1024;
+      u[c] = (drop && i < n) ? float_key(cand_key[base + i]) : 0u;
+    }
+    if (drop && cap > 0) sr = block_radix_select_regs<K>(u, n, cap, hist, sm);
+    int eq[K], eq_tot[K];
+#pragma unroll
+    for (int c = 0; c < K; ++c)
+      eq[c] = (drop && threadIdx.x + c * 1024 < n && u[c] == sr.tau) ? 1 : 0;
+    block_excl_scan_vec<K>(eq, sm, eq_tot);
+    int sel[K], sel_tot[K];
+    uint32_t selm = 0u;
+    int run = 0;
+#pragma unroll
+    for (int c = 0; c < K; ++c) {
+      const bool in = threadIdx.x + c * 1024 < n;
+      const bool is_eq = drop && in && u[c] == sr.tau;
+      const bool self = in && (!drop || u[c] > sr.tau || (is_eq && run + eq[c] < sr.need_eq));
+      run += eq_tot[c];
+      sel[c] = self ? 1 : 0;
+      selm |= (self ? 1u : 0u) << c;
+    }
+    block_excl_scan_vec<K>(sel, sm, sel_tot);
+    run = 0;
+#pragma unroll
+    for (int c = 0; c < K; ++c) {
+      const int i = threadIdx.x + c * 1024;
+      if (i < n) emit(i, (selm >> c) & 1u, run + sel[c]);
+      run += sel_tot[c];
+    }
+  };
+  if (n <= 2 * 1024) { in_regs(std::integral_constant<int, 2>{}); return; }
+  if (n <= 4 * 1024) { in_regs(std::integral_constant<int, 4>{}); return; }
+  if (n <= KPT * 1024) { in_regs(std::integral_constant<int, KPT>{}); return; }
+  // many candidates: keys re-read from memory, ranks by 1024-wide chunks in order
   if (drop && cap > 0) {
     auto get = [&](int i) { return float_key(cand_key[base + i]); };
     sr = block_radix_select(get, n, cap, hist, sm);
@@ -637,30 +749,16 @@ __global__ __launch_bounds__(1024) void cap_select_kernel(
   for (int c0 = 0; c0 < n; c0 += blockDim.x) {
     const int i = c0 + threadIdx.x;
     const bool in = i < n;
-    uint32_t u = 0u;
-    if (in && drop) u = float_key(cand_key[base + i]);
-    const int eqf = (in && drop && u == sr.tau) ? 1 : 0;
+    uint32_t uu = 0u;
+    if (in && drop) uu = float_key(cand_key[base + i]);
+    const int eqf = (in && drop && uu == sr.tau) ? 1 : 0;
     int tot;
     const int eq_rank = run_eq + block_excl_scan(eqf, sm, &tot);
     run_eq += tot;
-    const int self = in && (!drop || u > sr.tau || (eqf && eq_rank < sr.need_eq)) ? 1 : 0;
+    const int self = in && (!drop || uu > sr.tau || (eqf && eq_rank < sr.need_eq)) ? 1 : 0;
     const int rank = run_sel + block_excl_scan(self, sm, &tot);
     run_sel += tot;
-    if (in) {
-      const int t = cand_token[base + i], j = cand_slot[base + i];
-      const size_t ij = (size_t)t * S + j;
-      if (perm_token) {
-        if (self) {
-          const int q = off_fin[e] + rank;
-          perm_token[q] = t;
-          perm_w[q] = gates[ij];
-          slot_pos[ij] = q;
-        } else {
-          slot_pos[ij] = -1;
-        }
-      }
-      if (kept) kept[ij] = (uint8_t)self;
-    }
+    if (in) emit(i, self, rank);
   }
 }
 
@@ -675,7 +773,7 @@ __global__ __launch_bounds__(1024) void ec_select_kernel(const float *__restrict
                                                          int32_t *__restrict__ slot_pos,
                                                          int32_t *__restrict__ counts,
                                                          int32_t *__restrict__ offsets) {
-  __shared__ int hist[256];
+  __shared__ int hist[kSelWaves * 256];
   __shared__ int sm[1024 / 64 + 1];
   __shared__ float fsm[1024 / 64];
   const int e = blockIdx.x;
@@ -882,21 +980,23 @@ hipError_t launch_router(int dtype, const void *x, const float *w, const float *
 
 hipError_t launch_topk(const float *logits, int T, int E, int k, int kden, int renorm,
                        int want_key, int32_t *ids, float *gates, float *keys, hipStream_t st) {
+  // G lanes per token, each holding up to PL logits: narrow rows keep one logit per lane;
+  // up to 128 experts use 16 lanes x 8 (a 4-step butterfly per pick, 16 tokens per block)
   int G = 64;
   if (E <= 8) G = 8;
   else if (E <= 16) G = 16;
   else if (E <= 32) G = 32;
+  else if (E <= 128) G = 16;
   const int tpb = 256 / G;
   const size_t sh = want_key ? (size_t)tpb * E * sizeof(float) : 0;
   dim3 grid((T + tpb - 1) / tpb);
-#define MOE_TOPK(GG) hipLaunchKernelGGL(topk_kernel<GG>, grid, dim3(256), sh, st, logits, T, E, k, \
-                                        kden, renorm, want_key, ids, gates, keys)
-  switch (G) {
-    case 8: MOE_TOPK(8); break;
-    case 16: MOE_TOPK(16); break;
-    case 32: MOE_TOPK(32); break;
-    default: MOE_TOPK(64); break;
-  }
+#define MOE_TOPK(GG, PL) hipLaunchKernelGGL((topk_kernel<GG, PL>), grid, dim3(256), sh, st, logits, \
+                                            T, E, k, kden, renorm, want_key, ids, gates, keys)
+  if (E <= 8) MOE_TOPK(8, 1);
+  else if (E <= 16) MOE_TOPK(16, 1);
+  else if (E <= 32) MOE_TOPK(32, 1);
+  else if (E <= 128) MOE_TOPK(16, 8);
+  else MOE_TOPK(64, kMaxExperts / 64);
 #undef MOE_TOPK
   return hipGetLastError();
 }
@@ -917,7 +1017,7 @@ void assign_pairs(const RouteScratch &s, const int32_t *ids, const float *gates,
                      s.blk_base, cnt, off, (int32_t *)nullptr, (int32_t *)nullptr);
   if (candidates)
     hipLaunchKernelGGL(assign_scatter_kernel, dim3(nblk), dim3(256), msh, st, ids, gates, s.keys,
-                       T, f, B, off, s.blk_base, 1, s.cand_token, (float *)nullptr, s.cand_slot,
+                       T, f, B, off, s.blk_base, 1, s.cand_token, s.cand_w, s.cand_slot,
                        s.cand_key, (int32_t *)nullptr, (uint8_t *)nullptr);
   else
     hipLaunchKernelGGL(assign_scatter_kernel, dim3(nblk), dim3(256), msh, st, ids, gates,
@@ -943,11 +1043,11 @@ hipError_t launch_token_dispatch(const RouteScratch &s, const int32_t *ids, cons
   hipLaunchKernelGGL(assign_scan_kernel, dim3(1), dim3(1024), 0, st, s.blk_cnt, nblk, E, C,
                      s.blk_base, s.cnt_pre, s.off_pre, counts, offsets);
   hipLaunchKernelGGL(assign_scatter_kernel, dim3(nblk), dim3(256), msh, st, ids, gates, s.keys, T,
-                     all, E, s.off_pre, s.blk_base, 1, s.cand_token, (float *)nullptr,
+                     all, E, s.off_pre, s.blk_base, 1, s.cand_token, s.cand_w,
                      s.cand_slot, s.cand_key, (int32_t *)nullptr, (uint8_t *)nullptr);
   hipLaunchKernelGGL(cap_select_kernel, dim3(E), dim3(1024), 0, st, s.cand_token, s.cand_slot,
-                     s.cand_key, s.cnt_pre, s.off_pre, offsets, C, (const int32_t *)nullptr, k,
-                     gates, perm_token, perm_w, s.slot_pos, kept);
+                     s.cand_key, s.cand_w, s.cnt_pre, s.off_pre, offsets, C, (const int32_t *)nullptr, k,
+                     perm_token, perm_w, s.slot_pos, kept);
   return hipGetLastError();
 }
 
@@ -960,8 +1060,9 @@ hipError_t launch_group_capacity(const RouteScratch &s, const int32_t *ids, cons
   const PairSel grp{nullptr, k, 0, k, gs, k < gs ? k : gs};
   assign_pairs(s, ids, gates, T, grp, D, true, nullptr, nullptr, nullptr, nullptr, nullptr, st);
   hipLaunchKernelGGL(cap_select_kernel, dim3(D), dim3(1024), 0, st, s.cand_token, s.cand_slot,
-                     s.cand_key, s.cnt_pre, s.off_pre, s.off_pre, C_D, (const int32_t *)nullptr,
-                     k, gates, (int32_t *)nullptr, (float *)nullptr, (int32_t *)nullptr, kept);
+                     s.cand_key, s.cand_w, s.cnt_pre, s.off_pre, s.off_pre, C_D,
+                     (const int32_t *)nullptr, k, (int32_t *)nullptr, (float *)nullptr,
+                     (int32_t *)nullptr, kept);
   // dispatch of the kept pairs per expert
   const PairSel fin{kept, k, 0, k, 1, 1};
   assign_pairs(s, ids, gates, T, fin, E, false, perm_token, perm_w, nullptr, counts, offsets, st);
@@ -981,17 +1082,17 @@ hipError_t launch_expanded_drop(const RouteScratch &s, const int32_t *ids, const
   hipLaunchKernelGGL(assign_scan_kernel, dim3(1), dim3(1024), 0, st, s.blk_cnt, nblk, E, C,
                      s.blk_base, s.cnt_pre, s.off_pre, counts, offsets);
   hipLaunchKernelGGL(assign_scatter_kernel, dim3(nblk), dim3(256), msh, st, ids, gates, s.keys, T,
-                     top, E, s.off_pre, s.blk_base, 1, s.cand_token, (float *)nullptr,
+                     top, E, s.off_pre, s.blk_base, 1, s.cand_token, s.cand_w,
                      s.cand_slot, s.cand_key, (int32_t *)nullptr, (uint8_t *)nullptr);
   hipLaunchKernelGGL(cap_select_kernel, dim3(E), dim3(1024), 0, st, s.cand_token, s.cand_slot,
-                     s.cand_key, s.cnt_pre, s.off_pre, s.off_pre, C, (const int32_t *)nullptr, S,
-                     gates, (int32_t *)nullptr, (float *)nullptr, (int32_t *)nullptr, kept);
+                     s.cand_key, s.cand_w, s.cnt_pre, s.off_pre, s.off_pre, C, (const int32_t *)nullptr,
+                     S, (int32_t *)nullptr, (float *)nullptr, (int32_t *)nullptr, kept);
   // 2. offers of the tokens that lost picks, admitted into each expert's leftover places
   hipLaunchKernelGGL(expand_offer_kernel, dim3(nblk), dim3(256), 0, st, kept, T, k, S);
   const PairSel ext{kept, S, k, S, 1, 1};
   assign_pairs(s, ids, gates, T, ext, E, true, nullptr, nullptr, nullptr, nullptr, nullptr, st);
   hipLaunchKernelGGL(cap_select_kernel, dim3(E), dim3(1024), 0, st, s.cand_token, s.cand_slot,
-                     s.cand_key, s.cnt_pre, s.off_pre, s.off_pre, C, counts, S, gates,
+                     s.cand_key, s.cand_w, s.cnt_pre, s.off_pre, s.off_pre, C, counts, S,
                      (int32_t *)nullptr, (float *)nullptr, (int32_t *)nullptr, kept);
   // 3. each token keeps as many admitted extra pairs as it lost, in slot order
   hipLaunchKernelGGL(expand_keep_kernel, dim3(nblk), dim3(256), 0, st, kept, T, k, S);
