@@ -54,97 +54,110 @@ MOE_DEV float rexp_spec(float x) {
 }
 
 // ----------------------------------------------------------------------------------------
-// Router, E <= 8. One workgroup = 4 waves handles 8 tokens; wave w covers one quarter of
-// d_model, lane l the VEC consecutive columns l*VEC (+ 64*VEC steps). Each lane keeps
-// 8 tokens x 8 experts partial sums, a butterfly reduce-scatter leaves lane L with the
-// (token L/8, expert L%8) sum of its wave, and the 4 quarter sums are added in order.
+// Router, E <= 8. A workgroup of 8 waves streams a run of tokens: lane l of wave w owns VEC
+// consecutive columns (w*64 + l)*VEC of a 512*VEC-column pass and keeps their W_r rows in
+// registers, so W_r is read once per workgroup (per pass); x is read once. Per batch of 8
+// tokens each lane accumulates 8 tokens x 8 experts over its columns; a butterfly
+// reduce-scatter leaves lane L with the (token L/8, expert L%8) sum of its wave, and the 8
+// wave sums are added in wave order.
 template <typename XT>
-__global__ __launch_bounds__(256) void router_narrow_kernel(const XT *__restrict__ x,
+__global__ __launch_bounds__(512) void router_narrow_kernel(const XT *__restrict__ x,
                                                             const float *__restrict__ w,
                                                             const float *__restrict__ bias,
                                                             float *__restrict__ logits, int T,
-                                                            int d, int E) {
+                                                            int d, int E, int tok_per_blk) {
   constexpr int VEC = 16 / sizeof(XT);
-  constexpr int TOK = 8, EP = 8;
-  __shared__ float part[4][64];
+  constexpr int TOK = 8, EP = 8, NW = 8;
+  constexpr int PASS = NW * 64 * VEC;
+  __shared__ float part[NW][64];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int t0 = blockIdx.x * TOK;
-  // quarter of d handled by this wave, multiple of VEC
-  const int q = ((d + 4 * VEC - 1) / (4 * VEC)) * VEC;
-  const int jb = wv * q, je = min(d, jb + q);
-  float acc[TOK][EP];
-#pragma unroll
-  for (int i = 0; i < TOK; ++i)
-#pragma unroll
-    for (int e = 0; e < EP; ++e) acc[i][e] = 0.f;
-
-  for (int j0 = jb + lane * VEC; j0 < je; j0 += 64 * VEC) {
-    float wv8[VEC][EP];
-    const bool full = (j0 + VEC <= je);
-    if (E == 8 && full) {
+  const int t_begin = blockIdx.x * tok_per_blk, t_end = min(T, t_begin + tok_per_blk);
+  const int npass = (d + PASS - 1) / PASS;
+  float wreg[VEC][EP];
+  auto load_w = [&](int pass) {
+    const int j0 = pass * PASS + (wv * 64 + lane) * VEC;
+    if (E == 8 && j0 + VEC <= d) {
 #pragma unroll
       for (int v = 0; v < VEC; ++v) {
         const float4 *wp = reinterpret_cast<const float4 *>(w + (size_t)(j0 + v) * 8);
-        float4 a = wp[0], b = wp[1];
-        wv8[v][0] = a.x; wv8[v][1] = a.y; wv8[v][2] = a.z; wv8[v][3] = a.w;
-        wv8[v][4] = b.x; wv8[v][5] = b.y; wv8[v][6] = b.z; wv8[v][7] = b.w;
+        const float4 a = wp[0], b = wp[1];
+        wreg[v][0] = a.x; wreg[v][1] = a.y; wreg[v][2] = a.z; wreg[v][3] = a.w;
+        wreg[v][4] = b.x; wreg[v][5] = b.y; wreg[v][6] = b.z; wreg[v][7] = b.w;
       }
     } else {
 #pragma unroll
       for (int v = 0; v < VEC; ++v)
 #pragma unroll
         for (int e = 0; e < EP; ++e)
-          wv8[v][e] = (j0 + v < je && e < E) ? w[(size_t)(j0 + v) * E + e] : 0.f;
+          wreg[v][e] = (j0 + v < d && e < E) ? w[(size_t)(j0 + v) * E + e] : 0.f;
     }
+  };
+  if (npass == 1) load_w(0);
+  for (int tb = t_begin; tb < t_end; tb += TOK) {
+    float acc[TOK][EP];
 #pragma unroll
-    for (int i = 0; i < TOK; ++i) {
-      const int t = t0 + i;
-      float xv[VEC];
-      if (t < T && full) {
-        const XT *xp = x + (size_t)t * d + j0;
-        if constexpr (sizeof(XT) == 2) {
-          uint4 raw = *reinterpret_cast<const uint4 *>(xp);
-          uint32_t r4[4] = {raw.x, raw.y, raw.z, raw.w};
+    for (int i = 0; i < TOK; ++i)
 #pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            xv[2 * v] = __uint_as_float(r4[v] << 16);
-            xv[2 * v + 1] = __uint_as_float(r4[v] & 0xffff0000u);
+      for (int e = 0; e < EP; ++e) acc[i][e] = 0.f;
+    for (int pass = 0; pass < npass; ++pass) {
+      if (npass > 1) load_w(pass);
+      const int j0 = pass * PASS + (wv * 64 + lane) * VEC;
+      const bool full = j0 + VEC <= d;
+      float xv[TOK][VEC];
+#pragma unroll
+      for (int i = 0; i < TOK; ++i) {
+        const int t = tb + i;
+        if (t < t_end && full) {
+          const XT *xp = x + (size_t)t * d + j0;
+          if constexpr (sizeof(XT) == 2) {
+            const uint4 raw = *reinterpret_cast<const uint4 *>(xp);
+            const uint32_t r4[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+              xv[i][2 * v] = __uint_as_float(r4[v] << 16);
+              xv[i][2 * v + 1] = __uint_as_float(r4[v] & 0xffff0000u);
+            }
+          } else {
+            const float4 raw = *reinterpret_cast<const float4 *>(xp);
+            xv[i][0] = raw.x; xv[i][1] = raw.y; xv[i][2] = raw.z; xv[i][3] = raw.w;
           }
         } else {
-          float4 raw = *reinterpret_cast<const float4 *>(xp);
-          xv[0] = raw.x; xv[1] = raw.y; xv[2] = raw.z; xv[3] = raw.w;
-        }
-      } else {
 #pragma unroll
-        for (int v = 0; v < VEC; ++v)
-          xv[v] = (t < T && j0 + v < je) ? to_f32<XT>(x[(size_t)t * d + j0 + v]) : 0.f;
+          for (int v = 0; v < VEC; ++v)
+            xv[i][v] = (t < t_end && j0 + v < d) ? to_f32<XT>(x[(size_t)t * d + j0 + v]) : 0.f;
+        }
       }
 #pragma unroll
-      for (int v = 0; v < VEC; ++v)
+      for (int i = 0; i < TOK; ++i)
 #pragma unroll
-        for (int e = 0; e < EP; ++e) acc[i][e] = fmaf(xv[v], wv8[v][e], acc[i][e]);
+        for (int v = 0; v < VEC; ++v)
+#pragma unroll
+          for (int e = 0; e < EP; ++e) acc[i][e] = fmaf(xv[i][v], wreg[v][e], acc[i][e]);
     }
-  }
-  // butterfly reduce-scatter of the 64 (token, expert) sums across the wave
-  float v[64];
+    // butterfly reduce-scatter of the 64 (token, expert) sums across the wave
+    float v[64];
 #pragma unroll
-  for (int i = 0; i < 64; ++i) v[i] = acc[i / EP][i % EP];
+    for (int i = 0; i < 64; ++i) v[i] = acc[i / EP][i % EP];
 #pragma unroll
-  for (int o = 32, n = 64; o > 0; o >>= 1, n >>= 1) {
-    const bool up = (lane & o) != 0;
+    for (int o = 32, n = 64; o > 0; o >>= 1, n >>= 1) {
+      const bool up = (lane & o) != 0;
 #pragma unroll
-    for (int i = 0; i < n / 2; ++i) {
-      float send = up ? v[i] : v[i + n / 2];
-      float keep = up ? v[i + n / 2] : v[i];
-      v[i] = keep + __shfl_xor(send, o, 64);
+      for (int i = 0; i < n / 2; ++i) {
+        const float send = up ? v[i] : v[i + n / 2];
+        const float keep = up ? v[i + n / 2] : v[i];
+        v[i] = keep + __shfl_xor(send, o, 64);
+      }
     }
-  }
-  part[wv][lane] = v[0];
-  __syncthreads();
-  if (wv == 0) {
-    const int t = t0 + lane / EP, e = lane % EP;
-    float s = ((part[0][lane] + part[1][lane]) + part[2][lane]) + part[3][lane];
-    if (t < T && e < E) logits[(size_t)t * E + e] = s + (bias ? bias[e] : 0.f);
+    part[wv][lane] = v[0];
+    __syncthreads();
+    if (wv == 0) {
+      const int t = tb + lane / EP, e = lane % EP;
+      float sum = part[0][lane];
+#pragma unroll
+      for (int q = 1; q < NW; ++q) sum += part[q][lane];
+      if (t < t_end && e < E) logits[(size_t)t * E + e] = sum + (bias ? bias[e] : 0.f);
+    }
+    __syncthreads();
   }
 }
 
@@ -959,13 +972,16 @@ hipError_t launch_router(int dtype, const void *x, const float *w, const float *
     return hipGetLastError();
   }
   if (E <= 8) {
-    dim3 grid((T + 7) / 8);
+    // tokens per workgroup: a multiple of 8, about T / 256 (one workgroup per CU)
+    int tpb = ((T + 255) / 256 + 7) / 8 * 8;
+    if (tpb < 8) tpb = 8;
+    dim3 grid((T + tpb - 1) / tpb);
     if (dtype == 0)
-      hipLaunchKernelGGL(router_narrow_kernel<float>, grid, dim3(256), 0, st,
-                         (const float *)x, w, bias, logits, T, d, E);
+      hipLaunchKernelGGL(router_narrow_kernel<float>, grid, dim3(512), 0, st,
+                         (const float *)x, w, bias, logits, T, d, E, tpb);
     else
-      hipLaunchKernelGGL(router_narrow_kernel<bf16_t>, grid, dim3(256), 0, st,
-                         (const bf16_t *)x, w, bias, logits, T, d, E);
+      hipLaunchKernelGGL(router_narrow_kernel<bf16_t>, grid, dim3(512), 0, st,
+                         (const bf16_t *)x, w, bias, logits, T, d, E, tpb);
   } else {
     dim3 grid((T + 63) / 64, (E + 127) / 128);
     if (dtype == 0)
