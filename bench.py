@@ -13,6 +13,7 @@ from __future__ import annotations
 
 import argparse
 import json
+import math
 import os
 import sys
 import time
@@ -106,10 +107,17 @@ def cpu_baseline(inp, sample_tokens=0, target_s=20.0):
                 b = (dt - t1) / (sample_tokens - n1)
                 sample_tokens = int(min(T, sample_tokens + (target_s - dt) / b))
                 dt = timed(sample_tokens)
-    return {"value": round(sample_tokens / dt, 2), "unit": "tokens/s", "cores": int(threads),
+    reps = 1
+    if sample_tokens == T and dt < 10.0:
+        # the whole workload is quicker than the bound: repeat it to time ~10 s of work
+        reps = int(min(5, math.ceil(10.0 / max(dt, 1e-3))))
+        if reps > 1:
+            dt = sum(timed(T) for _ in range(reps))
+    what = (f"all {T} tokens, {reps} runs" if reps > 1 else
+            f"first {sample_tokens} of {T} tokens (routing over all {T})")
+    return {"value": round(reps * sample_tokens / dt, 2), "unit": "tokens/s", "cores": int(threads),
             "kind": "oracle",
-            "sample": f"first {sample_tokens} of {T} tokens (routing over all {T}), float64 "
-                      f"numpy oracle, {dt:.1f} s on {threads} BLAS threads"}
+            "sample": f"{what}, float64 numpy oracle, {dt:.1f} s on {threads} BLAS threads"}
 
 
 def recorded_traffic(workload):
