@@ -7,7 +7,8 @@
 // K-contiguous (weights in [out, in] layout), so A and B tiles stream along K.
 //
 // bf16 path: persistent workgroups walk a tile list built on the device from the
-// per-expert row counts (no host round trip). A tile is 256 rows x 256 columns; K goes in
+// per-expert row counts (no host round trip). A tile is 256 rows x 256 columns (a group's
+// last row tile shrinks to 64 or 128 rows when that covers its remaining rows); K goes in
 // slices of 64 through two 64 KB LDS stages (one lands while the other feeds the MFMAs).
 // Waves (4 as 2 x 2 of 128 x 128, or 8 as 2 x 4 of 128 x 64) compute with
 // v_mfma_f32_32x32x16_bf16 into float32 accumulators. Slices are copied from global memory
@@ -158,25 +159,31 @@ MOE_DEV void g2lds16(const void *g, char *lds_base) {
 // for writes to the stage being read.
 struct Stage { char a[BM * kRowBytes]; char b[BN * kRowBytes]; };
 
+// Row tiles. A group's rows go in tiles of 256; its last tile, holding rem = rows - m0 rows,
+// shrinks to 64 * MB rows with MB = 1 (rem <= 64), 2 (rem <= 128) or 4, so a ragged group
+// end costs MFMAs for at most 63 padding rows instead of up to 255. Wave row wm of a tile
+// owns rows wm * 32 MB .. + 32 MB - 1 as MB blocks of 32.
+MOE_DEV int tile_mb(int rem) { return rem > 128 ? 4 : (rem > 64 ? 2 : 1); }
+
 // fragments of sub-step ks (k = 16 ks .. 16 ks + 15 of the slice)
-template <int W>
-MOE_DEV void load_frags(const Stage &st, int lane, int wm, int wn, int ks, bf16x8_t (&af)[4],
+template <int W, int MB>
+MOE_DEV void load_frags(const Stage &st, int lane, int wm, int wn, int ks, bf16x8_t (&af)[MB],
                         bf16x8_t (&bfr)[Cfg<W>::NB]) {
   const int chunk = ks * 2 + (lane >> 5);
 #pragma unroll
-  for (int mb = 0; mb < 4; ++mb)
-    af[mb] = *reinterpret_cast<const bf16x8_t *>(st.a + swz(wm * 128 + mb * 32 + (lane & 31), chunk));
+  for (int mb = 0; mb < MB; ++mb)
+    af[mb] = *reinterpret_cast<const bf16x8_t *>(st.a + swz(wm * 32 * MB + mb * 32 + (lane & 31), chunk));
 #pragma unroll
   for (int nb = 0; nb < Cfg<W>::NB; ++nb)
     bfr[nb] = *reinterpret_cast<const bf16x8_t *>(
         st.b + swz(wn * Cfg<W>::WCOLS + nb * 32 + (lane & 31), chunk));
 }
 
-template <int W>
-MOE_DEV void mfma_block(const bf16x8_t (&af)[4], const bf16x8_t (&bfr)[Cfg<W>::NB],
-                        f32x16_t (&acc)[4][Cfg<W>::NB]) {
+template <int W, int MB>
+MOE_DEV void mfma_block(const bf16x8_t (&af)[MB], const bf16x8_t (&bfr)[Cfg<W>::NB],
+                        f32x16_t (&acc)[MB][Cfg<W>::NB]) {
 #pragma unroll
-  for (int mb = 0; mb < 4; ++mb)
+  for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
     for (int nb = 0; nb < Cfg<W>::NB; ++nb)
       acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mb], bfr[nb], acc[mb][nb], 0, 0, 0);
@@ -185,30 +192,203 @@ MOE_DEV void mfma_block(const bf16x8_t (&af)[4], const bf16x8_t (&bfr)[Cfg<W>::N
 // keep the instruction order written here (no scheduling across this point)
 MOE_DEV void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
 
+// Instruction order of one sub-step's N MFMAs: after MFMA I come I-th shares of the DMA
+// global->LDS copies and of the RD LDS fragment reads (one read after each of the first RD
+// MFMAs when RD <= N).
+template <int N, int DMA, int RD, int I = 0>
+MOE_DEV void sched_sub() {
+  if constexpr (I < N) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    constexpr int c = (DMA * (I + 1)) / N - (DMA * I) / N;
+    if constexpr (c > 0) __builtin_amdgcn_sched_group_barrier(0x020, c, 0);
+    constexpr int r = RD <= N ? (I < RD ? 1 : 0) : (RD * (I + 1)) / N - (RD * I) / N;
+    if constexpr (r > 0) __builtin_amdgcn_sched_group_barrier(0x100, r, 0);
+    sched_sub<N, DMA, RD, I + 1>();
+  }
+}
+
 // Offset of tile element (tr, tc) (tc a B-tile column) in a partial tile stored in
-// accumulator register order: wave (tr/128)*WN + tc/WCOLS, then block (mb, nb) =
-// (tr%128/32, tc%WCOLS/32), register i = 4*(tr%32/8) + tr%4, lane = tc%32 + 32*(tr%8/4).
+// accumulator register order: wave (tr/(32 MB))*WN + tc/WCOLS, then block (mb, nb) =
+// (tr%(32 MB)/32, tc%WCOLS/32), register i = 4*(tr%32/8) + tr%4, lane = tc%32 + 32*(tr%8/4).
 // The row and column parts add, and 4 adjacent columns (tc % 4 == 0) are 4 adjacent floats.
-template <int W> MOE_DEV int part_index(int tr, int tc) {
+template <int W> MOE_DEV int part_index(int tr, int tc, int MB) {
   using C = Cfg<W>;
-  const int row_part = (tr >> 7) * C::WN * C::PART_WAVE + ((tr >> 5) & 3) * C::NB * 16 * 64 +
+  const int rpw = 32 * MB;
+  const int row_part = (tr / rpw) * C::WN * C::PART_WAVE + ((tr % rpw) >> 5) * C::NB * 16 * 64 +
                        (4 * ((tr >> 3) & 3) + (tr & 3)) * 64 + 32 * ((tr >> 2) & 1);
   const int col_part = (tc / C::WCOLS) * C::PART_WAVE + ((tc % C::WCOLS) >> 5) * 16 * 64 + (tc & 31);
   return row_part + col_part;
 }
 
-template <bool GATE_UP, int W>
-__global__ __launch_bounds__(64 * W, 1) void gemm_bf16_kernel(GemmArgs args) {
+// One unit: a row tile of 64*MB rows x 256 B-columns over K-steps [k_begin, k_begin + nk),
+// stored whole (punit < 0) or as the float32 partial tile punit.
+template <bool GATE_UP, int W, int MB>
+MOE_DEV __attribute__((always_inline)) void gemm_tile(const GemmArgs &args, const GroupDesc &d,
+                                                      Stage &st0, Stage &st1, int n_tile, int m0,
+                                                      int nk, int k_begin, int punit) {
   using C = Cfg<W>;
   constexpr int NB = C::NB;
+  constexpr int TBM = 64 * MB;                    // tile rows
+  constexpr int A_DMA = TBM * kRowBytes / 1024 / W;   // A copies per wave per slice
+  constexpr int DMA = A_DMA + C::B_DMA;
+  constexpr int BNOUT = GATE_UP ? BN / 2 : BN;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int wm = wv / C::WN, wn = wv % C::WN;
+  // Loader: wave wv fills A rows wv*TBM/W .. and B rows wv*BN/W .. with copies of 1 KB
+  // (8 rows of 128 B); lane L fetches row r0 + L/8, physical chunk L%8, i.e. logical
+  // K-chunk (L%8) ^ ((row/2)%8). For gate/up the B tile holds, per wave column wn,
+  // WCOLS/2 gate rows then the matching WCOLS/2 up rows (h columns n_tile*128 +
+  // wn*WCOLS/2 + j), so the B rows a wave loads are all gate (wv even) or all up (wv odd).
+  const int wvu = __builtin_amdgcn_readfirstlane(wv);   // wave-uniform, kept in SGPRs
+  const char *Ab = (const char *)d.A;
+  const char *Bb = (const char *)((GATE_UP && (wvu & 1)) ? d.B1 : d.B0);
+  uint32_t aoff[A_DMA], boff[C::B_DMA];   // per-lane byte offsets from the slice bases
+#pragma unroll
+  for (int i = 0; i < A_DMA; ++i) {
+    const int r = wvu * (TBM / W) + i * 8 + (lane >> 3);
+    const int c = (lane & 7) ^ ((r >> 1) & 7);
+    int arow = min(m0 + r, d.rows - 1);
+    if (d.amap) arow = d.amap[arow];   // dispatch gather folded into the operand load
+    aoff[i] = ((uint32_t)arow * (uint32_t)d.lda + c * 8) * 2u;
+  }
+#pragma unroll
+  for (int i = 0; i < C::B_DMA; ++i) {
+    const int r = wvu * (BN / W) + i * 8 + (lane >> 3);
+    const int c = (lane & 7) ^ ((r >> 1) & 7);
+    const int n = GATE_UP ? n_tile * (BN / 2) + (wvu >> 1) * (C::WCOLS / 2) +
+                                (r & (C::WCOLS / 2 - 1))
+                          : n_tile * BN + r;
+    boff[i] = ((uint32_t)min(n, d.N - 1) * (uint32_t)d.K + c * 8) * 2u;
+  }
+  const int aofs = wvu * A_DMA * 1024, bofs = wvu * C::B_DMA * 1024;
+  auto issue = [&](Stage &s, int kt) {
+    const char *a = Ab + (size_t)(k_begin + kt) * kRowBytes;
+    const char *b = Bb + (size_t)(k_begin + kt) * kRowBytes;
+#pragma unroll
+    for (int i = 0; i < A_DMA; ++i) g2lds16(a + aoff[i], s.a + aofs + i * 1024);
+#pragma unroll
+    for (int i = 0; i < C::B_DMA; ++i) g2lds16(b + boff[i], s.b + bofs + i * 1024);
+  };
+  f32x16_t acc[MB][NB];
+#pragma unroll
+  for (int i = 0; i < MB; ++i)
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+
+  // Pipeline. Slice s lives in stage s % 2. Step kt waits until slice kt has landed,
+  // passes the barrier (every wave has its last fragments of slice kt-1 in registers by
+  // then, so that stage is free), issues the copy of slice kt+1 into it, and runs the
+  // MFMAs: those of the last sub-step of slice kt-1, then sub-steps 0..2 of slice kt, each
+  // with the LDS reads of the next sub-step (and, in the first, the copies) slotted
+  // between them. The last sub-step of slice kt runs after the next barrier. Fragments
+  // alternate between two register sets (even and odd sub-steps).
+  bf16x8_t fa0[MB], fb0[NB], fa1[MB], fb1[NB];
+#pragma unroll
+  for (int i = 0; i < MB; ++i) fa1[i] = bf16x8_t{};   // "slice -1": contributes 0 * 0
+#pragma unroll
+  for (int i = 0; i < NB; ++i) fb1[i] = bf16x8_t{};
+  issue(st0, 0);
+  // MFMAs of (fa, fb) with the fragment reads of the next sub-step between them
+  auto sub = [&](const bf16x8_t (&fa)[MB], const bf16x8_t (&fb)[NB], const Stage &cur, int ks,
+                 bf16x8_t (&na)[MB], bf16x8_t (&nb)[NB]) {
+    load_frags<W, MB>(cur, lane, wm, wn, ks, na, nb);
+    mfma_block<W, MB>(fa, fb, acc);
+    sched_sub<MB * NB, 0, MB + NB>();
+    sched_fence();
+  };
+  auto step = [&](Stage &cur, Stage &refill, int kt) {
+    sched_fence();
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");   // slice kt has landed
+    __builtin_amdgcn_s_barrier();
+    sched_fence();
+    issue(refill, min(kt + 1, nk - 1));   // past the end: re-read the last slice
+    load_frags<W, MB>(cur, lane, wm, wn, 0, fa0, fb0);
+    mfma_block<W, MB>(fa1, fb1, acc);      // last sub-step of slice kt-1
+    sched_sub<MB * NB, DMA, MB + NB>();    // copies and reads between the MFMAs
+    sched_fence();
+    sub(fa0, fb0, cur, 1, fa1, fb1);
+    sub(fa1, fb1, cur, 2, fa0, fb0);
+    sub(fa0, fb0, cur, 3, fa1, fb1);
+  };
+  static_assert(kSub == 4 && NSTAGE == 2, "the step above runs four sub-steps, two stages");
+  // Two steps per iteration alternate the stages. The loop body is one branch-free block,
+  // so the compiler's wait counts stay exact inside it; an odd last step follows it.
+  int kt = 0;
+  for (; kt + 2 <= nk; kt += 2) {
+    step(st0, st1, kt);
+    step(st1, st0, kt + 1);
+  }
+  if (kt < nk) step(st0, st1, kt);
+  mfma_block<W, MB>(fa1, fb1, acc);   // last sub-step of the last slice
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the surplus copy of the last step
+  __syncthreads();   // every wave is done with every stage before the next tile's loads
+  if (punit >= 0) {
+    // K-part of a split tile: the raw accumulators in register order (wave, mb, nb, i,
+    // lane), so each store is 256 contiguous bytes; the reduction maps them back
+    float *Pt = args.partials + (size_t)punit * (BM * BN) + wv * C::PART_WAVE + lane;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) Pt[((mb * NB + nb) * 16 + i) * 64] = acc[mb][nb][i];
+    return;
+  }
+  // epilogue: h in bf16 (it feeds the next bf16 GEMM), o in float32. Lane (c, r4) holds
+  // column c of rows r4*4 + {0..3} + 8j of each 32 x 32 block. Stores go through a buffer
+  // resource spanning exactly the group's output rows, so the hardware drops the stores of
+  // rows past the group's end (a partial last row tile needs no per-element branch). The
+  // lane index is made opaque so the per-lane offset is rebuilt each tile rather than
+  // hoisted with 256 others.
+  int lo = lane;
+  asm volatile("" : "+v"(lo));
+  constexpr int CE = GATE_UP ? 2 : 4;   // bytes per output element
+  constexpr int OB = GATE_UP ? NB / 2 : NB;   // output blocks per wave row
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      d.C, (short)0, (int)((uint32_t)d.rows * (uint32_t)d.ldc * CE), 0x00020000);
+  const int cw = n_tile * BNOUT + wn * (OB * 32);   // first output column of this wave
+  const int nbv = (d.N - cw) >= OB * 32 ? OB : (d.N - cw) / 32;   // live blocks
+  const uint32_t rowb = (uint32_t)d.ldc * CE;
+  // running byte offset of this lane's current row, advanced row by row (kept opaque so the
+  // compiler does not expand it into one live offset per row)
+  uint32_t roff = (uint32_t)(m0 + wm * 32 * MB + 4 * (lo >> 5)) * rowb + (uint32_t)(cw + (lo & 31)) * CE;
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+#pragma unroll
+      for (int nb = 0; nb < OB; ++nb) {
+        if (nb < nbv) {
+          if (GATE_UP) {
+            const float gv = acc[mb][nb][i], uv = acc[mb][nb + OB][i];
+            const float h = gv / (1.0f + __expf(-gv)) * uv;
+            __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(h), rs, (int)(roff + nb * 32 * CE),
+                                                  0, 0);
+          } else {
+            float v = acc[mb][nb][i];
+            asm volatile("" : "+v"(v));
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), rs,
+                                                  (int)(roff + nb * 32 * CE), 0, 0);
+          }
+        }
+      }
+      // next row of this lane: +1 inside a group of 4, +5 after the 4th (rows 4..7 belong
+      // to the other half-wave), the last i of a block steps to the next block the same way
+      roff += ((i & 3) == 3 ? 5u : 1u) * rowb;
+      asm volatile("" : "+v"(roff));
+    }
+}
+
+template <bool GATE_UP, int W>
+__global__ __launch_bounds__(64 * W, 1) void gemm_bf16_kernel(GemmArgs args) {
   __shared__ Stage st0, st1;
   __shared__ int tstart[kMaxGroups + 1];
   __shared__ int sm[kMaxWaves + 1];
   constexpr int BNOUT = GATE_UP ? BN / 2 : BN;   // output columns per tile (h or o)
   const int G = build_tile_table<BM, BNOUT>(args, tstart, sm);
   const int total = tstart[G];
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int wm = wv / C::WN, wn = wv % C::WN;
 
   const SplitPlan sp = split_plan(total, gridDim.x, args.K / BK, args.split_ok);
   const int units = sp.full + sp.L * sp.S;
@@ -227,161 +407,12 @@ __global__ __launch_bounds__(64 * W, 1) void gemm_bf16_kernel(GemmArgs args) {
     const int m0 = m_tile * BM;
     const int nk = (d.K / BK) / nparts;   // K-steps of this unit
     const int k_begin = part * nk;         // first K-step of this unit
-    // Loader: wave wv fills A rows wv*BM/W .. and B rows wv*BN/W .. with copies of 1 KB
-    // (8 rows of 128 B); lane L fetches row r0 + L/8, physical chunk L%8, i.e. logical
-    // K-chunk (L%8) ^ ((row/2)%8). For gate/up the B tile holds, per wave column wn,
-    // WCOLS/2 gate rows then the matching WCOLS/2 up rows (h columns n_tile*128 +
-    // wn*WCOLS/2 + j), so the B rows a wave loads are all gate (wv even) or all up (wv odd).
-    const int wvu = __builtin_amdgcn_readfirstlane(wv);   // wave-uniform, kept in SGPRs
-    const char *Ab = (const char *)d.A;
-    const char *Bb = (const char *)((GATE_UP && (wvu & 1)) ? d.B1 : d.B0);
-    uint32_t aoff[C::A_DMA], boff[C::B_DMA];   // per-lane byte offsets from the slice bases
-#pragma unroll
-    for (int i = 0; i < C::A_DMA; ++i) {
-      const int r = wvu * (BM / W) + i * 8 + (lane >> 3);
-      const int c = (lane & 7) ^ ((r >> 1) & 7);
-      int arow = min(m0 + r, d.rows - 1);
-      if (d.amap) arow = d.amap[arow];   // dispatch gather folded into the operand load
-      aoff[i] = ((uint32_t)arow * (uint32_t)d.lda + c * 8) * 2u;
+    const int punit = nparts > 1 ? u - sp.full : -1;
+    switch (tile_mb(d.rows - m0)) {
+      case 4: gemm_tile<GATE_UP, W, 4>(args, d, st0, st1, n_tile, m0, nk, k_begin, punit); break;
+      case 2: gemm_tile<GATE_UP, W, 2>(args, d, st0, st1, n_tile, m0, nk, k_begin, punit); break;
+      default: gemm_tile<GATE_UP, W, 1>(args, d, st0, st1, n_tile, m0, nk, k_begin, punit); break;
     }
-#pragma unroll
-    for (int i = 0; i < C::B_DMA; ++i) {
-      const int r = wvu * (BN / W) + i * 8 + (lane >> 3);
-      const int c = (lane & 7) ^ ((r >> 1) & 7);
-      const int n = GATE_UP ? n_tile * (BN / 2) + (wvu >> 1) * (C::WCOLS / 2) +
-                                  (r & (C::WCOLS / 2 - 1))
-                            : n_tile * BN + r;
-      boff[i] = ((uint32_t)min(n, d.N - 1) * (uint32_t)d.K + c * 8) * 2u;
-    }
-    const int aofs = wvu * C::A_DMA * 1024, bofs = wvu * C::B_DMA * 1024;
-    auto issue = [&](Stage &s, int kt) {
-      const char *a = Ab + (size_t)(k_begin + kt) * kRowBytes;
-      const char *b = Bb + (size_t)(k_begin + kt) * kRowBytes;
-#pragma unroll
-      for (int i = 0; i < C::A_DMA; ++i) g2lds16(a + aoff[i], s.a + aofs + i * 1024);
-#pragma unroll
-      for (int i = 0; i < C::B_DMA; ++i) g2lds16(b + boff[i], s.b + bofs + i * 1024);
-    };
-    f32x16_t acc[4][NB];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < NB; ++j)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
-
-    // Pipeline. Slice s lives in stage s % 2. Step kt waits until slice kt has landed,
-    // passes the barrier (every wave has its last fragments of slice kt-1 in registers by
-    // then, so that stage is free), issues the copy of slice kt+1 into it, and runs the
-    // MFMAs: those of the last sub-step of slice kt-1, then sub-steps 0..2 of slice kt, each
-    // with the LDS reads of the next sub-step (and, in the first, the copies) slotted
-    // between them. The last sub-step of slice kt runs after the next barrier. Fragments
-    // alternate between two register sets (even and odd sub-steps).
-    bf16x8_t fa0[4], fb0[NB], fa1[4], fb1[NB];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) fa1[i] = bf16x8_t{};   // "slice -1": contributes 0 * 0
-#pragma unroll
-    for (int i = 0; i < NB; ++i) fb1[i] = bf16x8_t{};
-    issue(st0, 0);
-    // MFMAs of (fa, fb) with the fragment reads of the next sub-step between them
-    auto sub = [&](const bf16x8_t (&fa)[4], const bf16x8_t (&fb)[NB], const Stage &cur, int ks,
-                   bf16x8_t (&na)[4], bf16x8_t (&nb)[NB]) {
-      load_frags<W>(cur, lane, wm, wn, ks, na, nb);
-      mfma_block<W>(fa, fb, acc);
-#pragma unroll
-      for (int i = 0; i < 4 * NB; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        if (i < 4 + NB) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      }
-      sched_fence();
-    };
-    auto step = [&](Stage &cur, Stage &refill, int kt) {
-      sched_fence();
-      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");   // slice kt has landed
-      __builtin_amdgcn_s_barrier();
-      sched_fence();
-      issue(refill, min(kt + 1, nk - 1));   // past the end: re-read the last slice
-      load_frags<W>(cur, lane, wm, wn, 0, fa0, fb0);
-      mfma_block<W>(fa1, fb1, acc);          // last sub-step of slice kt-1
-#pragma unroll
-      for (int i = 0; i < 4 * NB; ++i) {     // copies and reads between the MFMAs
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x020, C::DMA / (4 * NB), 0);
-        if (i < 4 + NB) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      }
-      sched_fence();
-      sub(fa0, fb0, cur, 1, fa1, fb1);
-      sub(fa1, fb1, cur, 2, fa0, fb0);
-      sub(fa0, fb0, cur, 3, fa1, fb1);
-    };
-    static_assert(kSub == 4 && NSTAGE == 2, "the step above runs four sub-steps, two stages");
-    static_assert(C::DMA % (4 * NB) == 0, "copies spread evenly over the first MFMAs");
-    // Two steps per iteration alternate the stages. The loop body is one branch-free block,
-    // so the compiler's wait counts stay exact inside it; an odd last step follows it.
-    int kt = 0;
-    for (; kt + 2 <= nk; kt += 2) {
-      step(st0, st1, kt);
-      step(st1, st0, kt + 1);
-    }
-    if (kt < nk) step(st0, st1, kt);
-    mfma_block<W>(fa1, fb1, acc);   // last sub-step of the last slice
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the surplus copy of the last step
-    __syncthreads();   // every wave is done with every stage before the next tile's loads
-    if (nparts > 1) {
-      // K-part of a split tile: the raw accumulators in register order (wave, mb, nb, i,
-      // lane), so each store is 256 contiguous bytes; the reduction maps them back
-      float *Pt = args.partials + (size_t)(u - sp.full) * (BM * BN) + wv * C::PART_WAVE + lane;
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) Pt[((mb * NB + nb) * 16 + i) * 64] = acc[mb][nb][i];
-      continue;
-    }
-    // epilogue: h in bf16 (it feeds the next bf16 GEMM), o in float32. Lane (c, r4) holds
-    // column c of rows r4*4 + {0..3} + 8j of each 32 x 32 block. Stores go through a buffer
-    // resource spanning exactly the group's output rows, so the hardware drops the stores of
-    // rows past the group's end (a partial last row tile needs no per-element branch). The
-    // lane index is made opaque so the per-lane offset is rebuilt each tile rather than
-    // hoisted with 256 others.
-    int lo = lane;
-    asm volatile("" : "+v"(lo));
-    constexpr int CE = GATE_UP ? 2 : 4;   // bytes per output element
-    constexpr int OB = GATE_UP ? NB / 2 : NB;   // output blocks per wave row
-    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-        d.C, (short)0, (int)((uint32_t)d.rows * (uint32_t)d.ldc * CE), 0x00020000);
-    const int cw = n_tile * BNOUT + wn * (OB * 32);   // first output column of this wave
-    const int nbv = (d.N - cw) >= OB * 32 ? OB : (d.N - cw) / 32;   // live blocks
-    const uint32_t rowb = (uint32_t)d.ldc * CE;
-    // running byte offset of this lane's current row, advanced row by row (kept opaque so the
-    // compiler does not expand it into one live offset per row)
-    uint32_t roff = (uint32_t)(m0 + wm * 128 + 4 * (lo >> 5)) * rowb + (uint32_t)(cw + (lo & 31)) * CE;
-#pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-#pragma unroll
-        for (int nb = 0; nb < OB; ++nb) {
-          if (nb < nbv) {
-            if (GATE_UP) {
-              const float gv = acc[mb][nb][i], uv = acc[mb][nb + OB][i];
-              const float h = gv / (1.0f + __expf(-gv)) * uv;
-              __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(h), rs, (int)(roff + nb * 32 * CE),
-                                                    0, 0);
-            } else {
-              float v = acc[mb][nb][i];
-              asm volatile("" : "+v"(v));
-              __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), rs,
-                                                    (int)(roff + nb * 32 * CE), 0, 0);
-            }
-          }
-        }
-        // next row of this lane: +1 inside a group of 4, +5 after the 4th (rows 4..7 belong
-        // to the other half-wave), the last i of a block steps to the next block the same way
-        roff += ((i & 3) == 3 ? 5u : 1u) * rowb;
-        asm volatile("" : "+v"(roff));
-      }
   }
 }
 
@@ -411,18 +442,19 @@ __global__ __launch_bounds__(256) void gemm_tail_reduce_kernel(GemmArgs args) {
     const int local = tile - tstart[g];
     const int mt = (d.rows + BM - 1) / BM;
     const int n_tile = local / mt, m_tile = local % mt;
+    const int MB = tile_mb(d.rows - m_tile * BM);      // the unit's row-tile height / 64
     const int c = (threadIdx.x % TPR) * 4;             // first of 4 output columns in the tile
     const int col = n_tile * BNOUT + c;
     if (col >= d.N) continue;                         // N is a multiple of 64: whole groups of 4
     for (int rr = threadIdx.x / TPR; rr < kReduceRows; rr += RPP) {
       const int tr = r0 + rr, row = m_tile * BM + tr;
       if (row >= d.rows) break;
-      const float *P0 = args.partials + (size_t)l * sp.S * PART + part_index<W>(tr, 0);
+      const float *P0 = args.partials + (size_t)l * sp.S * PART + part_index<W>(tr, 0, MB);
       if (GATE_UP) {
         // h column c: gate sum at B-tile column (c / (WCOLS/2)) * WCOLS + c % (WCOLS/2), up
         // sum WCOLS/2 columns further
         const int tc = (c / (C::WCOLS / 2)) * C::WCOLS + c % (C::WCOLS / 2);
-        const int og = part_index<W>(0, tc), ou = part_index<W>(0, tc + C::WCOLS / 2);
+        const int og = part_index<W>(0, tc, MB), ou = part_index<W>(0, tc + C::WCOLS / 2, MB);
         float4 gp[8], up[8];
 #pragma unroll
         for (int p = 0; p < 8; ++p)
@@ -450,7 +482,7 @@ __global__ __launch_bounds__(256) void gemm_tail_reduce_kernel(GemmArgs args) {
         float4 pp[8];
 #pragma unroll
         for (int p = 0; p < 8; ++p)
-          if (p < sp.S) pp[p] = *(const float4 *)(P0 + (size_t)p * PART + part_index<W>(0, c));
+          if (p < sp.S) pp[p] = *(const float4 *)(P0 + (size_t)p * PART + part_index<W>(0, c, MB));
         float4 v = pp[0];
 #pragma unroll
         for (int p = 1; p < 8; ++p)
