@@ -192,6 +192,24 @@ MOE_DEV void mfma_block(const bf16x8_t (&af)[MB], const bf16x8_t (&bfr)[Cfg<W>::
 // keep the instruction order written here (no scheduling across this point)
 MOE_DEV void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
 
+// s_waitcnt until at most VM vector-memory and LGKM LDS/scalar operations are outstanding.
+// Issued through the builtin, not inline asm, so the compiler's own wait insertion knows
+// which copies have landed: after an opaque wait it would still count the previous slice's
+// global->LDS copies as in flight and stall the first LDS read behind the copies just issued.
+template <int VM, int LGKM> MOE_DEV void wait_vm_lgkm() {
+  static_assert(VM >= 0 && VM < 64 && LGKM >= 0 && LGKM < 16, "gfx9 s_waitcnt fields");
+  __builtin_amdgcn_s_waitcnt((VM & 15) | ((VM >> 4) << 14) | (7 << 4) | (LGKM << 8));
+}
+
+// The wait above, then the workgroup barrier; the empty asm statements keep the compiler
+// from moving LDS accesses across either (they emit no instruction).
+template <int VM> MOE_DEV void wait_and_barrier() {
+  wait_vm_lgkm<VM, 0>();
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // Instruction order of one sub-step's N MFMAs: after MFMA I come I-th shares of the DMA
 // global->LDS copies and of the RD LDS fragment reads (one read after each of the first RD
 // MFMAs when RD <= N).
@@ -300,8 +318,7 @@ MOE_DEV __attribute__((always_inline)) void gemm_tile(const GemmArgs &args, cons
   };
   auto step = [&](Stage &cur, Stage &refill, int kt) {
     sched_fence();
-    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");   // slice kt has landed
-    __builtin_amdgcn_s_barrier();
+    wait_and_barrier<0>();                 // slice kt has landed
     sched_fence();
     issue(refill, min(kt + 1, nk - 1));   // past the end: re-read the last slice
     load_frags<W, MB>(cur, lane, wm, wn, 0, fa0, fb0);
@@ -322,7 +339,7 @@ MOE_DEV __attribute__((always_inline)) void gemm_tile(const GemmArgs &args, cons
   }
   if (kt < nk) step(st0, st1, kt);
   mfma_block<W, MB>(fa1, fb1, acc);   // last sub-step of the last slice
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the surplus copy of the last step
+  wait_vm_lgkm<0, 15>();   // the surplus copy of the last step
   __syncthreads();   // every wave is done with every stage before the next tile's loads
   if (punit >= 0) {
     // K-part of a split tile: the raw accumulators in register order (wave, mb, nb, i,
@@ -528,7 +545,6 @@ size_t skinny_partial_bytes(const GemmArgs &a, bool gate_up) {
   return (size_t)sp.S * (size_t)(a.rcap + a.s_rows) * sp.pitch * 4;
 }
 
-template <int N> MOE_DEV void wait_vm_n() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
 
 template <int MB> struct SkStage { char a[32 * MB * kRowBytes]; char b[BN * kRowBytes]; };
 
@@ -589,9 +605,7 @@ __global__ __launch_bounds__(256, 1) void gemm_skinny_kernel(GemmArgs args) {
     issue(st1, min(1, nk - 1));
     auto step = [&](const SkStage<MB> &cur, SkStage<MB> &refill, int kt) {
       sched_fence();
-      wait_vm_n<DMA>();                            // slice kt has landed (kt+1 may not)
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-      __builtin_amdgcn_s_barrier();
+      wait_and_barrier<DMA>();                     // slice kt has landed (kt+1 may not)
       sched_fence();
       issue(refill, min(kt + 2, nk - 1));           // past the end: re-read the last slice
 #pragma unroll
@@ -622,7 +636,7 @@ __global__ __launch_bounds__(256, 1) void gemm_skinny_kernel(GemmArgs args) {
       step(st0, st2, kt);
       if (kt + 1 < nk) step(st1, st0, kt + 1);
     }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    wait_vm_lgkm<0, 15>();
     __syncthreads();   // every wave is done with every stage before the next unit's copies
     // lane (c, r4) of block (m, j) holds column c of rows m*32 + r4*4 + {0..3} + 8q
     if (S == 1) {
