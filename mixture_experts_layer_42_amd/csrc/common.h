@@ -4,6 +4,7 @@
 #include <stdint.h>
 
 #define MOE_DEV __device__ __forceinline__
+#define MOE_HD __host__ __device__ __forceinline__
 
 typedef uint16_t bf16_t;   // bfloat16 storage
 

@@ -60,6 +60,7 @@ constexpr int kSkinnyRows = 64;       // groups of at most this many rows take t
 size_t skinny_partial_bytes(const GemmArgs &a, bool gate_up);
 
 int router_epad(int E);   // experts padded for the matrix-core router (bf16 x)
+size_t router_w3_bytes(int dtype, int d, int E);   // bf16 W_r parts the router needs
 hipError_t launch_router(int dtype, const void *x, const float *w, const float *bias,
                          float *logits, int T, int d, int E, uint16_t *w3, hipStream_t st);
 hipError_t launch_topk(const float *logits, int T, int E, int k, int kden, int renorm,

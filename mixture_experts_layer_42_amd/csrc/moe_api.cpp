@@ -92,7 +92,7 @@ Layout make_layout(const moe_problem &p) {
   L.tok_blk = take(nblk * 4);
   L.tok_blk_off = take(nblk * 4);
   L.stats_part = take(nblk * E * 4);
-  L.w3 = take(p.dtype == MOE_BF16 && p.E > 8 ? 3 * (size_t)router_epad(p.E) * d * 2 : 0);
+  L.w3 = take(router_w3_bytes(p.dtype == MOE_BF16 ? 1 : 0, (int)d, (int)E));
   L.partials = take(p.dtype == MOE_BF16 ? partial_bytes(p) : 0);
   L.logits = take(T * E * 4);
   L.ids = take(T * S * 4);

@@ -230,7 +230,12 @@ __global__ __launch_bounds__(256) void router_wide_kernel(const XT *__restrict__
 // gives float32-accurate logits at MFMA rate. The parts are stored transposed, [3][E_pad][d],
 // so both MFMA operands stream along d like the expert GEMMs.
 typedef __bf16 rbf16x8_t __attribute__((ext_vector_type(8)));
-typedef float rf32x16_t __attribute__((ext_vector_type(16)));
+
+// Row stride (elements) of the stored W parts: d plus 32, so that the 64-byte pieces the
+// MFMA fragment loads take from 16 rows at one K offset do not all fall on the same L2
+// channel (measured: +64 B per row runs the wide router 1.3x faster than a 4 KB or 8 KB
+// stride; +128 B and +256 B do not help).
+MOE_HD int router_w3_ld(int d) { return d + 32; }
 
 __global__ __launch_bounds__(256) void router_split_kernel(const float *__restrict__ w, int d,
                                                            int E, int E_pad,
@@ -243,105 +248,256 @@ __global__ __launch_bounds__(256) void router_split_kernel(const float *__restri
     const float r1 = v - bf16_to_f32(hi);
     const bf16_t mid = f32_to_bf16(r1);
     const bf16_t lo = f32_to_bf16(r1 - bf16_to_f32(mid));
-    w3[i] = hi;
-    w3[n + i] = mid;
-    w3[2 * n + i] = lo;
+    const size_t o = (size_t)e * router_w3_ld(d) + j, pl = (size_t)E_pad * router_w3_ld(d);
+    w3[o] = hi;
+    w3[pl + o] = mid;
+    w3[2 * pl + o] = lo;
   }
 }
 
-// WG = 4 waves; WE waves along experts (NB blocks of 32 experts each), 4/WE along tokens
-// (32 tokens each). K steps of 64: the three W parts for the WG's experts go straight from
-// global memory into a two-stage LDS buffer (rows of 128 B, 16-byte chunks XOR-swizzled by
-// row/2; lane L of a 1 KB copy fetches the chunk that lands at byte 16 L), the next stage
-// loading while the current one feeds the MFMAs; x fragments come straight from global
-// memory one chunk ahead (each x row is read once).
+// Wide router (E > 10). A workgroup of 8 waves takes 64 tokens x 128 experts (grid.y walks
+// groups of 128 experts); the 64 x 64 slice of x for each K step of 64 goes global -> LDS
+// (gfx950 global_load_lds, a three-stage ring, rows of 128 B with 16-byte chunks XOR-swizzled
+// by row/2), and wave w streams the W parts of expert block w (16 experts) straight from
+// global memory (L2) into a three-slice register ring, two K steps ahead. A wave owns all
+// three parts of its experts, so hi, mid and lo sums meet in its registers:
+// v_mfma_f32_16x16x32_bf16 over 4 token blocks x 3 parts per K half.
 typedef __attribute__((address_space(3))) void rlds_void_t;
 typedef __attribute__((address_space(1))) const void rgbl_void_t;
+typedef float rf32x4_t __attribute__((ext_vector_type(4)));
 
-template <int WE, int NB>
-__global__ __launch_bounds__(256) void router_mfma_kernel(const bf16_t *__restrict__ x,
-                                                          const bf16_t *__restrict__ w3,
-                                                          const float *__restrict__ bias,
-                                                          float *__restrict__ logits, int T,
-                                                          int d, int E, int E_pad) {
-  constexpr int EPW = WE * NB * 32;           // experts per workgroup
-  constexpr int TPW = (4 / WE) * 32;          // tokens per workgroup
-  constexpr int ROWS = 3 * EPW;               // LDS rows per K chunk (128 B each)
-  constexpr int COPIES = ROWS / 8 / 4;        // 1 KB copies per wave per chunk
-  __shared__ __attribute__((aligned(16))) char wl0[ROWS * 128];
-  __shared__ __attribute__((aligned(16))) char wl1[ROWS * 128];
+MOE_DEV int rswz(int row, int chunk) { return row * 128 + ((chunk ^ ((row >> 1) & 7)) << 4); }
+
+struct XStage { char b[64 * 128]; };
+
+__global__ __launch_bounds__(512) void router_mfma_kernel(const bf16_t *__restrict__ x,
+                                                             const bf16_t *__restrict__ w3,
+                                                             const float *__restrict__ bias,
+                                                             float *__restrict__ logits, int T,
+                                                             int d, int E, int E_pad) {
+  __shared__ XStage xs0, xs1, xs2;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int wvu = __builtin_amdgcn_readfirstlane(wv);
-  const int we = wv % WE, wt = wv / WE;
-  const int t0 = blockIdx.x * TPW + wt * 32, e0 = blockIdx.y * EPW;
-  const size_t plane = (size_t)E_pad * d;
-  auto swz = [](int row, int chunk) { return row * 128 + ((chunk ^ ((row >> 1) & 7)) << 4); };
-  uint32_t woff[COPIES];   // per-lane element offsets of this wave's copies
-#pragma unroll
-  for (int i = 0; i < COPIES; ++i) {
-    const int row = (wvu * COPIES + i) * 8 + (lane >> 3);
-    const int c = (lane & 7) ^ ((row >> 1) & 7);
-    const int part = row / EPW, e = e0 + row % EPW;
-    woff[i] = (uint32_t)(part * plane + (size_t)e * d + c * 8);
-  }
-  auto stage = [&](char *buf, int k0) {
-#pragma unroll
-    for (int i = 0; i < COPIES; ++i)
-      __builtin_amdgcn_global_load_lds((rgbl_void_t *)(w3 + woff[i] + k0),
-                                       (rlds_void_t *)(buf + (wvu * COPIES + i) * 1024), 16, 0, 0);
-  };
-  rf32x16_t acc[NB];
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-    for (int v = 0; v < 16; ++v) acc[nb][v] = 0.f;
-  const int tl = min(t0 + (lane & 31), T - 1);
-  const bf16_t *xr = x + (size_t)tl * d + 8 * (lane >> 5);
+  const int t0 = blockIdx.x * 64;
+  const int eg = blockIdx.y * 128;                   // first expert of the workgroup
+  const int neb_all = (min(E_pad - eg, 128)) / 16;   // expert blocks of the workgroup
+  constexpr int NEB = 1;
+  const int eb0 = wvu;                               // this wave's expert block
+  const int ldw = router_w3_ld(d);
+  const size_t plane = (size_t)E_pad * ldw;
   const int nk = d / 64;
-  rbf16x8_t a[4], an[4];
-  auto load_x = [&](rbf16x8_t (&dst)[4], int kc) {
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) dst[ks] = *reinterpret_cast<const rbf16x8_t *>(xr + kc * 64 + ks * 16);
+  // x copies: wave wv fills rows wv*8 .. +7 of a stage with one 1 KB copy
+  const int xrow = wvu * 8 + (lane >> 3);
+  const uint32_t xoff = (uint32_t)(min(t0 + xrow, T - 1)) * (uint32_t)d +
+                        (((lane & 7) ^ ((xrow >> 1) & 7)) * 8);   // elements
+  auto copy_x = [&](XStage &st, int kc) {
+    __builtin_amdgcn_global_load_lds((rgbl_void_t *)(x + xoff + kc * 64),
+                                     (rlds_void_t *)(st.b + wvu * 1024), 16, 0, 0);
   };
-  auto compute = [&](const char *buf) {
+  // W fragments: block (eb, part), K half kh: lane l reads row e = l%16 of the block,
+  // columns kc*64 + 32 kh + 8 (l/16) .. + 7. Idle waves (fewer expert blocks than waves)
+  // re-read the last block and store nothing.
+  const bool live = eb0 < neb_all;
+  const bf16_t *wrow[NEB][3];
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const int chunk = ks * 2 + (lane >> 5);
+  for (int j = 0; j < NEB; ++j)
 #pragma unroll
-      for (int part = 0; part < 3; ++part)
+    for (int p = 0; p < 3; ++p) {
+      const int e = eg + min(eb0 + j, neb_all - 1) * 16 + (lane & 15);
+      wrow[j][p] = w3 + p * plane + (size_t)e * ldw + 8 * (lane >> 4);
+    }
+  rbf16x8_t wb[3][NEB][3][2];   // ring of three K slices of W fragments
+  rf32x4_t acc[NEB][3][4];
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-          const int row = part * EPW + we * NB * 32 + nb * 32 + (lane & 31);
-          const rbf16x8_t b = *reinterpret_cast<const rbf16x8_t *>(buf + swz(row, chunk));
-          acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks], b, acc[nb], 0, 0, 0);
-        }
+  for (int j = 0; j < NEB; ++j)
+#pragma unroll
+    for (int p = 0; p < 3; ++p)
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb) acc[j][p][tb] = rf32x4_t{0.f, 0.f, 0.f, 0.f};
+  XStage *xs[3] = {&xs0, &xs1, &xs2};
+  auto load_w = [&](auto S, int kc) {
+#pragma unroll
+    for (int j = 0; j < NEB; ++j)
+#pragma unroll
+      for (int p = 0; p < 3; ++p)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          wb[S.value][j][p][h] = *reinterpret_cast<const rbf16x8_t *>(wrow[j][p] + kc * 64 + h * 32);
+  };
+  // Step kc (x slice kc in stage kc % 3, W slice kc in wb[kc % 3]): wait for this wave's
+  // copy of slice kc (issued two steps back, before the W loads and copy of slice kc+1:
+  // 6 NEB + 1 operations may stay in flight; the W loads of slice kc went out before its
+  // copies, so they have landed too), barrier (every wave's copies landed; every wave is
+  // done reading slice kc-1's stage), then the W loads and copies of slice kc+2 (past the
+  // end: the last slice again) into the ring entries slice kc-1 used, then the MFMAs.
+  constexpr int INFLIGHT = 6 * NEB + 1;
+  static_assert(INFLIGHT < 64, "vmcnt field");
+  auto step = [&](auto S, int kc) {
+    constexpr int s = decltype(S)::value, s2 = (s + 2) % 3;
+    __builtin_amdgcn_s_waitcnt((INFLIGHT & 15) | ((INFLIGHT >> 4) << 14) | (7 << 4));
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    load_w(std::integral_constant<int, s2>{}, min(kc + 2, nk - 1));
+    copy_x(*xs[s2], min(kc + 2, nk - 1));
+    __builtin_amdgcn_sched_barrier(0);   // the prefetch goes out before the MFMAs
+    const XStage &cur = *xs[s];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      rbf16x8_t a[4];
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb)
+        a[tb] = *reinterpret_cast<const rbf16x8_t *>(cur.b + rswz(tb * 16 + (lane & 15), 4 * h + (lane >> 4)));
+#pragma unroll
+      for (int j = 0; j < NEB; ++j)
+#pragma unroll
+        for (int p = 0; p < 3; ++p)
+#pragma unroll
+          for (int tb = 0; tb < 4; ++tb)
+            acc[j][p][tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[tb], wb[s][j][p][h], acc[j][p][tb], 0, 0, 0);
     }
   };
-  stage(wl0, 0);
-  load_x(a, 0);
-  for (int kc = 0; kc < nk; kc += 2) {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    if (kc + 1 < nk) { stage(wl1, (kc + 1) * 64); load_x(an, kc + 1); }
-    compute(wl0);
-    if (kc + 1 >= nk) break;
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) a[ks] = an[ks];
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    if (kc + 2 < nk) { stage(wl0, (kc + 2) * 64); load_x(an, kc + 2); }
-    compute(wl1);
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) a[ks] = an[ks];
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  // prologue in the order the steps assume: slice 0 (W, x), then slice 1
+  load_w(I0{}, 0);
+  copy_x(xs0, 0);
+  __builtin_amdgcn_sched_barrier(0);
+  load_w(I1{}, min(1, nk - 1));
+  copy_x(xs1, min(1, nk - 1));
+  __builtin_amdgcn_sched_barrier(0);
+  int kc = 0;
+  for (; kc + 3 <= nk; kc += 3) {
+    step(I0{}, kc);
+    step(I1{}, kc + 1);
+    step(I2{}, kc + 2);
   }
+  if (kc < nk) step(I0{}, kc);
+  if (kc + 1 < nk) step(I1{}, kc + 1);
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // the surplus loads and copies of the last steps
+  if (!live) return;
+  // lane l holds tokens 4*(l/16) + i of each block of 16, expert l%16 of each block
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    const int e = e0 + we * NB * 32 + nb * 32 + (lane & 31);
+  for (int j = 0; j < NEB; ++j) {
+    const int e = eg + (eb0 + j) * 16 + (lane & 15);
+    if (eb0 + j >= neb_all || e >= E) continue;
+    const float b = bias ? bias[e] : 0.f;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int t = t0 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-      if (t < T && e < E) logits[(size_t)t * E + e] = acc[nb][i] + (bias ? bias[e] : 0.f);
+    for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = t0 + tb * 16 + 4 * (lane >> 4) + i;
+        if (t < T) logits[(size_t)t * E + e] = ((acc[j][0][tb][i] + acc[j][1][tb][i]) + acc[j][2][tb][i]) + b;
+      }
+  }
+}
+
+// ----------------------------------------------------------------------------------------
+// Router, bf16 x and E <= 10, on the matrix cores. The three bf16 parts of W_r are 3E rows
+// of one [32][d] bf16 operand (row p*E + e holds part p of W_r[:, e]; rows 3E..31 are zero),
+// built by router_split_narrow_kernel. A workgroup of 8 waves takes 16 tokens; wave w sums the
+// 64-column units u = w, w+8, ... of d with v_mfma_f32_16x16x32_bf16 (A: 16 token rows of x,
+// B: 2 blocks of 16 W rows), four units' loads in flight. The 8 partial 16 x 32 tiles are
+// added in wave order in LDS, then each logit is (hi + mid) + lo + bias.
+constexpr int kNarrowRows = 32;
+
+__global__ __launch_bounds__(256) void router_split_narrow_kernel(const float *__restrict__ w,
+                                                                  int d, int E,
+                                                                  bf16_t *__restrict__ w3n) {
+  const size_t n = (size_t)kNarrowRows * d;
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) {
+    const int row = (int)(i / d), j = (int)(i % d);
+    const int part = row / E, e = row % E;
+    bf16_t out = 0;
+    if (part < 3) {
+      const float v = w[(size_t)j * E + e];
+      const bf16_t hi = f32_to_bf16(v);
+      const float r1 = v - bf16_to_f32(hi);
+      const bf16_t mid = f32_to_bf16(r1);
+      out = part == 0 ? hi : part == 1 ? mid : f32_to_bf16(r1 - bf16_to_f32(mid));
     }
+    w3n[(size_t)row * router_w3_ld(d) + j] = out;
+  }
+}
+
+template <int TB>
+__global__ __launch_bounds__(512) void router_mfma_narrow_kernel(const bf16_t *__restrict__ x,
+                                                                 const bf16_t *__restrict__ w3n,
+                                                                 const float *__restrict__ bias,
+                                                                 float *__restrict__ logits,
+                                                                 int T, int d, int E) {
+  constexpr int U = 4;          // 64-column units per wave in flight
+  constexpr int TT = 16 * TB;   // tokens per workgroup
+  __shared__ float part[8][TT * kNarrowRows];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int t0 = blockIdx.x * TT;
+  const int kq = 8 * (lane >> 4);   // this lane's 8 columns inside a 32-column MFMA step
+  const int ldw = router_w3_ld(d);
+  const bf16_t *xr[TB];
+#pragma unroll
+  for (int b = 0; b < TB; ++b) xr[b] = x + (size_t)min(t0 + 16 * b + (lane & 15), T - 1) * d + kq;
+  const bf16_t *b0 = w3n + (size_t)(lane & 15) * ldw + kq;
+  const bf16_t *b1 = w3n + (size_t)(16 + (lane & 15)) * ldw + kq;
+  const bool q_live = 16 + (lane & 15) < 3 * E;   // rows past the three parts are zero
+  rf32x4_t acc0[TB], acc1[TB];
+#pragma unroll
+  for (int b = 0; b < TB; ++b) acc0[b] = acc1[b] = rf32x4_t{0.f, 0.f, 0.f, 0.f};
+  const int nu = d / 64;
+  for (int ub = wv; ub < nu; ub += 8 * U) {
+    rbf16x8_t a[U][TB][2], p[U][2], q[U][2];
+#pragma unroll
+    for (int v = 0; v < U; ++v) {
+      const int u = min(ub + 8 * v, nu - 1);   // past the end: reloaded, not used
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const size_t o = (size_t)u * 64 + h * 32;
+#pragma unroll
+        for (int b = 0; b < TB; ++b) a[v][b][h] = *reinterpret_cast<const rbf16x8_t *>(xr[b] + o);
+        p[v][h] = *reinterpret_cast<const rbf16x8_t *>(b0 + o);
+        q[v][h] = q_live ? *reinterpret_cast<const rbf16x8_t *>(b1 + o) : rbf16x8_t{};
+      }
+    }
+#pragma unroll
+    for (int v = 0; v < U; ++v) {
+      if (ub + 8 * v < nu) {   // wave-uniform
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int b = 0; b < TB; ++b) {
+            acc0[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[v][b][h], p[v][h], acc0[b], 0, 0, 0);
+            acc1[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[v][b][h], q[v][h], acc1[b], 0, 0, 0);
+          }
+      }
+    }
+  }
+  // lane l holds rows 4*(l/16) + i, column l%16 of each 16 x 16 block
+#pragma unroll
+  for (int b = 0; b < TB; ++b)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 16 * b + 4 * (lane >> 4) + i;
+      part[wv][r * kNarrowRows + (lane & 15)] = acc0[b][i];
+      part[wv][r * kNarrowRows + 16 + (lane & 15)] = acc1[b][i];
+    }
+  __syncthreads();
+  float sum[TB];
+#pragma unroll
+  for (int b = 0; b < TB; ++b) {
+    const int idx = b * 512 + threadIdx.x;   // token * 32 + row
+    sum[b] = part[0][idx];
+#pragma unroll
+    for (int q = 1; q < 8; ++q) sum[b] += part[q][idx];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int b = 0; b < TB; ++b) part[0][b * 512 + threadIdx.x] = sum[b];
+  __syncthreads();
+  for (int i = threadIdx.x; i < TT * E; i += 512) {
+    const int r = i / E, e = i % E, t = t0 + r;
+    const float *sr = &part[0][r * kNarrowRows];
+    if (t < T) logits[(size_t)t * E + e] = ((sr[e] + sr[E + e]) + sr[2 * E + e]) + (bias ? bias[e] : 0.f);
   }
 }
 
@@ -949,26 +1105,41 @@ __global__ __launch_bounds__(1024) void stats_final_kernel(const float *__restri
 
 int router_epad(int E) { return E <= 32 ? 32 : E <= 64 ? 64 : ((E + 127) / 128) * 128; }
 
+bool router_narrow_mfma(int dtype, int d, int E) {
+  return dtype == 1 && 3 * E <= kNarrowRows && d % 64 == 0;
+}
+
+size_t router_w3_bytes(int dtype, int d, int E) {
+  if (router_narrow_mfma(dtype, d, E)) return (size_t)kNarrowRows * router_w3_ld(d) * 2;
+  if (dtype == 1 && E > 8 && d % 64 == 0) return 3 * (size_t)router_epad(E) * router_w3_ld(d) * 2;
+  return 0;
+}
+
 hipError_t launch_router(int dtype, const void *x, const float *w, const float *bias,
                          float *logits, int T, int d, int E, bf16_t *w3, hipStream_t st) {
-  if (dtype == 1 && E > 8) {
-    // bf16 activations, wide router: three-part split of W_r on the matrix cores (E <= 8
-    // stays on the narrow kernel below, whose one-token-row-per-lane-group streaming keeps
-    // every CU busy at small T)
+  if (router_narrow_mfma(dtype, d, E)) {
+    const size_t n = (size_t)kNarrowRows * d;
+    int g = (int)((n + 255) / 256);
+    if (g > 1024) g = 1024;
+    hipLaunchKernelGGL(router_split_narrow_kernel, dim3(g), dim3(256), 0, st, w, d, E, w3);
+    if (T >= 16 * 2 * 256)   // two token blocks per workgroup halve the W-part reads
+      hipLaunchKernelGGL(router_mfma_narrow_kernel<2>, dim3((T + 31) / 32), dim3(512), 0, st,
+                         (const bf16_t *)x, w3, bias, logits, T, d, E);
+    else
+      hipLaunchKernelGGL(router_mfma_narrow_kernel<1>, dim3((T + 15) / 16), dim3(512), 0, st,
+                         (const bf16_t *)x, w3, bias, logits, T, d, E);
+    return hipGetLastError();
+  }
+  if (dtype == 1 && E > 8 && d % 64 == 0) {
+    // bf16 activations, wide router: three-part split of W_r on the matrix cores
     const int E_pad = router_epad(E);
     const size_t n = (size_t)E_pad * d;
     int g = (int)((n + 255) / 256);
     if (g > 2048) g = 2048;
     hipLaunchKernelGGL(router_split_kernel, dim3(g), dim3(256), 0, st, w, d, E, E_pad, w3);
-    if (E_pad == 32)
-      hipLaunchKernelGGL((router_mfma_kernel<1, 1>), dim3((T + 127) / 128, 1), dim3(256), 0, st,
-                         (const bf16_t *)x, w3, bias, logits, T, d, E, E_pad);
-    else if (E_pad == 64)
-      hipLaunchKernelGGL((router_mfma_kernel<1, 2>), dim3((T + 127) / 128, 1), dim3(256), 0, st,
-                         (const bf16_t *)x, w3, bias, logits, T, d, E, E_pad);
-    else
-      hipLaunchKernelGGL((router_mfma_kernel<2, 2>), dim3((T + 63) / 64, E_pad / 128), dim3(256),
-                         0, st, (const bf16_t *)x, w3, bias, logits, T, d, E, E_pad);
+    const dim3 grid((T + 63) / 64, (E_pad + 127) / 128);
+    hipLaunchKernelGGL(router_mfma_kernel, grid, dim3(512), 0, st, (const bf16_t *)x, w3, bias,
+                       logits, T, d, E, E_pad);
     return hipGetLastError();
   }
   if (E <= 8) {
