@@ -31,6 +31,13 @@
  *    Expert outputs o_perm and o_shared, router weights, logits and all
  *    gates/weights are float32 (the expert outputs stay unrounded until the
  *    combine, which rounds once into y).
+ *  - Inputs must be finite; the hot path does not look for NaN or infinity. Debug mode
+ *    (environment variable MOE_DEBUG set to anything but "" or "0", read at every call):
+ *    each entry point first scans its floating-point inputs on the device (activations,
+ *    router weights and bias or given logits, expert weights, expert outputs and combine
+ *    weights for moe_combine), synchronises `stream`, and returns MOE_ERR_INVALID_ARG with
+ *    nothing further enqueued if any value is NaN or infinite. The scan uses one flag in
+ *    device memory per GPU, so debug-mode calls on one GPU must not overlap.
  *  - Row capacity R = T*k rows suffices for every selection form; buffers sized
  *    "[R, ...]" are indexed by dispatched row.
  *  - Errors: arguments are checked on the host BEFORE anything is enqueued; on

@@ -26,6 +26,7 @@ UNITS = {
     "gemm.hip": [],
     "move.hip": [],
     "moe_api.cpp": [],
+    "debug.hip": [],
 }
 
 

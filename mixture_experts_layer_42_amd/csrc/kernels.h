@@ -59,6 +59,18 @@ constexpr int kSkinnyRows = 64;       // groups of at most this many rows take t
 // float32 partial-sum bytes the skinny path needs for a GEMM (0 if it does not apply)
 size_t skinny_partial_bytes(const GemmArgs &a, bool gate_up);
 
+// Debug-mode input checks (environment MOE_DEBUG set and not "0").
+struct DebugSpan {
+  const void *p;               // device data (null: skipped)
+  size_t n;                    // elements, unless n_rows_dev is given
+  int elt;                     // 2: bf16, 4: float32
+  const int32_t *n_rows_dev;   // optional device row count; elements = rows * row_elems
+  int row_elems;
+};
+bool debug_checks_enabled();
+// enqueue the checks on st, synchronise st; found = some element is NaN or infinite
+hipError_t debug_any_nonfinite(const DebugSpan *spans, int n_spans, hipStream_t st, bool *found);
+
 int router_epad(int E);   // experts padded for the matrix-core router (bf16 x)
 size_t router_w3_bytes(int dtype, int d, int E);   // bf16 W_r parts the router needs
 hipError_t launch_router(int dtype, const void *x, const float *w, const float *bias,

@@ -4,6 +4,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <initializer_list>
 #include <mutex>
 
 #include "../../include/moe.h"
@@ -333,6 +334,33 @@ hipError_t do_combine(const moe_problem &p, const void *o_perm, const void *o_sh
                         r.tok_pos, r.perm_w, y, p.T, p.d_model, st);
 }
 
+// Debug mode (MOE_DEBUG): scan the floating-point inputs for NaN/Inf before anything else
+// is enqueued; a non-finite value is an invalid argument.
+moe_status debug_check(std::initializer_list<DebugSpan> spans, hipStream_t st) {
+  if (!debug_checks_enabled()) return MOE_OK;
+  bool bad = false;
+  if (debug_any_nonfinite(spans.begin(), (int)spans.size(), st, &bad) != hipSuccess)
+    return MOE_ERR_HIP;
+  return bad ? MOE_ERR_INVALID_ARG : MOE_OK;
+}
+
+size_t nz(size_t a, size_t b, size_t c = 1) { return a * b * c; }
+
+moe_status debug_check_weights(const moe_problem &p, const void *w_gate, const void *w_up,
+                               const void *w_down, const void *x, const void *ws_gate,
+                               const void *ws_up, const void *ws_down, hipStream_t st) {
+  const int elt = elt_of(p);
+  const size_t dff = p.d_ff, d = p.d_model, dfs = p.d_ff_shared;
+  return debug_check({{w_gate, nz(p.E, dff, d), elt, nullptr, 0},
+                      {w_up, nz(p.E, dff, d), elt, nullptr, 0},
+                      {w_down, nz(p.E, d, dff), elt, nullptr, 0},
+                      {dfs ? x : nullptr, nz(p.T, d), elt, nullptr, 0},
+                      {dfs ? ws_gate : nullptr, nz(dfs, d), elt, nullptr, 0},
+                      {dfs ? ws_up : nullptr, nz(dfs, d), elt, nullptr, 0},
+                      {dfs ? ws_down : nullptr, nz(d, dfs), elt, nullptr, 0}},
+                     st);
+}
+
 moe_status layer_forward(const moe_problem *pp, const void *x, const float *w_router,
                          const float *bias, const void *w_gate, const void *w_up,
                          const void *w_down, const void *ws_gate, const void *ws_up,
@@ -351,6 +379,13 @@ moe_status layer_forward(const moe_problem *pp, const void *x, const float *w_ro
   const Layout L = make_layout(p);
   moe_routing r = routing ? *routing : internal_routing(L, w);
   if (routing && (s = check_routing_out(p, routing)) != MOE_OK) return s;
+  if ((s = debug_check({{x, nz(p.T, p.d_model), elt_of(p), nullptr, 0},
+                        {w_router, nz(p.d_model, p.E), 4, nullptr, 0},
+                        {bias, (size_t)p.E, 4, nullptr, 0}},
+                       st)) != MOE_OK)
+    return s;
+  if ((s = debug_check_weights(p, w_gate, w_up, w_down, x, ws_gate, ws_up, ws_down, st)) != MOE_OK)
+    return s;
   if (ensure_attributes() != hipSuccess) return MOE_ERR_HIP;
   auto mark = [&](int i) { return ev ? hipEventRecord(ev[i], st) : hipSuccess; };
   MOE_TRY(mark(MOE_STAGE_ROUTE));
@@ -389,6 +424,14 @@ moe_status moe_route(const moe_problem *problem, const void *x, const float *w_r
     return MOE_ERR_INVALID_ARG;
   if ((s = check_routing_out(p, routing)) != MOE_OK) return s;
   if ((s = check_ws(p, ws, ws_bytes)) != MOE_OK) return s;
+  if (flags & MOE_ROUTE_LOGITS_IN)
+    s = debug_check({{routing->logits, nz(p.T, p.E), 4, nullptr, 0}}, stream);
+  else
+    s = debug_check({{x, nz(p.T, p.d_model), elt_of(p), nullptr, 0},
+                     {w_router, nz(p.d_model, p.E), 4, nullptr, 0},
+                     {bias, (size_t)p.E, 4, nullptr, 0}},
+                    stream);
+  if (s != MOE_OK) return s;
   if (do_route(p, x, w_router, bias, flags, *routing, (char *)ws, stream) != hipSuccess)
     return MOE_ERR_HIP;
   return MOE_OK;
@@ -401,6 +444,9 @@ moe_status moe_dispatch(const moe_problem *problem, const void *x, const moe_rou
   if (!ptr_ok(x) || !ptr_ok(x_perm) || !routing || !ptr_ok(routing->perm_token) ||
       !ptr_ok(routing->offsets))
     return MOE_ERR_INVALID_ARG;
+  if ((s = debug_check({{x, nz(problem->T, problem->d_model), elt_of(*problem), nullptr, 0}},
+                       stream)) != MOE_OK)
+    return s;
   if (do_dispatch(*problem, x, *routing, x_perm, stream) != hipSuccess) return MOE_ERR_HIP;
   return MOE_OK;
 }
@@ -420,6 +466,12 @@ moe_status moe_expert_ffn(const moe_problem *problem, const void *x_perm,
                             !ptr_ok(ws_down) || !ptr_ok(o_shared)))
     return MOE_ERR_INVALID_ARG;
   if ((s = check_ws(p, ws, ws_bytes)) != MOE_OK) return s;
+  if ((s = debug_check({{x_perm, 0, elt_of(p), routing->offsets + p.E, p.d_model}}, stream)) !=
+      MOE_OK)
+    return s;
+  if ((s = debug_check_weights(p, w_gate, w_up, w_down, x, ws_gate, ws_up, ws_down, stream)) !=
+      MOE_OK)
+    return s;
   if (ensure_attributes() != hipSuccess) return MOE_ERR_HIP;
   char *w = (char *)ws;
   if (do_gate_up(p, x_perm, *routing, w_gate, w_up, x, ws_gate, ws_up, w, stream) != hipSuccess)
@@ -438,6 +490,11 @@ moe_status moe_combine(const moe_problem *problem, const void *o_perm, const voi
       !ptr_ok(routing->tok_pos) || !ptr_ok(routing->perm_w))
     return MOE_ERR_INVALID_ARG;
   if (p.d_ff_shared > 0 && !ptr_ok(o_shared)) return MOE_ERR_INVALID_ARG;
+  if ((s = debug_check({{o_perm, 0, 4, routing->tok_ptr + p.T, p.d_model},
+                        {routing->perm_w, 0, 4, routing->tok_ptr + p.T, 1},
+                        {p.d_ff_shared > 0 ? o_shared : nullptr, nz(p.T, p.d_model), 4, nullptr, 0}},
+                       stream)) != MOE_OK)
+    return s;
   if (do_combine(p, o_perm, o_shared, *routing, y, stream) != hipSuccess) return MOE_ERR_HIP;
   return MOE_OK;
 }
@@ -473,6 +530,8 @@ moe_status moe_routing_stats(const moe_problem *problem, const moe_routing *rout
       !ptr_ok(routing->offsets) || !ptr_ok(out))
     return MOE_ERR_INVALID_ARG;
   if ((s = check_ws(p, ws, ws_bytes)) != MOE_OK) return s;
+  if ((s = debug_check({{routing->logits, nz(p.T, p.E), 4, nullptr, 0}}, stream)) != MOE_OK)
+    return s;
   const Layout L = make_layout(p);
   if (launch_stats(routing->logits, routing->counts, routing->offsets, p.T, p.E, p.k,
                    p.routing == MOE_TOKEN_CHOICE ? 1 : 0,
