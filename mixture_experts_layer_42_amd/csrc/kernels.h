@@ -73,14 +73,25 @@ hipError_t debug_any_nonfinite(const DebugSpan *spans, int n_spans, hipStream_t 
 
 int router_epad(int E);   // experts padded for the matrix-core router (bf16 x)
 size_t router_w3_bytes(int dtype, int d, int E);   // bf16 W_r parts the router needs
+// token-choice top-k outputs a router may produce alongside the logits (launch_topk's
+// arguments: k picks, renormalisation over the first kden, routing keys when want_key)
+struct TopkOut {
+  int k, kden, renorm, want_key;
+  int32_t *ids;
+  float *gates, *keys;
+};
+// logits = x W_r + b; with topk non-null, the router may also run the top-k of every token
+// (same results as launch_topk) and then sets *topk_done
 hipError_t launch_router(int dtype, const void *x, const float *w, const float *bias,
-                         float *logits, int T, int d, int E, uint16_t *w3, hipStream_t st);
+                         float *logits, int T, int d, int E, uint16_t *w3, hipStream_t st,
+                         const TopkOut *topk = nullptr, bool *topk_done = nullptr);
 hipError_t launch_topk(const float *logits, int T, int E, int k, int kden, int renorm,
                        int want_key, int32_t *ids, float *gates, float *keys, hipStream_t st);
+// with C < 0 (no capacity) and tok_ptr/tok_pos non-null the token -> rows CSR is written too
 hipError_t launch_token_dispatch(const RouteScratch &s, const int32_t *ids, const float *gates,
                                  int T, int k, int E, int C, int32_t *perm_token, float *perm_w,
                                  uint8_t *kept, int32_t *counts, int32_t *offsets,
-                                 hipStream_t st);
+                                 int32_t *tok_ptr, int32_t *tok_pos, hipStream_t st);
 hipError_t launch_group_capacity(const RouteScratch &s, const int32_t *ids, const float *gates,
                                  int T, int k, int E, int D, int C_D, int32_t *perm_token,
                                  float *perm_w, uint8_t *kept, int32_t *counts, int32_t *offsets,

@@ -255,15 +255,19 @@ hipError_t do_route(const moe_problem &p, const void *x, const float *w_router,
   const Layout L = make_layout(p);
   const RouteScratch s = scratch_of(L, ws);
   hipError_t e;
+  const int C = capacity_of(p);
+  const TopkOut tk{p.k + p.expand_m, p.k, p.renorm_topk, C >= 0 ? 1 : 0, r.topk_ids, r.topk_w,
+                   s.keys};
+  bool topk_done = false;
   if (!(flags & MOE_ROUTE_LOGITS_IN)) {
     e = launch_router(p.dtype == MOE_BF16 ? 1 : 0, x, w_router, bias, r.logits, p.T, p.d_model,
-                      p.E, s.w3, st);
+                      p.E, s.w3, st, p.routing == MOE_TOKEN_CHOICE ? &tk : nullptr, &topk_done);
     if (e != hipSuccess) return e;
   }
   if (p.routing == MOE_TOKEN_CHOICE) {
-    const int C = capacity_of(p);
-    e = launch_topk(r.logits, p.T, p.E, p.k + p.expand_m, p.k, p.renorm_topk, C >= 0 ? 1 : 0,
-                    r.topk_ids, r.topk_w, s.keys, st);
+    if (!topk_done)
+      e = launch_topk(r.logits, p.T, p.E, tk.k, tk.kden, tk.renorm, tk.want_key, r.topk_ids,
+                      r.topk_w, s.keys, st);
     if (e != hipSuccess) return e;
     if (p.cap_groups > 0)
       e = launch_group_capacity(s, r.topk_ids, r.topk_w, p.T, p.k, p.E, p.cap_groups,
@@ -272,9 +276,13 @@ hipError_t do_route(const moe_problem &p, const void *x, const float *w_router,
     else if (p.expand_m > 0)
       e = launch_expanded_drop(s, r.topk_ids, r.topk_w, p.T, p.k, p.expand_m, p.E, C,
                                r.perm_token, r.perm_w, r.kept, r.counts, r.offsets, st);
+    else if (C < 0)   // every pair kept: the scatter writes the CSR as well
+      return launch_token_dispatch(s, r.topk_ids, r.topk_w, p.T, p.k, p.E, C, r.perm_token,
+                                   r.perm_w, r.kept, r.counts, r.offsets, r.tok_ptr, r.tok_pos,
+                                   st);
     else
       e = launch_token_dispatch(s, r.topk_ids, r.topk_w, p.T, p.k, p.E, C, r.perm_token,
-                                r.perm_w, r.kept, r.counts, r.offsets, st);
+                                r.perm_w, r.kept, r.counts, r.offsets, nullptr, nullptr, st);
     if (e != hipSuccess) return e;
   } else {
     const int c = (int)(((int64_t)p.k * p.T) / p.E);

@@ -422,12 +422,55 @@ __global__ __launch_bounds__(256) void router_split_narrow_kernel(const float *_
   }
 }
 
+// Token-choice top-k of one token whose E <= 16 logits sit in LDS, computed by one thread
+// with the arithmetic topk_kernel uses for the same E (a group of G = 8 or 16 lanes, one logit
+// per lane): picks by (logit desc, expert asc), gate numerators exp(l - max) over the first
+// pick's logit, the renormalisation mass of the first kden picks in pick order or the full
+// softmax sum in the butterfly order of G lanes, and the routing keys of the capacity forms.
+MOE_DEV void topk_one_token(const float *l, int E, int t, const TopkOut &o) {
+  const int G = E <= 8 ? 8 : 16;
+  uint32_t taken = 0u;
+  float mx = 0.f, qsum = 0.f, qn[16];
+  int pick[16];
+  for (int r = 0; r < o.k; ++r) {
+    float bv = -INFINITY;
+    int be = -1;
+    for (int e = 0; e < E; ++e)
+      if (!((taken >> e) & 1u) && (be < 0 || l[e] > bv)) { bv = l[e]; be = e; }
+    taken |= 1u << be;
+    if (r == 0) mx = bv;
+    qn[r] = expf(bv - mx);
+    pick[r] = be;
+    if (r < o.kden) qsum += qn[r];
+  }
+  float denom = qsum;
+  if (!o.renorm) {
+    float sv[16];
+    for (int g = 0; g < G; ++g) sv[g] = g < E ? expf(l[g] - mx) : 0.f;
+    for (int d = G / 2; d > 0; d >>= 1)
+      for (int g = 0; g < d; ++g) sv[g] = sv[g] + sv[g + d];   // lane 0 of the butterfly
+    denom = sv[0];
+  }
+  for (int r = 0; r < o.k; ++r) {
+    o.ids[(size_t)t * o.k + r] = pick[r];
+    o.gates[(size_t)t * o.k + r] = qn[r] / denom;
+  }
+  if (o.want_key) {
+    float q[16];
+    for (int e = 0; e < E; ++e) q[e] = rexp_spec(__fsub_rn(l[e], mx));
+    float S = q[0];
+    for (int e = 1; e < E; ++e) S = __fadd_rn(S, q[e]);
+    for (int r = 0; r < o.k; ++r) o.keys[(size_t)t * o.k + r] = q[pick[r]] / S;
+  }
+}
+
 template <int TB>
 __global__ __launch_bounds__(512) void router_mfma_narrow_kernel(const bf16_t *__restrict__ x,
                                                                  const bf16_t *__restrict__ w3n,
                                                                  const float *__restrict__ bias,
                                                                  float *__restrict__ logits,
-                                                                 int T, int d, int E) {
+                                                                 int T, int d, int E,
+                                                                 TopkOut topk) {
   constexpr int U = 4;          // 64-column units per wave in flight
   constexpr int TT = 16 * TB;   // tokens per workgroup
   __shared__ float part[8][TT * kNarrowRows];
@@ -494,11 +537,18 @@ __global__ __launch_bounds__(512) void router_mfma_narrow_kernel(const bf16_t *_
 #pragma unroll
   for (int b = 0; b < TB; ++b) part[0][b * 512 + threadIdx.x] = sum[b];
   __syncthreads();
+  float *lg = &part[1][0];   // [TT][E] final logits for the fused top-k
   for (int i = threadIdx.x; i < TT * E; i += 512) {
     const int r = i / E, e = i % E, t = t0 + r;
     const float *sr = &part[0][r * kNarrowRows];
-    if (t < T) logits[(size_t)t * E + e] = ((sr[e] + sr[E + e]) + sr[2 * E + e]) + (bias ? bias[e] : 0.f);
+    const float v = ((sr[e] + sr[E + e]) + sr[2 * E + e]) + (bias ? bias[e] : 0.f);
+    lg[i] = v;
+    if (t < T) logits[(size_t)t * E + e] = v;
   }
+  if (!topk.ids) return;   // block-uniform
+  __syncthreads();
+  if (threadIdx.x < TT && t0 + (int)threadIdx.x < T)
+    topk_one_token(lg + threadIdx.x * E, E, t0 + threadIdx.x, topk);
 }
 
 // ----------------------------------------------------------------------------------------
@@ -684,16 +734,23 @@ __global__ __launch_bounds__(1024) void assign_scan_kernel(const int32_t *__rest
 // Stable scatter: pair (t, j) of bucket b goes to off[b] + blk_base[blk][b] + (its rank in
 // the block). Candidate mode writes (token, slot, key) lists for cap_select; final mode
 // writes the dispatch arrays, and marks the slots in [j0, j1) that were not taken with -1.
+// When every slot of every token is kept (no capacity limit), final mode can also write the
+// token -> rows CSR directly (csr_ptr, csr_pos non-null): token t owns entries t*S .. t*S+S-1.
 __global__ __launch_bounds__(256) void assign_scatter_kernel(
     const int32_t *__restrict__ ids, const float *__restrict__ gates,
     const float *__restrict__ keys, int T, PairSel f, int B, const int32_t *__restrict__ off,
     const int32_t *__restrict__ blk_base, int candidates, int32_t *__restrict__ out_token,
     float *__restrict__ out_w, int32_t *__restrict__ out_slot, float *__restrict__ out_key,
-    int32_t *__restrict__ slot_pos, uint8_t *__restrict__ kept_out) {
+    int32_t *__restrict__ slot_pos, uint8_t *__restrict__ kept_out, int32_t *__restrict__ csr_ptr,
+    int32_t *__restrict__ csr_pos) {
   extern __shared__ uint32_t mask[];
   build_masks(mask, ids, f, T, B);
   const int t = blockIdx.x * 256 + threadIdx.x;
   if (t >= T) return;
+  if (csr_ptr) {   // every pair kept, in slot order: token t's rows are CSR entries t*S ..
+    csr_ptr[t] = t * f.S;
+    if (t == T - 1) csr_ptr[T] = T * f.S;
+  }
   const int word = threadIdx.x >> 5, bit = threadIdx.x & 31;
   int seen[kMaxSlots];
   int ns = 0;
@@ -726,6 +783,7 @@ __global__ __launch_bounds__(256) void assign_scatter_kernel(
       out_w[pos] = gates[ij];
       slot_pos[ij] = pos;
       if (kept_out) kept_out[ij] = 1;
+      if (csr_pos) csr_pos[ij] = pos;
     }
   }
 }
@@ -1116,18 +1174,22 @@ size_t router_w3_bytes(int dtype, int d, int E) {
 }
 
 hipError_t launch_router(int dtype, const void *x, const float *w, const float *bias,
-                         float *logits, int T, int d, int E, bf16_t *w3, hipStream_t st) {
+                         float *logits, int T, int d, int E, bf16_t *w3, hipStream_t st,
+                         const TopkOut *topk, bool *topk_done) {
+  if (topk_done) *topk_done = false;
   if (router_narrow_mfma(dtype, d, E)) {
+    const TopkOut tk = topk ? *topk : TopkOut{0, 0, 0, 0, nullptr, nullptr, nullptr};
+    if (topk && topk_done) *topk_done = true;
     const size_t n = (size_t)kNarrowRows * d;
     int g = (int)((n + 255) / 256);
     if (g > 1024) g = 1024;
     hipLaunchKernelGGL(router_split_narrow_kernel, dim3(g), dim3(256), 0, st, w, d, E, w3);
     if (T >= 16 * 2 * 256)   // two token blocks per workgroup halve the W-part reads
       hipLaunchKernelGGL(router_mfma_narrow_kernel<2>, dim3((T + 31) / 32), dim3(512), 0, st,
-                         (const bf16_t *)x, w3, bias, logits, T, d, E);
+                         (const bf16_t *)x, w3, bias, logits, T, d, E, tk);
     else
       hipLaunchKernelGGL(router_mfma_narrow_kernel<1>, dim3((T + 15) / 16), dim3(512), 0, st,
-                         (const bf16_t *)x, w3, bias, logits, T, d, E);
+                         (const bf16_t *)x, w3, bias, logits, T, d, E, tk);
     return hipGetLastError();
   }
   if (dtype == 1 && E > 8 && d % 64 == 0) {
@@ -1195,7 +1257,8 @@ namespace {
 // Final mode: counts/offsets and the dispatch arrays.
 void assign_pairs(const RouteScratch &s, const int32_t *ids, const float *gates, int T,
                   const PairSel &f, int B, bool candidates, int32_t *perm_token, float *perm_w,
-                  uint8_t *kept_out, int32_t *counts, int32_t *offsets, hipStream_t st) {
+                  uint8_t *kept_out, int32_t *counts, int32_t *offsets, hipStream_t st,
+                  int32_t *csr_ptr = nullptr, int32_t *csr_pos = nullptr) {
   const int nblk = (T + 255) / 256;
   const size_t msh = (size_t)B * f.mult * 8 * sizeof(uint32_t);
   hipLaunchKernelGGL(assign_count_kernel, dim3(nblk), dim3(256), msh, st, ids, T, f, B, s.blk_cnt);
@@ -1205,11 +1268,13 @@ void assign_pairs(const RouteScratch &s, const int32_t *ids, const float *gates,
   if (candidates)
     hipLaunchKernelGGL(assign_scatter_kernel, dim3(nblk), dim3(256), msh, st, ids, gates, s.keys,
                        T, f, B, off, s.blk_base, 1, s.cand_token, s.cand_w, s.cand_slot,
-                       s.cand_key, (int32_t *)nullptr, (uint8_t *)nullptr);
+                       s.cand_key, (int32_t *)nullptr, (uint8_t *)nullptr, (int32_t *)nullptr,
+                       (int32_t *)nullptr);
   else
     hipLaunchKernelGGL(assign_scatter_kernel, dim3(nblk), dim3(256), msh, st, ids, gates,
                        (const float *)nullptr, T, f, B, off, s.blk_base, 0, perm_token, perm_w,
-                       (int32_t *)nullptr, (float *)nullptr, s.slot_pos, kept_out);
+                       (int32_t *)nullptr, (float *)nullptr, s.slot_pos, kept_out, csr_ptr,
+                       csr_pos);
 }
 
 }  // namespace
@@ -1217,11 +1282,12 @@ void assign_pairs(const RouteScratch &s, const int32_t *ids, const float *gates,
 hipError_t launch_token_dispatch(const RouteScratch &s, const int32_t *ids, const float *gates,
                                  int T, int k, int E, int C, int32_t *perm_token, float *perm_w,
                                  uint8_t *kept, int32_t *counts, int32_t *offsets,
-                                 hipStream_t st) {
+                                 int32_t *tok_ptr, int32_t *tok_pos, hipStream_t st) {
   const int nblk = (T + 255) / 256;
   const PairSel all{nullptr, k, 0, k, 1, 1};
   if (C < 0) {
-    assign_pairs(s, ids, gates, T, all, E, false, perm_token, perm_w, kept, counts, offsets, st);
+    assign_pairs(s, ids, gates, T, all, E, false, perm_token, perm_w, kept, counts, offsets, st,
+                 tok_ptr, tok_pos);
     return hipGetLastError();
   }
   const size_t msh = (size_t)E * 8 * sizeof(uint32_t);
@@ -1231,7 +1297,8 @@ hipError_t launch_token_dispatch(const RouteScratch &s, const int32_t *ids, cons
                      s.blk_base, s.cnt_pre, s.off_pre, counts, offsets);
   hipLaunchKernelGGL(assign_scatter_kernel, dim3(nblk), dim3(256), msh, st, ids, gates, s.keys, T,
                      all, E, s.off_pre, s.blk_base, 1, s.cand_token, s.cand_w,
-                     s.cand_slot, s.cand_key, (int32_t *)nullptr, (uint8_t *)nullptr);
+                     s.cand_slot, s.cand_key, (int32_t *)nullptr, (uint8_t *)nullptr,
+                     (int32_t *)nullptr, (int32_t *)nullptr);
   hipLaunchKernelGGL(cap_select_kernel, dim3(E), dim3(1024), 0, st, s.cand_token, s.cand_slot,
                      s.cand_key, s.cand_w, s.cnt_pre, s.off_pre, offsets, C, (const int32_t *)nullptr, k,
                      perm_token, perm_w, s.slot_pos, kept);
@@ -1270,7 +1337,8 @@ hipError_t launch_expanded_drop(const RouteScratch &s, const int32_t *ids, const
                      s.blk_base, s.cnt_pre, s.off_pre, counts, offsets);
   hipLaunchKernelGGL(assign_scatter_kernel, dim3(nblk), dim3(256), msh, st, ids, gates, s.keys, T,
                      top, E, s.off_pre, s.blk_base, 1, s.cand_token, s.cand_w,
-                     s.cand_slot, s.cand_key, (int32_t *)nullptr, (uint8_t *)nullptr);
+                     s.cand_slot, s.cand_key, (int32_t *)nullptr, (uint8_t *)nullptr,
+                     (int32_t *)nullptr, (int32_t *)nullptr);
   hipLaunchKernelGGL(cap_select_kernel, dim3(E), dim3(1024), 0, st, s.cand_token, s.cand_slot,
                      s.cand_key, s.cand_w, s.cnt_pre, s.off_pre, s.off_pre, C, (const int32_t *)nullptr,
                      S, (int32_t *)nullptr, (float *)nullptr, (int32_t *)nullptr, kept);

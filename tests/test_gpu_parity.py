@@ -75,6 +75,8 @@ def _bits(a):
     if isinstance(a, torch.Tensor):
         a = a.contiguous()
         a = (a.view(torch.int16) if a.element_size() == 2 else a.view(torch.int32)).cpu().numpy()
+    if a.dtype.itemsize == 1:
+        return a.view(np.uint8)
     return a.view(np.uint16) if a.dtype.itemsize == 2 else a.view(np.uint32)
 
 
@@ -125,6 +127,36 @@ def test_selection_bit_exact(name):
     ro = oracle.route(cfg, logits=l)
     rb, _, _ = run_route(cfg, dev, logits_in=l)
     _compare_routing(cfg, rb, ro, exact_logits=l)
+
+
+# bf16 layers with E <= 10: the matrix-core router also runs the top-k of its tokens
+FUSED_TOPK = {
+    "ragged-bf16": SMALL["ragged-bf16"],
+    "expanded-drop-bf16": SMALL["expanded-drop-bf16"],
+    "no-renorm-bf16": C0.with_(dtype="bf16", k=3, renorm_topk=False, T=200, bias=("normal", 0.5)),
+    "E10-drop-bf16": C0.with_(dtype="bf16", T=333, d_model=192, E=10, k=3, d_ff=128, gamma=0.9,
+                              bias=("zipf", 1.2)),
+    "E9-nodrop-bf16": C0.with_(dtype="bf16", T=50, d_model=64, E=9, k=9, d_ff=64),
+}
+
+
+@pytest.mark.parametrize("name", list(FUSED_TOPK))
+def test_fused_topk_equals_topk_kernel(name):
+    """moe_route with the router computing logits (and, for these shapes, the top-k inside the
+    same kernel) against moe_route fed those very logits (the separate top-k kernel): every
+    routing array bit-identical; and the selection against the oracle on the same logits."""
+    cfg = FUSED_TOPK[name]
+    inp = inputs_for(cfg)
+    dev = dev_weights(inp)
+    ra, _, _ = run_route(cfg, dev)
+    ha = ra.host()
+    rb, _, _ = run_route(cfg, dev, logits_in=ha["logits"])
+    hb = rb.host()
+    ma, mb = _meaningful(cfg, ha), _meaningful(cfg, hb)
+    for key in ma:
+        assert (_bits(np.asarray(ma[key])) == _bits(np.asarray(mb[key]))).all(), key
+    ro = oracle.route(cfg, logits=ha["logits"])
+    _compare_routing(cfg, ra, ro, exact_logits=ha["logits"])
 
 
 TIE_CASES = [
