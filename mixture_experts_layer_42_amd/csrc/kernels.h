@@ -112,7 +112,7 @@ hipError_t launch_gather(int elt, const void *x, const int32_t *perm_token,
                          int num_cu, hipStream_t st);
 hipError_t launch_combine(int y_elt, const float *o, const float *o_shared,
                           const int32_t *tok_ptr, const int32_t *tok_pos, const float *perm_w,
-                          void *y, int T, int d, hipStream_t st);
+                          void *y, int T, int d, int max_rows, hipStream_t st);
 hipError_t launch_gemm(const GemmArgs &a, bool gate_up, int max_rows, int num_cu,
                        hipStream_t st);
 hipError_t gemm_setup_attributes();

@@ -339,7 +339,7 @@ hipError_t do_combine(const moe_problem &p, const void *o_perm, const void *o_sh
                       const moe_routing &r, void *y, hipStream_t st) {
   return launch_combine(p.y_dtype == MOE_BF16 ? 2 : 4, (const float *)o_perm,
                         p.d_ff_shared > 0 ? (const float *)o_shared : nullptr, r.tok_ptr,
-                        r.tok_pos, r.perm_w, y, p.T, p.d_model, st);
+                        r.tok_pos, r.perm_w, y, p.T, p.d_model, (int)rows_cap(p), st);
 }
 
 // Debug mode (MOE_DEBUG): scan the floating-point inputs for NaN/Inf before anything else

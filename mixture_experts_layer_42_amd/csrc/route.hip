@@ -636,6 +636,110 @@ __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ log
   }
 }
 
+// Token-choice top-k for 33..128 experts and k <= 8, by merging instead of k rounds of group
+// argmax. A group of 16 lanes handles one token, lane i holding experts i, i+16, ... (8 each).
+// Each lane sorts its 8 (logit, expert) pairs by (logit desc, expert asc) with a 19-comparator
+// network; then, for partner distance 8, 4, 2, 1, it takes the partner's sorted list, keeps
+// the better of A[i] and B[7-i] (a bitonic sequence holding the top 8 of both lists) and
+// sorts that with a 12-comparator bitonic merge. The order is total, so after four merges
+// every lane of the group holds the same sorted top 8: the picks in order. Gates and routing
+// keys follow topk_kernel's arithmetic exactly.
+struct KE { float v; int e; };
+MOE_DEV bool ke_before(const KE &a, const KE &b) { return a.v > b.v || (a.v == b.v && a.e < b.e); }
+MOE_DEV void ke_ce(KE &a, KE &b) {
+  const bool keep = ke_before(a, b);
+  const KE lo = keep ? b : a;
+  a = keep ? a : b;
+  b = lo;
+}
+
+__global__ __launch_bounds__(256) void topk_merge_kernel(const float *__restrict__ logits, int T,
+                                                         int E, int k, int kden, int renorm,
+                                                         int want_key, int32_t *__restrict__ ids,
+                                                         float *__restrict__ gates,
+                                                         float *__restrict__ keys) {
+  constexpr int G = 16, PL = 8;
+  extern __shared__ float qsh[];   // [16][E] when want_key
+  const int gl = threadIdx.x % G, gi = threadIdx.x / G;
+  const int t = blockIdx.x * (256 / G) + gi;
+  const bool live = t < T;
+  float lv[PL];
+  KE a[PL];
+#pragma unroll
+  for (int i = 0; i < PL; ++i) {
+    const int e = gl + i * G;
+    lv[i] = (live && e < E) ? logits[(size_t)t * E + e] : -INFINITY;
+    a[i] = KE{lv[i], e < E ? e : 0x7fffffff};
+  }
+  // sort the lane's 8 pairs (Batcher's odd-even merge sort)
+  ke_ce(a[0], a[1]); ke_ce(a[2], a[3]); ke_ce(a[4], a[5]); ke_ce(a[6], a[7]);
+  ke_ce(a[0], a[2]); ke_ce(a[1], a[3]); ke_ce(a[4], a[6]); ke_ce(a[5], a[7]);
+  ke_ce(a[1], a[2]); ke_ce(a[5], a[6]);
+  ke_ce(a[0], a[4]); ke_ce(a[1], a[5]); ke_ce(a[2], a[6]); ke_ce(a[3], a[7]);
+  ke_ce(a[2], a[4]); ke_ce(a[3], a[5]);
+  ke_ce(a[1], a[2]); ke_ce(a[3], a[4]); ke_ce(a[5], a[6]);
+#pragma unroll
+  for (int o = G / 2; o > 0; o >>= 1) {
+    KE b[PL];
+#pragma unroll
+    for (int i = 0; i < PL; ++i) {
+      b[i].v = __shfl_xor(a[i].v, o, 64);
+      b[i].e = __shfl_xor(a[i].e, o, 64);
+    }
+#pragma unroll
+    for (int i = 0; i < PL; ++i)
+      if (!ke_before(a[i], b[PL - 1 - i])) a[i] = b[PL - 1 - i];
+#pragma unroll
+    for (int dd = PL / 2; dd > 0; dd >>= 1)
+#pragma unroll
+      for (int i = 0; i < PL; ++i)
+        if ((i & dd) == 0) ke_ce(a[i], a[i + dd]);
+  }
+  const float mx = a[0].v;
+  float qn[PL], qsum = 0.f;
+#pragma unroll
+  for (int r = 0; r < PL; ++r) {
+    qn[r] = expf(a[r].v - mx);
+    if (r < k && r < kden) qsum += qn[r];
+  }
+  float denom = qsum;
+  if (!renorm) {
+    float sm = 0.f;
+#pragma unroll
+    for (int i = 0; i < PL; ++i) {
+      const int e = gl + i * G;
+      if (e < E) sm += expf(lv[i] - mx);
+    }
+#pragma unroll
+    for (int o = G / 2; o > 0; o >>= 1) sm += __shfl_xor(sm, o, 64);
+    denom = sm;
+  }
+  if (gl == 0 && live) {
+#pragma unroll
+    for (int r = 0; r < PL; ++r)
+      if (r < k) {
+        ids[(size_t)t * k + r] = a[r].e;
+        gates[(size_t)t * k + r] = qn[r] / denom;
+      }
+  }
+  if (want_key) {
+    float *qrow = qsh + gi * E;
+#pragma unroll
+    for (int i = 0; i < PL; ++i) {
+      const int e = gl + i * G;
+      if (e < E) qrow[e] = live ? rexp_spec(__fsub_rn(lv[i], mx)) : 0.f;
+    }
+    __syncthreads();
+    if (gl == 0 && live) {
+      float S = qrow[0];
+      for (int e = 1; e < E; ++e) S = __fadd_rn(S, qrow[e]);
+#pragma unroll
+      for (int r = 0; r < PL; ++r)
+        if (r < k) keys[(size_t)t * k + r] = qrow[a[r].e] / S;
+    }
+  }
+}
+
 // ----------------------------------------------------------------------------------------
 // Dispatch histogram. Block b owns tokens [256b, 256b+256). Each token has a row of S slots
 // (expert ids); the pairs taken are the slots in [j0, j1), minus those with kept == 0 when a
@@ -1244,6 +1348,9 @@ hipError_t launch_topk(const float *logits, int T, int E, int k, int kden, int r
   if (E <= 8) MOE_TOPK(8, 1);
   else if (E <= 16) MOE_TOPK(16, 1);
   else if (E <= 32) MOE_TOPK(32, 1);
+  else if (E <= 128 && k >= 5 && k <= 8)   // merging beats k argmax rounds from k = 5 on
+    hipLaunchKernelGGL(topk_merge_kernel, grid, dim3(256), sh, st, logits, T, E, k, kden, renorm,
+                       want_key, ids, gates, keys);
   else if (E <= 128) MOE_TOPK(16, 8);
   else MOE_TOPK(64, kMaxExperts / 64);
 #undef MOE_TOPK
