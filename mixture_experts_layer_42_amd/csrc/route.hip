@@ -54,7 +54,8 @@ MOE_DEV float rexp_spec(float x) {
 }
 
 // ----------------------------------------------------------------------------------------
-// Router, E <= 8. A workgroup of 8 waves streams a run of tokens: lane l of wave w owns VEC
+// SIMT router, E <= 8 (float32 x, or bf16 x with d not a multiple of 64). A workgroup of 8
+// waves streams a run of tokens: lane l of wave w owns VEC
 // consecutive columns (w*64 + l)*VEC of a 512*VEC-column pass and keeps their W_r rows in
 // registers, so W_r is read once per workgroup (per pass); x is read once. Per batch of 8
 // tokens each lane accumulates 8 tokens x 8 experts over its columns; a butterfly
@@ -162,7 +163,8 @@ __global__ __launch_bounds__(512) void router_narrow_kernel(const XT *__restrict
 }
 
 // ----------------------------------------------------------------------------------------
-// Router, E > 8. One workgroup = 4 waves handles 64 tokens x up to 128 experts (grid.y
+// SIMT router, E > 8 (float32 x, or bf16 x with d not a multiple of 64). One workgroup = 4
+// waves handles 64 tokens x up to 128 experts (grid.y
 // walks expert blocks of 128). x and W_r tiles of 64 columns are staged in LDS; lane l
 // owns experts l and l+64, wave w tokens w*16..w*16+15. Each 64-column chunk is summed
 // into a fresh partial before being added to the total (two-level float32 sum).
@@ -1308,6 +1310,7 @@ hipError_t launch_router(int dtype, const void *x, const float *w, const float *
                        logits, T, d, E, E_pad);
     return hipGetLastError();
   }
+  // SIMT float32: float32 x, or bf16 x whose d is not a multiple of 64
   if (E <= 8) {
     // tokens per workgroup: a multiple of 8, about T / 256 (one workgroup per CU)
     int tpb = ((T + 255) / 256 + 7) / 8 * 8;
@@ -1334,7 +1337,8 @@ hipError_t launch_router(int dtype, const void *x, const float *w, const float *
 hipError_t launch_topk(const float *logits, int T, int E, int k, int kden, int renorm,
                        int want_key, int32_t *ids, float *gates, float *keys, hipStream_t st) {
   // G lanes per token, each holding up to PL logits: narrow rows keep one logit per lane;
-  // up to 128 experts use 16 lanes x 8 (a 4-step butterfly per pick, 16 tokens per block)
+  // up to 128 experts use 16 lanes x 8 (16 tokens per block): merged sorted lists for
+  // k = 5..8, else a 4-step butterfly per pick
   int G = 64;
   if (E <= 8) G = 8;
   else if (E <= 16) G = 16;
