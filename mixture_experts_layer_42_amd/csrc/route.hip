@@ -54,8 +54,8 @@ MOE_DEV float rexp_spec(float x) {
 }
 
 // ----------------------------------------------------------------------------------------
-// SIMT router, E <= 8 (float32 x, or bf16 x with d not a multiple of 64). A workgroup of 8
-// waves streams a run of tokens: lane l of wave w owns VEC
+// SIMT router for float32 x, E <= 8 (bf16 x always takes the matrix-core routers: bf16
+// problems have d a multiple of 64). A workgroup of 8 waves streams a run of tokens: lane l of wave w owns VEC
 // consecutive columns (w*64 + l)*VEC of a 512*VEC-column pass and keeps their W_r rows in
 // registers, so W_r is read once per workgroup (per pass); x is read once. Per batch of 8
 // tokens each lane accumulates 8 tokens x 8 experts over its columns; a butterfly
@@ -163,8 +163,8 @@ __global__ __launch_bounds__(512) void router_narrow_kernel(const XT *__restrict
 }
 
 // ----------------------------------------------------------------------------------------
-// SIMT router, E > 8 (float32 x, or bf16 x with d not a multiple of 64). One workgroup = 4
-// waves handles 64 tokens x up to 128 experts (grid.y
+// SIMT router for float32 x, E > 8. One workgroup = 4 waves handles 64 tokens x up to 128
+// experts (grid.y
 // walks expert blocks of 128). x and W_r tiles of 64 columns are staged in LDS; lane l
 // owns experts l and l+64, wave w tokens w*16..w*16+15. Each 64-column chunk is summed
 // into a fresh partial before being added to the total (two-level float32 sum).
@@ -1310,26 +1310,19 @@ hipError_t launch_router(int dtype, const void *x, const float *w, const float *
                        logits, T, d, E, E_pad);
     return hipGetLastError();
   }
-  // SIMT float32: float32 x, or bf16 x whose d is not a multiple of 64
+  // SIMT float32 routers (bf16 problems, whose d is a multiple of 64, never get here)
+  if (dtype != 0) return hipErrorInvalidValue;
   if (E <= 8) {
     // tokens per workgroup: a multiple of 8, about T / 256 (one workgroup per CU)
     int tpb = ((T + 255) / 256 + 7) / 8 * 8;
     if (tpb < 8) tpb = 8;
     dim3 grid((T + tpb - 1) / tpb);
-    if (dtype == 0)
-      hipLaunchKernelGGL(router_narrow_kernel<float>, grid, dim3(512), 0, st,
-                         (const float *)x, w, bias, logits, T, d, E, tpb);
-    else
-      hipLaunchKernelGGL(router_narrow_kernel<bf16_t>, grid, dim3(512), 0, st,
-                         (const bf16_t *)x, w, bias, logits, T, d, E, tpb);
+    hipLaunchKernelGGL(router_narrow_kernel<float>, grid, dim3(512), 0, st, (const float *)x, w,
+                       bias, logits, T, d, E, tpb);
   } else {
     dim3 grid((T + 63) / 64, (E + 127) / 128);
-    if (dtype == 0)
-      hipLaunchKernelGGL(router_wide_kernel<float>, grid, dim3(256), 0, st, (const float *)x, w,
-                         bias, logits, T, d, E);
-    else
-      hipLaunchKernelGGL(router_wide_kernel<bf16_t>, grid, dim3(256), 0, st, (const bf16_t *)x,
-                         w, bias, logits, T, d, E);
+    hipLaunchKernelGGL(router_wide_kernel<float>, grid, dim3(256), 0, st, (const float *)x, w,
+                       bias, logits, T, d, E);
   }
   return hipGetLastError();
 }
