@@ -515,8 +515,10 @@ __global__ __launch_bounds__(256) void gemm_tail_reduce_kernel(GemmArgs args) {
 // read once, so the GEMM is bound by streaming the weights from HBM; a 256-row tile would
 // spend its MFMAs on padding. A unit is 32*MB rows x 256 B-columns x one K part of a group;
 // 4 waves own 64 B-columns each (for gate/up 32 gate and the matching 32 up columns), K in
-// slices of 64 through three LDS stages. With S > 1 K parts, each unit writes float32 sums
-// to the partial buffer and gemm_skinny_reduce_kernel adds the parts in order.
+// slices of 64 through three LDS stages. K is cut into S parts only as far as needed for about
+// one unit per CU (longer units keep the copy pipeline full: fewer parts measured faster than
+// a thousand short units); with S > 1 each unit writes float32 sums to the partial buffer
+// and gemm_skinny_reduce_kernel adds the parts in order.
 struct SkinnyPlan { int mb, S, nt, snt, pitch; };
 
 SkinnyPlan skinny_plan(const GemmArgs &a, bool gate_up) {
@@ -530,7 +532,7 @@ SkinnyPlan skinny_plan(const GemmArgs &a, bool gate_up) {
   const int tiles = used * sp.nt + sp.snt;
   const int nk = a.K / BK, snk = a.s_rows > 0 ? a.sK / BK : nk;
   int S = 1;
-  while (S < 16 && tiles * S < 1024 && nk % (2 * S) == 0 && snk % (2 * S) == 0 &&
+  while (S < 16 && tiles * S < 256 && nk % (2 * S) == 0 && snk % (2 * S) == 0 &&
          nk / (2 * S) >= 2 && snk / (2 * S) >= 2)
     S *= 2;
   sp.S = S;
@@ -553,6 +555,7 @@ __global__ __launch_bounds__(256, 1) void gemm_skinny_kernel(GemmArgs args) {
   constexpr int SBM = 32 * MB;
   constexpr int DMA = MB + 8;   // 1 KB copies per wave per slice: A MB, B 8
   constexpr int BNOUT = GATE_UP ? BN / 2 : BN;
+  constexpr int NS = 3;   // stages (a fourth measured no faster)
   __shared__ SkStage<MB> st0, st1, st2;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int wvu = __builtin_amdgcn_readfirstlane(wv);
@@ -602,12 +605,13 @@ __global__ __launch_bounds__(256, 1) void gemm_skinny_kernel(GemmArgs args) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[m][j][v] = 0.f;
     issue(st0, 0);
+    sched_fence();
     issue(st1, min(1, nk - 1));
     auto step = [&](const SkStage<MB> &cur, SkStage<MB> &refill, int kt) {
       sched_fence();
-      wait_and_barrier<DMA>();                     // slice kt has landed (kt+1 may not)
+      wait_and_barrier<(NS - 2) * DMA>();          // slice kt has landed (later ones may not)
       sched_fence();
-      issue(refill, min(kt + 2, nk - 1));           // past the end: re-read the last slice
+      issue(refill, min(kt + NS - 1, nk - 1));      // past the end: re-read the last slice
 #pragma unroll
       for (int ks = 0; ks < kSub; ++ks) {
         const int chunk = ks * 2 + (lane >> 5);
@@ -827,7 +831,7 @@ hipError_t launch_bf16(const GemmArgs &a0, bool gate_up, int max_rows, int num_c
   GemmArgs a = a0;
   const int bn_out = gate_up ? BN / 2 : BN;
   int grid = gemm_tiles_upper(a, BM, bn_out, max_rows);
-  int cap = num_cu;   // one workgroup per CU (the four LDS stages take 128 KB)
+  int cap = num_cu;   // one workgroup per CU (the two 64 KB LDS stages)
   if (cap > kMaxPersistent) cap = kMaxPersistent;
   if (grid > cap) grid = cap;
   if (grid < 1) grid = 1;
