@@ -42,6 +42,9 @@ def parse():
                     help="tokens in the oracle sample (default: about 15 s of oracle work)")
     ap.add_argument("--pmc-copy", action="store_true",
                     help="after timing, run a plain 256 MiB device copy (counter calibration)")
+    ap.add_argument("--library-gemm", action="store_true",
+                    help="also time torch.matmul (the vendor GEMM library) on the same expert "
+                         "GEMM shapes, as a reference point for the grouped GEMM")
     return ap.parse_args()
 
 
@@ -138,6 +141,61 @@ def recorded_traffic(workload):
         return None
     ent = rec.get("gate_up", {}).get(workload)
     return None if ent is None else float(ent["hbm_bytes_per_launch"])
+
+
+def library_gemm(cfg, counts, dev, reps=10):
+    """Reference throughput of the vendor GEMM library (torch.matmul) on the routed expert
+    GEMMs: one call per expert with that expert's row count (contiguous rows, no gather, no
+    SwiGLU), and the same kept rows through a single expert's weights as one dense call
+    (the weights then stay in cache across row tiles). Flops count kept rows only."""
+    import torch
+    d, f = cfg.d_model, cfg.d_ff
+    rows = [int(c) for c in counts]
+    n = sum(rows)
+    torch.manual_seed(0)
+    xs = torch.randn(max(n, 1), d, device="cuda", dtype=torch.bfloat16)
+    hs = torch.randn(max(n, 1), f, device="cuda", dtype=torch.bfloat16)
+    wgu = [torch.cat([dev["w_gate"][e], dev["w_up"][e]], 0) if r else None
+           for e, r in enumerate(rows)]
+    wdn = dev["w_down"]
+
+    def timed(fn):
+        for _ in range(2):
+            fn()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0.record()
+        for _ in range(reps):
+            fn()
+        t1.record()
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / reps * 1e-3
+
+    def per_expert(kind):
+        def run():
+            o = 0
+            for e, r in enumerate(rows):
+                if r:
+                    if kind == "gate_up":
+                        torch.matmul(xs[o:o + r], wgu[e].t())
+                    else:
+                        torch.matmul(hs[o:o + r], wdn[e].t())
+                    o += r
+        return run
+
+    e0 = next(e for e, r in enumerate(rows) if r)
+    out = {}
+    for kind, fl in (("gate_up", 4.0 * d * f * n), ("down", 2.0 * d * f * n)):
+        t_pe = timed(per_expert(kind))
+        if kind == "gate_up":
+            t_dn = timed(lambda: torch.matmul(xs[:n], wgu[e0].t()))
+        else:
+            t_dn = timed(lambda: torch.matmul(hs[:n], wdn[e0].t()))
+        out[kind] = {"per_expert_tflops": round(fl / t_pe / 1e12, 1),
+                     "per_expert_frac": round(fl / t_pe / 1e12 / PEAK_BF16_TFLOPS, 4),
+                     "dense_tflops": round(fl / t_dn / 1e12, 1),
+                     "dense_frac": round(fl / t_dn / 1e12 / PEAK_BF16_TFLOPS, 4)}
+    return out
 
 
 def main():
@@ -266,6 +324,9 @@ def main():
         "stages": stages,
         "host_s": round(host_s, 4),
     }
+    if args.library_gemm and cfg.dtype == "bf16":
+        print("[bench] library GEMM reference", file=sys.stderr, flush=True)
+        out["library_gemm"] = library_gemm(cfg, rb.counts.cpu().numpy(), dev)
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline: oracle on a token sample", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(inp, args.cpu_sample)
