@@ -7,7 +7,10 @@ indices, row gather, grouped gate/up + SwiGLU GEMM, grouped down GEMM, weighted
 combine), inputs resident in HBM. Prints ONE JSON line. The per-stage durations come
 from HIP events that the library records on its own stream at each stage boundary
 (moe_layer_forward_traced), so the dominant kernel's time is measured inside the timed
-region. The cpu_baseline leg times the CPU oracle on a bounded token sample.
+region. After the timed steps: the same steps with the last-level cache flushed before each
+("cold"), and measured ceilings on this GPU ("achievable": the vendor GEMM library on the
+dense-equivalent gate/up GEMM, a plain device copy). The cpu_baseline leg times the CPU
+oracle on a bounded token sample.
 """
 from __future__ import annotations
 
@@ -45,6 +48,10 @@ def parse():
     ap.add_argument("--library-gemm", action="store_true",
                     help="also time torch.matmul (the vendor GEMM library) on the same expert "
                          "GEMM shapes, as a reference point for the grouped GEMM")
+    ap.add_argument("--no-cold", action="store_true",
+                    help="skip the cold-cache steps (last-level cache flushed before each)")
+    ap.add_argument("--no-achievable", action="store_true",
+                    help="skip the measured ceilings (library GEMM, device copy)")
     return ap.parse_args()
 
 
@@ -198,6 +205,45 @@ def library_gemm(cfg, counts, dev, reps=10):
     return out
 
 
+def achievable(cfg, n_kept, dev):
+    """Measured ceilings on this GPU for the two rooflines: the vendor GEMM library
+    (torch.matmul) on the dense-equivalent of the gate/up GEMM (the kept rows through one
+    expert's gate and up weights, so the weights are reused by every row tile), and a plain
+    device copy of 1 GiB (read + write bytes / time)."""
+    import torch
+    out = {}
+
+    def timed(fn, reps):
+        for _ in range(2):
+            fn()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0.record()
+        for _ in range(reps):
+            fn()
+        t1.record()
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / reps * 1e-3
+
+    if cfg.dtype == "bf16" and n_kept >= 256:
+        torch.manual_seed(0)
+        a = torch.randn(n_kept, cfg.d_model, device="cuda", dtype=torch.bfloat16)
+        w = torch.cat([dev["w_gate"][0], dev["w_up"][0]], 0)
+        t = timed(lambda: torch.matmul(a, w.t()), 10)
+        tf = 4.0 * cfg.d_model * cfg.d_ff * n_kept / t / 1e12
+        out["gemm_tflops"] = round(tf, 1)
+        out["gemm_frac_of_peak"] = round(tf / PEAK_BF16_TFLOPS, 4)
+        out["gemm_how"] = "torch.matmul bf16, kept rows x one expert's gate+up weights (dense)"
+        del a, w
+    src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    t = timed(lambda: dst.copy_(src), 10)
+    gbs = 2.0 * src.numel() / t / 1e9
+    out["hbm_copy_gbs"] = round(gbs, 1)
+    out["hbm_copy_frac_of_peak"] = round(gbs / PEAK_HBM_GBS, 4)
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -268,6 +314,21 @@ def main():
     ms_per_step = total_ms / args.steps
     value = cfg.T / (ms_per_step * 1e-3)
 
+    cold = None
+    if not args.no_cold:
+        # the same steps with the 256 MB last-level cache flushed (a 512 MB write) before
+        # each; per-step time between the layer's first and last stage events
+        flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+        cold_ms = []
+        for i in range(args.steps):
+            flush.fill_(i & 0xFF)
+            step(step_events[i])
+        torch.cuda.synchronize()
+        cold_ms = [step_events[i][0].elapsed_time(step_events[i][moe.MOE_STAGE_COUNT])
+                   for i in range(args.steps)]
+        cold = float(np.median(cold_ms))
+        del flush
+
     if args.pmc_copy:
         a = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
         b = torch.empty_like(a)
@@ -321,9 +382,18 @@ def main():
                      "traffic": None if (args.tokens or args.gamma is not None or args.expand_m
                                          or args.cap_groups) else recorded_traffic(cfg.name)},
         "grouped_gemm_mfma_util": round(gemm_tf / PEAK_BF16_TFLOPS, 4),
+        "cold": None if cold is None else {
+            "ms_per_step": round(cold, 4), "tokens_per_s": round(cfg.T / (cold * 1e-3), 1),
+            "how": "median over the steps, 512 MB write before each (flushes the last-level cache)"},
         "stages": stages,
         "host_s": round(host_s, 4),
     }
+    if not args.no_achievable:
+        print("[bench] measured ceilings", file=sys.stderr, flush=True)
+        ach = achievable(cfg, n_kept, dev)
+        out["achievable"] = ach
+        if "gemm_tflops" in ach:
+            out["roofline"]["frac_of_achievable"] = round(gu_tf / ach["gemm_tflops"], 4)
     if args.library_gemm and cfg.dtype == "bf16":
         print("[bench] library GEMM reference", file=sys.stderr, flush=True)
         out["library_gemm"] = library_gemm(cfg, rb.counts.cpu().numpy(), dev)
