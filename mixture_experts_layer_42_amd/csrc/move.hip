@@ -29,8 +29,9 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(const uint4 *__restric
 }
 
 // y[t] = sum_{i in [tok_ptr[t], tok_ptr[t+1])} perm_w[tok_pos[i]] * o[tok_pos[i]] (+ o_shared[t]),
-// float32 sum in CSR order (the shared row added last), one rounding into y. One wave per
-// token: the token's row indices and weights sit one per lane and are broadcast; each step
+// float32 sum in CSR order (the shared row added last), one rounding into y. WPT waves per
+// token (more than one when there are few tokens), each taking every WPT-th block of 1024
+// columns: the token's row indices and weights sit one per lane and are broadcast; each step
 // issues the loads of two rows x CH column chunks (16 bytes of o per lane per chunk) before
 // the multiply-adds, so several rows' loads are in flight at once. A missing second row of a
 // pair reads the first row again with weight 0, which leaves the sum unchanged
@@ -54,13 +55,15 @@ __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ 
                                                       const int32_t *__restrict__ tok_ptr,
                                                       const int32_t *__restrict__ tok_pos,
                                                       const float *__restrict__ perm_w,
-                                                      TY *__restrict__ y, int Tn, int d) {
+                                                      TY *__restrict__ y, int Tn, int d, int wpt) {
   constexpr int CH = 4;   // 256-column chunks per step
   const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int gw = blockIdx.x * 4 + (threadIdx.x >> 6);   // global wave
+  const int t = gw / wpt, part = gw % wpt;
   if (t >= Tn) return;
   const int b = tok_ptr[t], n = tok_ptr[t + 1] - b;
-  for (int cb = 0; cb < d; cb += 256 * CH) {   // uniform over the wave (the shuffles below)
+  // uniform over the wave (the shuffles below)
+  for (int cb = part * 256 * CH; cb < d; cb += wpt * 256 * CH) {
     const int c0 = cb + lane * 4;
     float4 acc[CH];
 #pragma unroll
@@ -132,13 +135,18 @@ hipError_t launch_gather(int elt, const void *x, const int32_t *perm_token,
 hipError_t launch_combine(int y_elt, const float *o, const float *o_shared,
                           const int32_t *tok_ptr, const int32_t *tok_pos, const float *perm_w,
                           void *y, int T, int d, int max_rows, hipStream_t st) {
-  dim3 grid((T + 3) / 4);
+  // few tokens: split each row's 1024-column blocks over several waves (about 1024 waves)
+  const int blocks = (d + 1023) / 1024;
+  int wpt = (1024 + T - 1) / T;
+  if (wpt > blocks) wpt = blocks;
+  if (wpt < 1) wpt = 1;
+  dim3 grid((unsigned)(((long)T * wpt + 3) / 4));
   // bytes of o the combine may read: past ~320 MB (above the 256 MB MALL) streaming loads
   // measured faster (fine-grained layer 63% -> 78% of HBM); below, plain loads win
   const double obytes = ((double)max_rows + (o_shared ? T : 0)) * d * 4.0;
   const bool nt = obytes > 320e6;
 #define MOE_COMB(TYY, NTT) hipLaunchKernelGGL((combine_kernel<TYY, NTT>), grid, dim3(256), 0, st, o, \
-                                               o_shared, tok_ptr, tok_pos, perm_w, (TYY *)y, T, d)
+                                               o_shared, tok_ptr, tok_pos, perm_w, (TYY *)y, T, d, wpt)
   if (y_elt == 2) { if (nt) MOE_COMB(bf16_t, true); else MOE_COMB(bf16_t, false); }
   else { if (nt) MOE_COMB(float, true); else MOE_COMB(float, false); }
 #undef MOE_COMB

@@ -837,20 +837,21 @@ __global__ __launch_bounds__(1024) void assign_scan_kernel(const int32_t *__rest
   }
 }
 
-// Stable scatter: pair (t, j) of bucket b goes to off[b] + blk_base[blk][b] + (its rank in
-// the block). Candidate mode writes (token, slot, key) lists for cap_select; final mode
-// writes the dispatch arrays, and marks the slots in [j0, j1) that were not taken with -1.
-// When every slot of every token is kept (no capacity limit), final mode can also write the
-// token -> rows CSR directly (csr_ptr, csr_pos non-null): token t owns entries t*S .. t*S+S-1.
-__global__ __launch_bounds__(256) void assign_scatter_kernel(
-    const int32_t *__restrict__ ids, const float *__restrict__ gates,
-    const float *__restrict__ keys, int T, PairSel f, int B, const int32_t *__restrict__ off,
-    const int32_t *__restrict__ blk_base, int candidates, int32_t *__restrict__ out_token,
-    float *__restrict__ out_w, int32_t *__restrict__ out_slot, float *__restrict__ out_key,
-    int32_t *__restrict__ slot_pos, uint8_t *__restrict__ kept_out, int32_t *__restrict__ csr_ptr,
-    int32_t *__restrict__ csr_pos) {
-  extern __shared__ uint32_t mask[];
-  build_masks(mask, ids, f, T, B);
+// Stable scatter: pair (t, j) of bucket b goes to off[b] + base[b] + (its rank in the
+// block), base = this block's offsets inside the buckets (null: 0, a single block).
+// Candidate mode writes (token, slot, key) lists for cap_select; final mode writes the
+// dispatch arrays, and marks the slots in [j0, j1) that were not taken with -1. When every
+// slot of every token is kept (no capacity limit), final mode can also write the token ->
+// rows CSR directly (csr_ptr, csr_pos non-null): token t owns entries t*S .. t*S+S-1.
+// Expects the block's masks (build_masks) in `mask`.
+MOE_DEV void scatter_block(const uint32_t *mask, const int32_t *__restrict__ ids,
+                           const float *__restrict__ gates, const float *__restrict__ keys, int T,
+                           const PairSel &f, const int32_t *off, const int32_t *base,
+                           int candidates, int32_t *__restrict__ out_token,
+                           float *__restrict__ out_w, int32_t *__restrict__ out_slot,
+                           float *__restrict__ out_key, int32_t *__restrict__ slot_pos,
+                           uint8_t *__restrict__ kept_out, int32_t *__restrict__ csr_ptr,
+                           int32_t *__restrict__ csr_pos) {
   const int t = blockIdx.x * 256 + threadIdx.x;
   if (t >= T) return;
   if (csr_ptr) {   // every pair kept, in slot order: token t's rows are CSR entries t*S ..
@@ -878,7 +879,7 @@ __global__ __launch_bounds__(256) void assign_scatter_kernel(
       rank += __popc(mk[word] & ((1u << bit) - 1u));
       for (int w = 0; w < word; ++w) rank += __popc(mk[w]);
     }
-    const int pos = off[b] + blk_base[(size_t)blockIdx.x * B + b] + rank;
+    const int pos = off[b] + (base ? base[b] : 0) + rank;
     if (candidates) {
       out_token[pos] = t;
       out_slot[pos] = j;
@@ -892,6 +893,71 @@ __global__ __launch_bounds__(256) void assign_scatter_kernel(
       if (csr_pos) csr_pos[ij] = pos;
     }
   }
+}
+
+__global__ __launch_bounds__(256) void assign_scatter_kernel(
+    const int32_t *__restrict__ ids, const float *__restrict__ gates,
+    const float *__restrict__ keys, int T, PairSel f, int B, const int32_t *__restrict__ off,
+    const int32_t *__restrict__ blk_base, int candidates, int32_t *__restrict__ out_token,
+    float *__restrict__ out_w, int32_t *__restrict__ out_slot, float *__restrict__ out_key,
+    int32_t *__restrict__ slot_pos, uint8_t *__restrict__ kept_out, int32_t *__restrict__ csr_ptr,
+    int32_t *__restrict__ csr_pos) {
+  extern __shared__ uint32_t mask[];
+  build_masks(mask, ids, f, T, B);
+  scatter_block(mask, ids, gates, keys, T, f, off, blk_base + (size_t)blockIdx.x * B, candidates,
+                out_token, out_w, out_slot, out_key, slot_pos, kept_out, csr_ptr, csr_pos);
+}
+
+// All three steps for at most 256 tokens (one block): masks, bucket counts and offsets (as
+// assign_scan_kernel computes them for one block, including the capped second table when
+// C >= 0), then the scatter. Thread i owns buckets 4i .. 4i+3 for the scans (B <= 1024).
+// Dynamic LDS: the masks, then B ints of bucket offsets.
+__global__ __launch_bounds__(256) void assign_single_kernel(
+    const int32_t *__restrict__ ids, const float *__restrict__ gates,
+    const float *__restrict__ keys, int T, PairSel f, int B, int C, int32_t *__restrict__ cnt_pre,
+    int32_t *__restrict__ off_pre, int32_t *__restrict__ cnt_fin, int32_t *__restrict__ off_fin,
+    int candidates, int32_t *__restrict__ out_token, float *__restrict__ out_w,
+    int32_t *__restrict__ out_slot, float *__restrict__ out_key, int32_t *__restrict__ slot_pos,
+    uint8_t *__restrict__ kept_out, int32_t *__restrict__ csr_ptr, int32_t *__restrict__ csr_pos) {
+  extern __shared__ uint32_t mask[];
+  int32_t *soff = reinterpret_cast<int32_t *>(mask + (size_t)B * f.mult * 8);
+  __shared__ int sm[256 / 64 + 1];
+  build_masks(mask, ids, f, T, B);
+  int c[4], own = 0, own_fin = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int b = threadIdx.x * 4 + q;
+    c[q] = 0;
+    if (b < B)
+      for (int m = 0; m < f.mult; ++m)
+#pragma unroll
+        for (int w = 0; w < 8; ++w) c[q] += __popc(mask[(b * f.mult + m) * 8 + w]);
+    own += c[q];
+    own_fin += C >= 0 ? min(c[q], C) : 0;
+  }
+  int tot;
+  int run = block_excl_scan(own, sm, &tot);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int b = threadIdx.x * 4 + q;
+    if (b < B) { cnt_pre[b] = c[q]; off_pre[b] = run; soff[b] = run; }
+    run += c[q];
+  }
+  if (threadIdx.x == 0) off_pre[B] = tot;
+  if (C >= 0) {
+    int run2 = block_excl_scan(own_fin, sm, &tot);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int b = threadIdx.x * 4 + q;
+      const int kc = min(c[q], C);
+      if (b < B) { cnt_fin[b] = kc; off_fin[b] = run2; }
+      run2 += kc;
+    }
+    if (threadIdx.x == 0) off_fin[B] = tot;
+  }
+  __syncthreads();
+  scatter_block(mask, ids, gates, keys, T, f, soff, nullptr, candidates, out_token, out_w, out_slot,
+                out_key, slot_pos, kept_out, csr_ptr, csr_pos);
 }
 
 // Expanded drop, between its two selections: a token that lost some of its first k picks
@@ -1365,8 +1431,22 @@ void assign_pairs(const RouteScratch &s, const int32_t *ids, const float *gates,
                   int32_t *csr_ptr = nullptr, int32_t *csr_pos = nullptr) {
   const int nblk = (T + 255) / 256;
   const size_t msh = (size_t)B * f.mult * 8 * sizeof(uint32_t);
-  hipLaunchKernelGGL(assign_count_kernel, dim3(nblk), dim3(256), msh, st, ids, T, f, B, s.blk_cnt);
   int32_t *cnt = candidates ? s.cnt_pre : counts, *off = candidates ? s.off_pre : offsets;
+  if (nblk == 1) {   // one launch instead of three
+    if (candidates)
+      hipLaunchKernelGGL(assign_single_kernel, dim3(1), dim3(256), msh + (size_t)B * 4, st, ids,
+                         gates, s.keys, T, f, B, -1, cnt, off, (int32_t *)nullptr,
+                         (int32_t *)nullptr, 1, s.cand_token, s.cand_w, s.cand_slot, s.cand_key,
+                         (int32_t *)nullptr, (uint8_t *)nullptr, (int32_t *)nullptr,
+                         (int32_t *)nullptr);
+    else
+      hipLaunchKernelGGL(assign_single_kernel, dim3(1), dim3(256), msh + (size_t)B * 4, st, ids,
+                         gates, (const float *)nullptr, T, f, B, -1, cnt, off, (int32_t *)nullptr,
+                         (int32_t *)nullptr, 0, perm_token, perm_w, (int32_t *)nullptr,
+                         (float *)nullptr, s.slot_pos, kept_out, csr_ptr, csr_pos);
+    return;
+  }
+  hipLaunchKernelGGL(assign_count_kernel, dim3(nblk), dim3(256), msh, st, ids, T, f, B, s.blk_cnt);
   hipLaunchKernelGGL(assign_scan_kernel, dim3(1), dim3(1024), 0, st, s.blk_cnt, nblk, B, -1,
                      s.blk_base, cnt, off, (int32_t *)nullptr, (int32_t *)nullptr);
   if (candidates)
@@ -1395,14 +1475,21 @@ hipError_t launch_token_dispatch(const RouteScratch &s, const int32_t *ids, cons
     return hipGetLastError();
   }
   const size_t msh = (size_t)E * 8 * sizeof(uint32_t);
-  hipLaunchKernelGGL(assign_count_kernel, dim3(nblk), dim3(256), msh, st, ids, T, all, E,
-                     s.blk_cnt);
-  hipLaunchKernelGGL(assign_scan_kernel, dim3(1), dim3(1024), 0, st, s.blk_cnt, nblk, E, C,
-                     s.blk_base, s.cnt_pre, s.off_pre, counts, offsets);
-  hipLaunchKernelGGL(assign_scatter_kernel, dim3(nblk), dim3(256), msh, st, ids, gates, s.keys, T,
-                     all, E, s.off_pre, s.blk_base, 1, s.cand_token, s.cand_w,
-                     s.cand_slot, s.cand_key, (int32_t *)nullptr, (uint8_t *)nullptr,
-                     (int32_t *)nullptr, (int32_t *)nullptr);
+  if (nblk == 1) {   // one launch instead of three
+    hipLaunchKernelGGL(assign_single_kernel, dim3(1), dim3(256), msh + (size_t)E * 4, st, ids,
+                       gates, s.keys, T, all, E, C, s.cnt_pre, s.off_pre, counts, offsets, 1,
+                       s.cand_token, s.cand_w, s.cand_slot, s.cand_key, (int32_t *)nullptr,
+                       (uint8_t *)nullptr, (int32_t *)nullptr, (int32_t *)nullptr);
+  } else {
+    hipLaunchKernelGGL(assign_count_kernel, dim3(nblk), dim3(256), msh, st, ids, T, all, E,
+                       s.blk_cnt);
+    hipLaunchKernelGGL(assign_scan_kernel, dim3(1), dim3(1024), 0, st, s.blk_cnt, nblk, E, C,
+                       s.blk_base, s.cnt_pre, s.off_pre, counts, offsets);
+    hipLaunchKernelGGL(assign_scatter_kernel, dim3(nblk), dim3(256), msh, st, ids, gates, s.keys,
+                       T, all, E, s.off_pre, s.blk_base, 1, s.cand_token, s.cand_w,
+                       s.cand_slot, s.cand_key, (int32_t *)nullptr, (uint8_t *)nullptr,
+                       (int32_t *)nullptr, (int32_t *)nullptr);
+  }
   hipLaunchKernelGGL(cap_select_kernel, dim3(E), dim3(1024), 0, st, s.cand_token, s.cand_slot,
                      s.cand_key, s.cand_w, s.cnt_pre, s.off_pre, offsets, C, (const int32_t *)nullptr, k,
                      perm_token, perm_w, s.slot_pos, kept);

@@ -170,6 +170,9 @@ TIE_CASES = [
     dict(T=999, E=16, k=2, gamma=0.75, expand_m=3), dict(T=300, E=32, k=4, gamma=0.5, expand_m=8),
     dict(T=1000, E=8, k=2, gamma=0.5, cap_groups=2), dict(T=500, E=64, k=8, gamma=1.25, cap_groups=8),
     dict(T=333, E=16, k=4, gamma=0.25, cap_groups=1),
+    # at most 256 tokens: the single-block histogram + scan + scatter
+    dict(T=200, E=16, k=2, gamma=0.75, expand_m=3), dict(T=150, E=16, k=4, gamma=0.5, cap_groups=4),
+    dict(T=256, E=1024, k=8, gamma=1.0), dict(T=256, E=8, k=2),
 ]
 
 
