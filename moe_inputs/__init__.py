@@ -79,6 +79,21 @@ CONFIGS = {
 }
 
 
+def workload(name: str) -> MoEConfig:
+    """The workload of that name (see CONFIGS)."""
+    for c in CONFIGS.values():
+        if c.name == name:
+            return c
+    raise KeyError(name)
+
+
+TINY = workload("tiny-token-choice-fp32")
+MIXTRAL = workload("mixtral-token-choice-bf16")
+EXPERT_CHOICE = workload("expert-choice-bf16")
+CAPACITY_ZIPF = workload("capacity-drop-zipf-bf16")
+FINE_GRAINED = workload("fine-grained-shared-bf16")
+
+
 def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
     """Round float32 to bfloat16 (nearest, ties to even); returns uint16 bit patterns.
     Inputs are finite by construction."""

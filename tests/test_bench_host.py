@@ -37,9 +37,9 @@ def test_recorded_traffic_follows_the_kernel_source(tmp_path, monkeypatch):
     assert bench.recorded_traffic("no-such-workload") is None
 
 
-@pytest.mark.parametrize("ci", [1, 4])
-def test_algorithmic_flops(ci):
-    cfg = mi.CONFIGS[ci]
+@pytest.mark.parametrize("name", ["mixtral-token-choice-bf16", "fine-grained-shared-bf16"])
+def test_algorithmic_flops(name):
+    cfg = mi.workload(name)
     w = bench.algorithmic(cfg, 1000)
     d, f, fs, T = cfg.d_model, cfg.d_ff, cfg.d_ff_shared, cfg.T
     assert w["gate_up"] == 4.0 * d * f * 1000 + 4.0 * d * fs * T

@@ -8,7 +8,7 @@ from gpu_support import dev_weights, inputs_for, run_steps, workspace
 
 pytestmark = pytest.mark.gpu
 
-CFG = mi.CONFIGS[0].with_(dtype="bf16", T=96, d_model=128, d_ff=192, d_ff_shared=64,
+CFG = mi.TINY.with_(dtype="bf16", T=96, d_model=128, d_ff=192, d_ff_shared=64,
                           bias=("normal", 0.5))
 
 

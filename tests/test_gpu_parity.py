@@ -23,7 +23,7 @@ from gpu_support import (check_y, dev_weights, host_f32, inputs_for, rel_err, ru
 
 pytestmark = pytest.mark.gpu
 
-C0 = mi.CONFIGS[0]
+C0 = mi.TINY
 SMALL = {
     "cfg0-fp32": C0,
     "ragged-bf16": C0.with_(dtype="bf16", T=300, d_model=256, d_ff=320, bias=("normal", 0.5)),
@@ -305,25 +305,27 @@ def _explained(cfg, t, l, ro, ndiff):
     return False
 
 
-FULL = [1, 2, 3, 4]
+FULL = ["mixtral-token-choice-bf16", "expert-choice-bf16", "capacity-drop-zipf-bf16",
+        "fine-grained-shared-bf16"]
 
 
-@pytest.mark.parametrize("cid", FULL)
-def test_full_size_layer(cid):
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_layer(name):
     import torch
     """The named workload at full size, in the launch configuration the bench times
     (moe_layer_forward). Checks: logits within 1e-5; with the oracle's logits fed in, every
     routing array bit-identical; y on sampled tokens within 2e-2 of the oracle for both the
     oracle-logit path and moe_layer_forward (tokens whose decisions moved across a tie
     within the logit tolerance are listed and excluded, and must be rare)."""
-    cfg = mi.CONFIGS[cid]
-    say(f"[full] cfg{cid} {cfg.name}: generating inputs")
+    cfg = mi.workload(name)
+    cid = FULL.index(name) + 1
+    say(f"[full] {name}: generating inputs")
     inp = inputs_for(cfg)
     dev = dev_weights(inp)
-    say(f"[full] cfg{cid}: oracle routing")
+    say(f"[full] {name}: oracle routing")
     l = oracle.router_logits(inp.x, inp.w_router, inp.bias)
     ro = oracle.route(cfg, logits=l)
-    say(f"[full] cfg{cid}: rows kept {int(ro['offsets'][-1])} of {cfg.T * cfg.k}")
+    say(f"[full] {name}: rows kept {int(ro['offsets'][-1])} of {cfg.T * cfg.k}")
     # 1) selection with the oracle's logits, and the rest of the layer on that routing
     steps = run_steps(cfg, dev, logits_in=l)
     _compare_routing(cfg, steps["rb"], ro, exact_logits=l)
@@ -333,13 +335,13 @@ def test_full_size_layer(cid):
     assert np.abs(g["logits"] - l).max() <= 1e-5
     d_o, d_g = _decisions(ro, cfg.T), _decisions(g, cfg.T)
     diff = [t for t in range(cfg.T) if d_o[t] != d_g[t]]
-    say(f"[full] cfg{cid}: tokens whose routing moved across a near-tie: {len(diff)}")
+    say(f"[full] {name}: tokens whose routing moved across a near-tie: {len(diff)}")
     assert len(diff) <= max(3, cfg.T // 500)
     for t in diff:
         assert _explained(cfg, t, l, ro, len(diff)), f"token {t} routing differs without a tie"
     rng = np.random.default_rng(cid)
     sample = np.unique(np.concatenate([[0, cfg.T - 1], rng.choice(cfg.T, 22, replace=False)]))
-    say(f"[full] cfg{cid}: oracle FFN on {sample.size} sampled tokens")
+    say(f"[full] {name}: oracle FFN on {sample.size} sampled tokens")
     y_ref, _ = oracle.layer_forward(inp, tokens=sample, routing=ro)
     ok = np.array([t not in diff for t in sample])
     # float32 output of the same launch: the arithmetic against the stated bar
@@ -352,7 +354,7 @@ def test_full_size_layer(cid):
     ps, gs = check_y(cfg, host_f32(steps["y"])[sample], y_ref)
     pl, gl = check_y(cfg, host_f32(y_layer)[sample][ok], y_ref[ok])
     e_round = rel_err(mi.bf16_to_f32(mi.f32_to_bf16_bits(y_ref.astype(np.float32))), y_ref)
-    say(f"[full] cfg{cid}: max|dy|/RMS per-token/global: f32 y {p32:.4f}/{g32:.4f}  bf16 y "
+    say(f"[full] {name}: max|dy|/RMS per-token/global: f32 y {p32:.4f}/{g32:.4f}  bf16 y "
         f"{pl:.4f}/{gl:.4f} (oracle-logit path {ps:.4f}/{gs:.4f}); exact answer rounded to "
         f"bf16: {e_round:.4f}")
 
@@ -362,7 +364,7 @@ def test_decode_shaped_layer(T):
     """The Mixtral-shaped layer with a decode-sized batch (T tokens, every expert's rows fit
     the skinny GEMM path): y of every token against the oracle, through moe_layer_forward
     (row gather folded into the GEMM) and through the separate steps (x_perm copied)."""
-    cfg = mi.CONFIGS[1].with_(T=T)
+    cfg = mi.MIXTRAL.with_(T=T)
     say(f"[decode] T={T}: generating inputs")
     inp = inputs_for(cfg)
     dev = dev_weights(inp)

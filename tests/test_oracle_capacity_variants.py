@@ -159,7 +159,7 @@ def test_route_with_variants_keeps_at_most_k_rows_per_token():
     T, E, k = 256, 16, 2
     l = (rng.normal(size=(T, E)) + np.linspace(2, -2, E)).astype(np.float32)
     for kw in (dict(expand_m=2, gamma=0.8), dict(cap_groups=4, gamma=0.8), dict(cap_groups=1, gamma=0.5)):
-        cfg = mi.CONFIGS[0].with_(T=T, E=E, k=k, **kw)
+        cfg = mi.TINY.with_(T=T, E=E, k=k, **kw)
         r = oracle.route(cfg, logits=l)
         per_tok = np.diff(r["tok_ptr"])
         assert per_tok.max() <= k
@@ -174,7 +174,7 @@ def test_route_with_variants_keeps_at_most_k_rows_per_token():
 
 def test_route_rejects_inconsistent_variants():
     l = np.zeros((8, 4), dtype=np.float32)
-    base = mi.CONFIGS[0].with_(T=8, E=4, k=2)
+    base = mi.TINY.with_(T=8, E=4, k=2)
     for kw in (dict(expand_m=1), dict(cap_groups=2), dict(expand_m=1, cap_groups=2, gamma=1.0),
                dict(expand_m=3, gamma=1.0), dict(cap_groups=3, gamma=1.0)):
         with pytest.raises(ValueError):

@@ -50,12 +50,12 @@ def _dense_y(inp, r):
 
 
 SMALL = [
-    mi.CONFIGS[0],
-    mi.CONFIGS[0].with_(gamma=0.75, bias=("zipf", 1.2)),
-    mi.CONFIGS[0].with_(routing="expert", T=40),
-    mi.CONFIGS[0].with_(dtype="bf16", E=16, k=4, T=48, d_model=64, d_ff=96, d_ff_shared=32,
+    mi.TINY,
+    mi.TINY.with_(gamma=0.75, bias=("zipf", 1.2)),
+    mi.TINY.with_(routing="expert", T=40),
+    mi.TINY.with_(dtype="bf16", E=16, k=4, T=48, d_model=64, d_ff=96, d_ff_shared=32,
                         gamma=1.25, bias=("normal", 1.0)),
-    mi.CONFIGS[0].with_(renorm_topk=False, k=3),
+    mi.TINY.with_(renorm_topk=False, k=3),
 ]
 
 
@@ -68,7 +68,7 @@ def test_layer_equals_dense_definition(cfg):
 
 
 def test_single_expert_is_textbook_swiglu():
-    cfg = mi.CONFIGS[0].with_(E=1, k=1)
+    cfg = mi.TINY.with_(E=1, k=1)
     inp = mi.make_inputs(cfg)
     y, r = oracle.layer_forward(inp)
     X = _t(inp.x)
@@ -79,7 +79,7 @@ def test_single_expert_is_textbook_swiglu():
 
 
 def test_linearity_in_w_down_and_zero():
-    cfg = mi.CONFIGS[0].with_(gamma=1.0)
+    cfg = mi.TINY.with_(gamma=1.0)
     inp = mi.make_inputs(cfg)
     y, _ = oracle.layer_forward(inp)
     inp.w_down = inp.w_down * np.float32(2.0)
@@ -91,7 +91,7 @@ def test_linearity_in_w_down_and_zero():
 
 
 def test_expert_relabelling_invariance():
-    cfg = mi.CONFIGS[0]
+    cfg = mi.TINY
     inp = mi.make_inputs(cfg)
     y, _ = oracle.layer_forward(inp)
     perm = np.random.default_rng(0).permutation(cfg.E)
@@ -102,7 +102,7 @@ def test_expert_relabelling_invariance():
 
 
 def test_token_permutation_equivariance():
-    cfg = mi.CONFIGS[0]
+    cfg = mi.TINY
     inp = mi.make_inputs(cfg)
     y, _ = oracle.layer_forward(inp)
     perm = np.random.default_rng(1).permutation(cfg.T)
@@ -112,7 +112,7 @@ def test_token_permutation_equivariance():
 
 
 def test_sampled_tokens_equal_full_rows():
-    cfg = mi.CONFIGS[0].with_(gamma=0.75, bias=("zipf", 1.2), d_ff_shared=64)
+    cfg = mi.TINY.with_(gamma=0.75, bias=("zipf", 1.2), d_ff_shared=64)
     inp = mi.make_inputs(cfg)
     y, r = oracle.layer_forward(inp)
     toks = np.array([0, 5, 17, 63, 31])
@@ -121,7 +121,7 @@ def test_sampled_tokens_equal_full_rows():
 
 
 def test_dropped_everywhere_gives_shared_only():
-    cfg = mi.CONFIGS[0].with_(gamma=1e-6, d_ff_shared=64)
+    cfg = mi.TINY.with_(gamma=1e-6, d_ff_shared=64)
     inp = mi.make_inputs(cfg)
     y, r = oracle.layer_forward(inp)
     assert r["C"] == 0
@@ -131,7 +131,7 @@ def test_dropped_everywhere_gives_shared_only():
 def test_logits_closed_form():
     """l = x W_r + b, one rounding of the exact product (bf16 x times fp32 W is exact in
     fp64 per term; sum of d terms in fp64 is far inside fp32 rounding)."""
-    cfg = mi.CONFIGS[1].with_(T=16, d_model=256, d_ff=64)
+    cfg = mi.MIXTRAL.with_(T=16, d_model=256, d_ff=64)
     inp = mi.make_inputs(cfg)
     l = oracle.router_logits(inp.x, inp.w_router, inp.bias)
     X = torch.from_numpy(mi.bf16_to_f32(inp.x).astype(np.float64))

@@ -143,11 +143,10 @@ def _dispatch_by_loop(pairs, T, E):
     return counts, offsets, perm_token, pos
 
 
-@pytest.mark.parametrize("cfg_id,overrides", [(0, {}), (0, dict(gamma=0.75)),
-                                               (0, dict(routing="expert")),
-                                               (0, dict(E=5, k=3, T=37, gamma=1.0))])
-def test_dispatch_is_stable_counting_sort(cfg_id, overrides):
-    cfg = mi.CONFIGS[cfg_id].with_(**overrides)
+@pytest.mark.parametrize("overrides", [{}, dict(gamma=0.75), dict(routing="expert"),
+                                       dict(E=5, k=3, T=37, gamma=1.0)])
+def test_dispatch_is_stable_counting_sort(overrides):
+    cfg = mi.TINY.with_(**overrides)
     l = mi.quantised_logits(cfg.T, cfg.E, levels=5, seed=7)
     r = oracle.route(cfg, logits=l)
     if cfg.routing == "expert":
@@ -187,7 +186,7 @@ def test_gates_closed_forms():
 
 
 def test_capacity_special_cases():
-    cfg = mi.CONFIGS[0].with_(gamma=0.0)
+    cfg = mi.TINY.with_(gamma=0.0)
     l = mi.normal_logits(cfg.T, cfg.E, seed=4, bias=np.linspace(2, -2, cfg.E).astype(np.float32))
     nodrop = oracle.route(cfg, logits=l)
     # gamma >= E/k: C >= T, identical to no drop
