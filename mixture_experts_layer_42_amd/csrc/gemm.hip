@@ -189,6 +189,12 @@ MOE_DEV void mfma_block(const bf16x8_t (&af)[MB], const bf16x8_t (&bfr)[Cfg<W>::
       acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mb], bfr[nb], acc[mb][nb], 0, 0, 0);
 }
 
+// silu(g) * u of the bf16 paths: the hardware reciprocal (about 1 ulp) instead of a
+// correctly rounded division; h is rounded to bf16 (8 significant bits) right after
+MOE_DEV float swiglu(float g, float u) {
+  return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
+}
+
 // keep the instruction order written here (no scheduling across this point)
 MOE_DEV void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
 
@@ -380,7 +386,7 @@ MOE_DEV __attribute__((always_inline)) void gemm_tile(const GemmArgs &args, cons
         if (nb < nbv) {
           if (GATE_UP) {
             const float gv = acc[mb][nb][i], uv = acc[mb][nb + OB][i];
-            const float h = gv / (1.0f + __expf(-gv)) * uv;
+            const float h = swiglu(gv, uv);
             __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(h), rs, (int)(roff + nb * 32 * CE),
                                                   0, 0);
           } else {
@@ -490,8 +496,8 @@ __global__ __launch_bounds__(256) void gemm_tail_reduce_kernel(GemmArgs args) {
         uint32_t pk[2];
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-          const float h0 = gv[2 * j] / (1.0f + __expf(-gv[2 * j])) * uv[2 * j];
-          const float h1 = gv[2 * j + 1] / (1.0f + __expf(-gv[2 * j + 1])) * uv[2 * j + 1];
+          const float h0 = swiglu(gv[2 * j], uv[2 * j]);
+          const float h1 = swiglu(gv[2 * j + 1], uv[2 * j + 1]);
           pk[j] = (uint32_t)f32_to_bf16(h0) | ((uint32_t)f32_to_bf16(h1) << 16);
         }
         *(uint2 *)((bf16_t *)d.C + (size_t)row * d.ldc + col) = make_uint2(pk[0], pk[1]);
@@ -660,7 +666,7 @@ __global__ __launch_bounds__(256, 1) void gemm_skinny_kernel(GemmArgs args) {
             const uint32_t off = ((uint32_t)row * d.ldc + col) * CE;
             if (GATE_UP) {
               const float gv = acc[m][0][i], uv = acc[m][1][i];
-              __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(gv / (1.0f + __expf(-gv)) * uv),
+              __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(swiglu(gv, uv)),
                                                     rs, (int)off, 0, 0);
             } else {
               __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[m][j][i]), rs, (int)off,
@@ -726,8 +732,8 @@ __global__ __launch_bounds__(256) void gemm_skinny_reduce_kernel(GemmArgs args) 
       uint32_t pk[2];
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        const float h0 = gv[2 * j] / (1.0f + __expf(-gv[2 * j])) * uv[2 * j];
-        const float h1 = gv[2 * j + 1] / (1.0f + __expf(-gv[2 * j + 1])) * uv[2 * j + 1];
+        const float h0 = swiglu(gv[2 * j], uv[2 * j]);
+        const float h1 = swiglu(gv[2 * j + 1], uv[2 * j + 1]);
         pk[j] = (uint32_t)f32_to_bf16(h0) | ((uint32_t)f32_to_bf16(h1) << 16);
       }
       *(uint2 *)((bf16_t *)C + c) = make_uint2(pk[0], pk[1]);
