@@ -14,13 +14,8 @@ constexpr int kWave = 64;
 
 MOE_DEV float bf16_to_f32(bf16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
 
-// round to nearest even; inputs are finite on the hot path, NaN stays NaN
-MOE_DEV bf16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16_t)((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (bf16_t)(u >> 16);
-}
+// round to nearest even (gfx950's v_cvt_pk_bf16_f32); NaN stays NaN
+MOE_DEV bf16_t f32_to_bf16(float f) { return __builtin_bit_cast(bf16_t, (__bf16)f); }
 
 template <typename T> MOE_DEV float to_f32(T v);
 template <> MOE_DEV float to_f32<float>(float v) { return v; }
