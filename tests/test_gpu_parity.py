@@ -383,3 +383,51 @@ def test_decode_shaped_layer(T):
     assert ok.sum() >= T - 1
     p32, g32 = check_y(cfg32, host_f32(y32)[ok], y_ref[ok])
     say(f"[decode] T={T}: max|dy|/RMS per-token/global {p32:.4f}/{g32:.4f}")
+
+
+# ------------------------------------------------------------------------------ random shapes
+
+def _random_problem(seed):
+    """A valid small problem drawn from every option the ABI has (seeded)."""
+    r = np.random.default_rng(1000 + seed)
+    bf16 = r.random() < 0.8
+    E = int(r.choice([1, 2, 5, 8, 9, 10, 16, 24, 33, 64, 100, 128]))
+    k = int(r.integers(1, min(E, 8) + 1))
+    T = int(r.choice([1, 2, 7, 31, 64, 65, 129, 256, 257, 333, 600]))
+    kw = dict(dtype="bf16" if bf16 else "f32", T=T, E=E, k=k,
+              d_model=int(r.choice([64, 128, 192, 256])), d_ff=int(r.choice([64, 128, 192, 320])),
+              d_ff_shared=int(r.choice([0, 0, 64])), renorm_topk=bool(r.random() < 0.8),
+              bias=[("none",), ("normal", 1.0), ("zipf", 1.2)][int(r.integers(0, 3))], seed=seed)
+    form = r.random()
+    if form < 0.2 and k * T >= E:
+        kw.update(routing="expert")
+    elif form < 0.6:
+        kw.update(gamma=float(r.choice([0.25, 0.5, 1.0, 1.25])))
+        extra = r.random()
+        if extra < 0.2 and k + 2 <= E:
+            kw.update(expand_m=int(r.integers(1, min(4, E - k) + 1)))
+        elif extra < 0.4:
+            divs = [D for D in (1, 2, 4, 8) if E % D == 0]
+            kw.update(cap_groups=int(r.choice(divs)))
+    if not bf16:
+        kw.update(y_dtype="f32")
+    return C0.with_(name=f"random-{seed}", **kw)
+
+
+@pytest.mark.parametrize("seed", range(int(__import__("os").environ.get("MOE_RANDOM_CASES", "48"))))
+def test_random_shapes(seed):
+    """Seeded random problems over the ABI's options (dtype, ragged T, 1..128 experts, k,
+    shared expert, renormalisation, biases, every selection form): routing with the oracle's
+    logits bit-identical, then the dispatch, expert FFN and combine on that routing against
+    the oracle's layer output."""
+    cfg = _random_problem(seed)
+    say(f"[random] seed {seed}: {cfg}")
+    inp = inputs_for(cfg)
+    dev = dev_weights(inp)
+    l = oracle.router_logits(inp.x, inp.w_router, inp.bias)
+    ro = oracle.route(cfg, logits=l)
+    rb, _, _ = run_route(cfg, dev, logits_in=l)
+    _compare_routing(cfg, rb, ro, exact_logits=l)
+    out = run_steps(cfg, dev, logits_in=l)
+    y_ref, _ = oracle.layer_forward(inp, routing=ro)
+    check_y(cfg, host_f32(out["y"]), y_ref)
