@@ -155,6 +155,21 @@ MOE_DEV void g2lds16(const void *g, char *lds_base) {
   __builtin_amdgcn_global_load_lds((gbl_void_t *)g, (lds_void_t *)lds_base, 16, 0, 0);
 }
 
+// The same copy through a buffer resource: lane L writes LDS bytes [lds_base + 16 L, +16)
+// from byte voff + soff of the resource (soff wave-uniform). Buffer copies count only
+// against the vector-memory counter, while global copies into LDS also count as LDS events
+// for the compiler's wait insertion, which then has to wait for every outstanding LDS read
+// (lgkmcnt(0)) before each MFMA sub-step instead of only the fragments that sub-step needs.
+MOE_DEV void b2lds16(__amdgpu_buffer_rsrc_t r, uint32_t voff, int soff, char *lds_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t *)lds_base, 16, (int)voff, soff, 0, 0);
+}
+
+// Buffer resource over an operand with the whole 32-bit byte range (operand byte offsets
+// stay below 4 GiB: the entry points reject larger panels).
+MOE_DEV __amdgpu_buffer_rsrc_t operand_rsrc(const void *p) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, -1, 0x00020000);
+}
+
 // The pipeline stages are separate LDS objects, so loads into one stage are never mistaken
 // for writes to the stage being read.
 struct Stage { char a[BM * kRowBytes]; char b[BN * kRowBytes]; };
@@ -170,13 +185,18 @@ template <int W, int MB>
 MOE_DEV void load_frags(const Stage &st, int lane, int wm, int wn, int ks, bf16x8_t (&af)[MB],
                         bf16x8_t (&bfr)[Cfg<W>::NB]) {
   const int chunk = ks * 2 + (lane >> 5);
+  // in the order the MFMAs (mb outer, nb inner) consume them: A0, every B, then A1 ..
+  // so that the first MFMAs of the sub-step wait only for the reads issued first
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb)
+  for (int mb = 0; mb < MB; ++mb) {
     af[mb] = *reinterpret_cast<const bf16x8_t *>(st.a + swz(wm * 32 * MB + mb * 32 + (lane & 31), chunk));
+    if (mb == 0) {
 #pragma unroll
-  for (int nb = 0; nb < Cfg<W>::NB; ++nb)
-    bfr[nb] = *reinterpret_cast<const bf16x8_t *>(
-        st.b + swz(wn * Cfg<W>::WCOLS + nb * 32 + (lane & 31), chunk));
+      for (int nb = 0; nb < Cfg<W>::NB; ++nb)
+        bfr[nb] = *reinterpret_cast<const bf16x8_t *>(
+            st.b + swz(wn * Cfg<W>::WCOLS + nb * 32 + (lane & 31), chunk));
+    }
+  }
 }
 
 template <int W, int MB>
@@ -285,13 +305,13 @@ MOE_DEV __attribute__((always_inline)) void gemm_tile(const GemmArgs &args, cons
     boff[i] = ((uint32_t)min(n, d.N - 1) * (uint32_t)d.K + c * 8) * 2u;
   }
   const int aofs = wvu * A_DMA * 1024, bofs = wvu * C::B_DMA * 1024;
+  const __amdgpu_buffer_rsrc_t ra = operand_rsrc(Ab), rb = operand_rsrc(Bb);
   auto issue = [&](Stage &s, int kt) {
-    const char *a = Ab + (size_t)(k_begin + kt) * kRowBytes;
-    const char *b = Bb + (size_t)(k_begin + kt) * kRowBytes;
+    const int so = (k_begin + kt) * kRowBytes;   // K offset of the slice, bytes
 #pragma unroll
-    for (int i = 0; i < A_DMA; ++i) g2lds16(a + aoff[i], s.a + aofs + i * 1024);
+    for (int i = 0; i < A_DMA; ++i) b2lds16(ra, aoff[i], so, s.a + aofs + i * 1024);
 #pragma unroll
-    for (int i = 0; i < C::B_DMA; ++i) g2lds16(b + boff[i], s.b + bofs + i * 1024);
+    for (int i = 0; i < C::B_DMA; ++i) b2lds16(rb, boff[i], so, s.b + bofs + i * 1024);
   };
   f32x16_t acc[MB][NB];
 #pragma unroll
