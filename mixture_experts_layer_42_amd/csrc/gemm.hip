@@ -12,7 +12,7 @@
 // slices of 64 through two 64 KB LDS stages (one lands while the other feeds the MFMAs).
 // Waves (4 as 2 x 2 of 128 x 128, or 8 as 2 x 4 of 128 x 64) compute with
 // v_mfma_f32_32x32x16_bf16 into float32 accumulators. Slices are copied from global memory
-// straight into LDS (gfx950 global_load_lds, no register staging); each 1 KB copy covers 8
+// straight into LDS (gfx950 buffer loads into LDS, no register staging); each 1 KB copy covers 8
 // rows x 128 B, i.e. whole 128-byte lines, which streams about twice as fast as half-line
 // rows. 16-byte chunks are XOR-swizzled by row so the MFMA fragment reads hit distinct banks.
 // Tiles of one expert that share a weight column are consecutive in the tile list, and
