@@ -8,7 +8,7 @@
 //
 // bf16 path: persistent workgroups walk a tile list built on the device from the
 // per-expert row counts (no host round trip). A tile is 256 rows x 256 columns (a group's
-// last row tile shrinks to 64 or 128 rows when that covers its remaining rows); K goes in
+// last row tile shrinks to 64, 128 or 192 rows when that covers its remaining rows); K goes in
 // slices of 64 through two 64 KB LDS stages (one lands while the other feeds the MFMAs).
 // Waves (4 as 2 x 2 of 128 x 128, or 8 as 2 x 4 of 128 x 64) compute with
 // v_mfma_f32_32x32x16_bf16 into float32 accumulators. Slices are copied from global memory
@@ -175,10 +175,10 @@ MOE_DEV __amdgpu_buffer_rsrc_t operand_rsrc(const void *p) {
 struct Stage { char a[BM * kRowBytes]; char b[BN * kRowBytes]; };
 
 // Row tiles. A group's rows go in tiles of 256; its last tile, holding rem = rows - m0 rows,
-// shrinks to 64 * MB rows with MB = 1 (rem <= 64), 2 (rem <= 128) or 4, so a ragged group
-// end costs MFMAs for at most 63 padding rows instead of up to 255. Wave row wm of a tile
-// owns rows wm * 32 MB .. + 32 MB - 1 as MB blocks of 32.
-MOE_DEV int tile_mb(int rem) { return rem > 128 ? 4 : (rem > 64 ? 2 : 1); }
+// shrinks to 64 * MB rows with MB = 1 (rem <= 64), 2 (rem <= 128), 3 (rem <= 192) or 4, so a
+// ragged group end costs MFMAs for at most 63 padding rows instead of up to 255. Wave row wm
+// of a tile owns rows wm * 32 MB .. + 32 MB - 1 as MB blocks of 32.
+MOE_DEV int tile_mb(int rem) { return rem > 192 ? 4 : (rem > 128 ? 3 : (rem > 64 ? 2 : 1)); }
 
 // fragments of sub-step ks (k = 16 ks .. 16 ks + 15 of the slice)
 template <int W, int MB>
@@ -453,6 +453,7 @@ __global__ __launch_bounds__(64 * W, 1) void gemm_bf16_kernel(GemmArgs args) {
     const int punit = nparts > 1 ? u - sp.full : -1;
     switch (tile_mb(d.rows - m0)) {
       case 4: gemm_tile<GATE_UP, W, 4>(args, d, st0, st1, n_tile, m0, nk, k_begin, punit); break;
+      case 3: gemm_tile<GATE_UP, W, 3>(args, d, st0, st1, n_tile, m0, nk, k_begin, punit); break;
       case 2: gemm_tile<GATE_UP, W, 2>(args, d, st0, st1, n_tile, m0, nk, k_begin, punit); break;
       default: gemm_tile<GATE_UP, W, 1>(args, d, st0, st1, n_tile, m0, nk, k_begin, punit); break;
     }
