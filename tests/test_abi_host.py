@@ -79,6 +79,12 @@ def ws_status(p):
     # one expert's float32 GEMM output (up to T rows of d_model) must stay under 4 GiB
     (dict(T=1 << 18, d_model=4096, k=1), moe.MOE_ERR_UNSUPPORTED),
     (dict(T=(1 << 18) - 64, d_model=4096, k=1), moe.MOE_OK),
+    # the GEMMs address an operand panel (one expert's weights, the routed rows' activations)
+    # with 32-bit byte offsets: each must hold fewer than 2^31 elements
+    (dict(d_model=32768, d_ff=65536), moe.MOE_ERR_UNSUPPORTED),
+    (dict(d_model=32768, d_ff=65472), moe.MOE_OK),
+    (dict(T=1 << 17, k=8, d_model=2048, d_ff=2048), moe.MOE_ERR_UNSUPPORTED),
+    (dict(T=1 << 17, k=8, d_model=1984, d_ff=1984), moe.MOE_OK),
 ])
 def test_problem_validation(kw, status):
     st, n = ws_status(good(**kw))
