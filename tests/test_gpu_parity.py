@@ -359,6 +359,40 @@ def test_full_size_layer(name):
         f"bf16: {e_round:.4f}")
 
 
+def test_operand_offsets_past_2gib():
+    """A layer whose down-GEMM activation panel (h: T k = 524288 rows x d_ff = 3072 bf16,
+    3.2 GB) reaches past 2 GiB, so the GEMM's 32-bit operand offsets exceed 2^31 and must be
+    taken as unsigned. Logits within 1e-5; y (float32 output) on sampled tokens, which include
+    rows beyond the 2 GiB mark, within the bar; tokens whose decisions moved across a near-tie
+    are excluded and must be rare."""
+    cfg = C0.with_(name="offsets-past-2gib", dtype="bf16", y_dtype="f32", T=65536, d_model=64,
+                   E=16, k=8, d_ff=3072, d_ff_shared=0, bias=("none",), seed=7)
+    say("[big] generating inputs")
+    inp = inputs_for(cfg)
+    dev = dev_weights(inp)
+    l = oracle.router_logits(inp.x, inp.w_router, inp.bias)
+    ro = oracle.route(cfg, logits=l)
+    say("[big] moe_layer_forward")
+    y32, rb = run_layer(cfg, dev)
+    g = rb.host()
+    assert np.abs(g["logits"] - l).max() <= 1e-5
+    d_o, d_g = _decisions(ro, cfg.T), _decisions(g, cfg.T)
+    diff = {t for t in range(cfg.T) if d_o[t] != d_g[t]}
+    assert len(diff) <= cfg.T // 500
+    rng = np.random.default_rng(11)
+    sample = np.array(sorted({0, cfg.T - 1} | set(rng.choice(cfg.T, 30, replace=False).tolist())
+                             - diff))
+    # rows past 2 GiB of h: some sampled token must own one
+    first_far = (1 << 31) // (cfg.d_ff * 2) + 1
+    pos = ro["tok_pos"]
+    owned = [pos[ro["tok_ptr"][t]:ro["tok_ptr"][t + 1]] for t in sample]
+    assert any((p >= first_far).any() for p in owned)
+    say(f"[big] oracle FFN on {sample.size} sampled tokens")
+    y_ref, _ = oracle.layer_forward(inp, tokens=sample, routing=ro)
+    p32, g32 = check_y(cfg, host_f32(y32)[sample], y_ref)
+    say(f"[big] max|dy|/RMS per-token/global {p32:.4f}/{g32:.4f}")
+
+
 @pytest.mark.parametrize("T", [1, 8, 64])
 def test_decode_shaped_layer(T):
     """The Mixtral-shaped layer with a decode-sized batch (T tokens, every expert's rows fit
