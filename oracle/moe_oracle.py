@@ -24,7 +24,10 @@ is a fixed float32 encoding (the routing-score spec below). Steps:
      expert choice  each expert keeps the c = floor(k*T/E) tokens with the
                     largest logit in its column (ties: lower token first);
                     weight = softmax over the T tokens of that column
-                    (hrletsgo page, Mixture-of-Tokens section)
+                    (hrletsgo page, Mixture-of-Tokens section). Parity
+                    unpinned for this weight: no page fixes the softmax axis,
+                    so it rests on the workload's wording; the selection
+                    itself is pinned against brute-force subsets
      capacity drop  after token choice, an expert with more than
                     C = floor(gamma * T*k/E) candidates keeps the C with the
                     highest routing score p32 (ties: lower token first); dropped
