@@ -222,15 +222,20 @@ moe_status moe_layer_forward_traced(const moe_problem *problem, const void *x,
                                     void *y, moe_routing *routing, void *ws, size_t ws_bytes,
                                     hipStream_t stream, hipEvent_t *events, int n_events);
 
-/* Expert-utilisation statistics of a routing result (hrletsgo page: the Switch
- * balance term sums f_i * P_i; gillilab page: the utilisation distribution is the
- * leading indicator of routing collapse). out [2*E + 4] float32 on the device:
+/* Expert-utilisation statistics of a routing result (hrletsgo page "MoE vs MoT routing
+ * inference cost", section on the basic MoE structure, load-imbalance paragraph: the
+ * balance term is the sum over experts of f_i, the share of tokens expert i received,
+ * times P_i, its router probability; gillilab page on active parameters, routing section:
+ * the utilisation distribution is the leading indicator of routing collapse).
+ * Reads routing->logits, counts, offsets (as moe_route left them). out [2*E + 4] float32
+ * on the device, written in one pass of two small kernels on `stream`:
  *   out[0..E)     f_i = counts[i] / offsets[E]        (0 if no rows)
  *   out[E..2E)    P_i = mean over tokens of softmax_E(logits)[t, i]
- *   out[2E]       E * sum_i f_i P_i
+ *   out[2E]       sum_i f_i P_i  (no scale factor: uniform routing gives 1/E)
  *   out[2E+1]     max_i counts[i] / (offsets[E] / E)  (0 if no rows)
  *   out[2E+2]     assignments dropped by capacity (T*k - offsets[E] for token choice, else 0)
- *   out[2E+3]     number of experts with no rows */
+ *   out[2E+3]     number of experts with no rows
+ * Uses the workspace's statistics region; errors as for every entry point. */
 moe_status moe_routing_stats(const moe_problem *problem, const moe_routing *routing, float *out,
                              void *ws, size_t ws_bytes, hipStream_t stream);
 

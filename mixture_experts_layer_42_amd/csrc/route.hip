@@ -1323,7 +1323,7 @@ __global__ __launch_bounds__(1024) void stats_final_kernel(const float *__restri
   mxc = block_max(mxc, fsm);
   empty = block_sum(empty, fsm);
   if (threadIdx.x == 0) {
-    out[2 * E] = (float)E * fp;
+    out[2 * E] = fp;   // sum_i f_i P_i, unscaled
     out[2 * E + 1] = rows > 0 ? mxc / ((float)rows / (float)E) : 0.f;
     out[2 * E + 2] = token_choice ? (float)(T * k - rows) : 0.f;
     out[2 * E + 3] = empty;

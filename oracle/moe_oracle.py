@@ -69,14 +69,19 @@ evaluated as 1 + (r + r*(r*P(r))) with P(r) = 1/2! + r/3! + ... + r^5/7! in Horn
 form (adding the 1 last keeps the result monotone in x), then scaling by 2**n
 built in the exponent field; rexp(x) = +0 for x < -87.
 
-Pins (tests/test_oracle_*.py): hand-derived examples (tests/golden/), brute-force
+Pins (tests/test_oracle_*.py): hand-derived examples (tests/golden/) for every selection
+form and for router_logits (integer products, the bfloat16 widening, one rounding of the
+exact sum), routing_stats, combine, expert_rows_ffn and shared_expert; brute-force
 enumeration for every selection form (subset dominance for the group capacity), the
 reductions of the capacity variants to the token drop (m = 0; groups of one expert),
 a dense evaluation of the definition, closed forms (k = E gives the plain
 softmax mixture; E = k = 1 gives a textbook SwiGLU FFN through torch.nn.functional),
 invariants fixed by the pages (exactly k per token, exactly c per expert,
-no expert above C, dropped pairs never outrank kept ones), and an exhaustive
-check of rexp against the float64 exponential over every float32 in [-87, 0].
+no expert above C, dropped pairs never outrank kept ones), agreement of the per-row
+route (expert_rows_ffn + combine) with the per-token one (layer_forward), and an
+exhaustive check of rexp against the float64 exponential over every float32 in [-87, 0].
+Parity unpinned: the expert-choice combine weight's axis (see above) and the Zipf bias
+mapping of the skewed workload, which rests on its stated ~40% share only.
 """
 from __future__ import annotations
 
@@ -455,15 +460,28 @@ def shared_expert(inp, tokens: Optional[np.ndarray] = None) -> np.ndarray:
 
 
 def routing_stats(routing: dict, E: int, T: int, k: int) -> dict:
-    """Expert-utilisation statistics: f_i (fraction of kept assignments per expert),
-    P_i (mean router probability per expert), the Switch balance term E*sum f_i P_i,
-    max/mean load and drop fraction (hrletsgo page: the auxiliary balance loss is the
-    sum of f_i times P_i; routing/active-parameter page: the utilisation distribution is
-    the leading indicator of routing collapse)."""
+    """Expert-utilisation statistics of one routing result.
+
+    f_i      share of the kept (token, expert) assignments that expert i received
+             (0 for every expert when nothing was kept)
+    P_i      router probability of expert i, averaged over all T tokens: the mean of
+             softmax_E(logits)[t, i]
+    balance  sum_i f_i * P_i, the load-balancing term as the hrletsgo page states it
+             ("MoE vs MoT routing inference cost", section on the basic MoE structure,
+             load-imbalance paragraph: the sum over experts of f_i times P_i is added
+             to the loss). The page gives no scale factor, so none is applied; uniform
+             routing gives 1/E
+    max_over_mean  largest expert load over the mean load (rows / E); 0 with no rows
+    dropped  assignments removed by a capacity limit (T*k - rows for token choice, 0 for
+             expert choice)
+    empty    experts that received no rows
+    The gillilab page (routing section) treats the utilisation distribution as the
+    leading indicator of routing collapse; these are its summary numbers."""
     counts = routing["counts"].astype(np.float64)
     total = counts.sum()
     f = counts / total if total > 0 else np.zeros(E)
     P = softmax_rows(routing["logits"]).mean(axis=0)
-    return dict(f=f, P=P, balance=float(E * np.sum(f * P)),
+    return dict(f=f, P=P, balance=float(np.sum(f * P)),
                 max_over_mean=float(counts.max() / (total / E)) if total > 0 else 0.0,
-                dropped=int(T * k - total) if "kept" in routing else 0)
+                dropped=int(T * k - total) if "kept" in routing else 0,
+                empty=int(np.count_nonzero(counts == 0)))
