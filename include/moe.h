@@ -40,19 +40,28 @@
  *    device memory per GPU, so debug-mode calls on one GPU must not overlap.
  *  - Row capacity R = T*k rows suffices for every selection form; buffers sized
  *    "[R, ...]" are indexed by dispatched row.
- *  - Errors: arguments are checked on the host BEFORE anything is enqueued; on
- *    any error nothing is enqueued and the outputs are untouched.
+ *  - Errors: arguments are checked on the host BEFORE anything is enqueued. On
+ *    MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED and MOE_ERR_WORKSPACE nothing of the call
+ *    is enqueued and the outputs are untouched (in debug mode the input scans above are
+ *    enqueued and synchronised first; a NaN or infinity they find is reported as
+ *    MOE_ERR_INVALID_ARG before any kernel of the layer is enqueued).
  *      MOE_ERR_INVALID_ARG  bad shape (T, d_model, E, k, d_ff < 1; k > E;
  *                           expert choice with k*T < E or gamma > 0; y_dtype
  *                           bf16 with dtype f32), a NULL
  *                           required pointer, a pointer not 16-byte aligned,
  *                           unknown enum value
  *      MOE_ERR_UNSUPPORTED  valid but without a kernel: bf16 with d_model or d_ff
- *                           (or d_ff_shared) not a multiple of 64
+ *                           (or d_ff_shared) not a multiple of 64; E > 1024; operand
+ *                           or output panels past the GEMMs' 32-bit byte offsets
  *      MOE_ERR_WORKSPACE    ws_bytes below moe_workspace_bytes(problem)
- *      MOE_ERR_HIP          a HIP launch failed (the HIP error is not cleared)
+ *      MOE_ERR_HIP          a HIP launch failed (the HIP error is not cleared). This one
+ *                           can come after earlier kernels of the same call were
+ *                           enqueued: the call's outputs are then unspecified.
  *    Device faults surface at the caller's next synchronisation. Inputs must be
- *    finite; NaN/Inf in x or weights is not detected.
+ *    finite; NaN/Inf in x or weights is not detected outside debug mode.
+ *  - Environment: MOE_GRID_CUS (read at every call) caps the persistent grids at that
+ *    many workgroups; no result depends on it (every K split and every sum order is
+ *    fixed independently of the grid).
  */
 #ifndef MOE_MI355X_H
 #define MOE_MI355X_H
@@ -147,51 +156,77 @@ typedef struct {
   int32_t *tok_ptr, *tok_pos;
 } moe_routing;
 
-/* Bytes of device workspace every entry point below needs for `problem`
- * (one size for all of them; 256-byte aligned regions inside). */
+/* Bytes of device workspace every entry point below needs for `problem` (one size for all
+ * of them; 256-byte aligned regions inside). This is the library's own convention, not an
+ * operation of the pages. Validates `problem` exactly as the compute calls do; writes
+ * *bytes only on MOE_OK. Host only, enqueues nothing. */
 moe_status moe_workspace_bytes(const moe_problem *problem, size_t *bytes);
 
-/* Router + selection + dispatch indices (steps: logits = x W_r + b; softmax scores;
- * one selection rule; per-expert histogram, prefix scan and stable permutation).
- * x [T, d_model]. Fills every non-NULL field of `routing` (logits too unless
- * MOE_ROUTE_LOGITS_IN). Routing decisions depend only on the float32 logits and are
- * reproducible bit for bit; the capacity drop ranks pairs by a fixed float32
- * encoding of the softmax probability (Cody-Waite exponential, left-to-right sum
- * over experts, IEEE division). */
+/* Router + selection + dispatch indices. Steps and the passages that define them:
+ *   logits = x W_r + b: the router scores every token for every expert (dongbusteel page,
+ *     section on the roles of the expert and the router);
+ *   softmax scores: the router probability P_i (hrletsgo page "MoE vs MoT routing inference
+ *     cost", section on the basic MoE structure);
+ *   one selection rule (see moe_routing_kind): TopK(G(x), k) (dongbusteel page, same
+ *     section), expert choice with c = k T / N (hrletsgo page, Mixture-of-Tokens part of the
+ *     basic-structure section), capacity C = gamma N-bar with the lowest gating scores
+ *     dropped, Expanded Drop and device-level capacity (gist.science summary of
+ *     "Capacity-Aware Inference", section 2 Methodology, items 1-3);
+ *   per-expert histogram, prefix scan and stable permutation: the dispatch that sends each
+ *     token to its experts (hrletsgo page, basic-structure section, the dispatch step).
+ * x [T, d_model] (dtype), w_router [d_model, E] float32, bias [E] float32 or NULL (x,
+ * w_router and bias are not read with MOE_ROUTE_LOGITS_IN and may be NULL then).
+ * flags: 0 or MOE_ROUTE_LOGITS_IN. Fills every non-NULL field of `routing` (logits too
+ * unless MOE_ROUTE_LOGITS_IN). Routing decisions depend only on the float32 logits and are
+ * reproducible bit for bit; the capacity drop ranks pairs by a fixed float32 encoding of
+ * the softmax probability (Cody-Waite exponential, left-to-right sum over experts, IEEE
+ * division). Uses the routing scratch of `ws`. */
 moe_status moe_route(const moe_problem *problem, const void *x, const float *w_router,
                      const float *bias, int flags, moe_routing *routing, void *ws,
                      size_t ws_bytes, hipStream_t stream);
 
-/* Row gather of the dispatch: x_perm[p] = x[perm_token[p]] for p < offsets[E]
- * (hrletsgo page: the dispatch step that sends tokens to their experts).
- * x [T, d_model], x_perm [R, d_model]. */
+/* Row gather of the dispatch: x_perm[p] = x[perm_token[p]] for p < offsets[E] (hrletsgo
+ * page, basic-structure section: the dispatch that moves each token to its experts;
+ * devcy0922 page "Ugh, bandwidth", section on MoE not being a light dense model: token and
+ * activation movement to the selected experts). x [T, d_model], x_perm [R, d_model], both
+ * of the problem dtype; reads routing->perm_token and routing->offsets (as moe_route left
+ * them). Needs no workspace, so it takes none. Rows p >= offsets[E] of x_perm are left
+ * untouched. The layer path (moe_layer_forward) folds this gather into the gate/up GEMM's
+ * operand loads instead. */
 moe_status moe_dispatch(const moe_problem *problem, const void *x, const moe_routing *routing,
                         void *x_perm, hipStream_t stream);
 
-/* Expert SwiGLU FFN as a grouped GEMM over the dispatched rows:
+/* Expert SwiGLU FFN as a grouped GEMM over the dispatched rows (hrletsgo page, basic-structure
+ * section: the layer holds N copies of the FFN and each token passes through the ones it
+ * was routed to; gillilab page on active parameters, section on how routing allocates the
+ * compute budget: a shared expert that every token passes through):
  *   o_perm[p] = W_down_e ( silu(W_gate_e x_perm[p]) * (W_up_e x_perm[p]) ),  e = expert of row p
  * plus, when d_ff_shared > 0, the shared expert over all T tokens of x:
  *   o_shared[t] = Ws_down ( silu(Ws_gate x[t]) * (Ws_up x[t]) ).
  * The hidden activation is rounded to the problem dtype between the two GEMMs;
  * accumulation is float32. x_perm [R, d_model] (dtype), o_perm [R, d_model] float32;
  * x [T, d_model] (dtype), o_shared [T, d_model] float32
- * (x, ws_* and o_shared may be NULL without a shared expert). */
+ * (x, ws_* and o_shared may be NULL without a shared expert). Reads routing->counts and
+ * routing->offsets; uses the h and partial-sum regions of `ws`. */
 moe_status moe_expert_ffn(const moe_problem *problem, const void *x_perm,
                           const moe_routing *routing, const void *w_gate, const void *w_up,
                           const void *w_down, const void *x, const void *ws_gate,
                           const void *ws_up, const void *ws_down, void *o_perm, void *o_shared,
                           void *ws, size_t ws_bytes, hipStream_t stream);
 
-/* Gate-weighted combine back to token order (dongbusteel page, the weighted sum):
+/* Gate-weighted combine back to token order (dongbusteel page, section on how MoE differs
+ * from the Transformer: y = sum_i G(x)_i E_i(x), the gate-weighted sum of expert outputs):
  *   y[t] = sum over rows p of token t of perm_w[p] * o_perm[p]  (+ o_shared[t])
  * summed in float32 in CSR order; a token without rows gets 0 (+ o_shared[t]).
  * o_perm, o_shared float32; y [T, d_model] in problem.y_dtype (one rounding, to nearest
- * even, for bf16). */
+ * even, for bf16). Reads routing->tok_ptr, tok_pos and perm_w; needs no workspace. */
 moe_status moe_combine(const moe_problem *problem, const void *o_perm, const void *o_shared,
                        const moe_routing *routing, void *y, hipStream_t stream);
 
-/* The whole layer: the results of moe_route, moe_dispatch, moe_expert_ffn and moe_combine,
- * on `stream`. The dispatch row gather is folded into the gate/up GEMM's operand loads
+/* The whole layer, y = sum_i G(x)_i E_i(x) (dongbusteel page, section on how MoE differs
+ * from the Transformer), as the pages' per-token path token -> router -> selected experts
+ * -> combine (devcy0922 page, section on MoE not being a light dense model): the results
+ * of moe_route, moe_dispatch, moe_expert_ffn and moe_combine, on `stream`. The dispatch row gather is folded into the gate/up GEMM's operand loads
  * (routed row p is read as x[perm_token[p]]), so no x_perm is materialised; the output is
  * bit-identical to the four separate calls. routing may be NULL (then the routing arrays
  * live inside the workspace). */
@@ -212,9 +247,10 @@ enum {
   MOE_STAGE_COUNT = 5
 };
 
-/* moe_layer_forward with stage timing for measurement: the same kernels in the same
- * order, plus hipEventRecord(events[i], stream) at each stage boundary.
- * n_events must be MOE_STAGE_COUNT + 1; events are created by the caller. */
+/* moe_layer_forward with stage timing for measurement (the same passages): the same kernels
+ * in the same order, plus hipEventRecord(events[i], stream) at each stage boundary.
+ * n_events must be MOE_STAGE_COUNT + 1; events are created and owned by the caller
+ * (MOE_ERR_INVALID_ARG for a NULL array or event). */
 moe_status moe_layer_forward_traced(const moe_problem *problem, const void *x,
                                     const float *w_router, const float *bias,
                                     const void *w_gate, const void *w_up, const void *w_down,

@@ -19,6 +19,7 @@ CSRC = os.path.join(PKG, "csrc")
 ROOT = os.path.dirname(PKG)
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmoe.so")
+PEAK_LIB = os.path.join(PKG, "libmoe_peak.so")
 ARCH = os.environ.get("MOE_OFFLOAD_ARCH", "gfx950")
 
 UNITS = {
@@ -28,6 +29,7 @@ UNITS = {
     "moe_api.cpp": [],
     "debug.hip": [],
 }
+PEAK_UNITS = {"peak.hip": []}
 
 
 def hipcc() -> str:
@@ -55,19 +57,27 @@ def _compile(unit, extra, verbose):
     return obj
 
 
-def build_library(verbose: bool = False) -> str:
-    """Compile every unit and link libmoe.so next to this file. Always rebuilds."""
-    os.makedirs(BUILD, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=len(UNITS)) as ex:
-        objs = list(ex.map(lambda kv: _compile(kv[0], kv[1], verbose), UNITS.items()))
-    tmp = LIB + ".tmp"
+def _link(objs, lib, verbose):
+    tmp = lib + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
-        raise RuntimeError(f"linking libmoe.so failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+        raise RuntimeError(f"linking {os.path.basename(lib)} failed:\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, lib)
+
+
+def build_library(verbose: bool = False) -> str:
+    """Compile every unit and link libmoe.so (the layer) and libmoe_peak.so (the
+    achievable-peak microbenchmarks the bench reports) next to this file. Always rebuilds."""
+    os.makedirs(BUILD, exist_ok=True)
+    units = dict(UNITS)
+    units.update(PEAK_UNITS)
+    with ThreadPoolExecutor(max_workers=len(units)) as ex:
+        objs = dict(zip(units, ex.map(lambda kv: _compile(kv[0], kv[1], verbose), units.items())))
+    _link([objs[u] for u in UNITS], LIB, verbose)
+    _link([objs[u] for u in PEAK_UNITS], PEAK_LIB, verbose)
     return LIB
 
 

@@ -105,7 +105,9 @@ MOE_DEV int xcd_virtual_block() {
 // rounds) run whole; if the remaining L tiles fill at most half a round, each is cut into S
 // K-parts (S a power of two, S*L <= P, S <= 8, each part at least 4 K-slices) so that the
 // last round takes about 1/S of a tile's time. Both the GEMM and the reduction kernel derive
-// the same plan from the device-side tile count.
+// the same plan from the device-side tile count. P is always kMaxPersistent (one workgroup
+// per CU of a full MI355X), whatever grid actually runs: which tiles are split, and so the
+// order of every float32 sum, does not depend on how many CUs the launch gets.
 struct SplitPlan { int full, L, S; };
 
 MOE_DEV SplitPlan split_plan(int total, int P, int nk, int ok) {
@@ -433,7 +435,7 @@ __global__ __launch_bounds__(64 * W, 1) void gemm_bf16_kernel(GemmArgs args) {
   const int G = build_tile_table<BM, BNOUT>(args, tstart, sm);
   const int total = tstart[G];
 
-  const SplitPlan sp = split_plan(total, gridDim.x, args.K / BK, args.split_ok);
+  const SplitPlan sp = split_plan(total, kMaxPersistent, args.K / BK, args.split_ok);
   const int units = sp.full + sp.L * sp.S;
   for (int u = xcd_virtual_block(); u < units; u += gridDim.x) {
     int tile = u, part = 0, nparts = 1;
@@ -462,8 +464,8 @@ __global__ __launch_bounds__(64 * W, 1) void gemm_bf16_kernel(GemmArgs args) {
 
 // Sum of the K-parts of split tiles, in part order, then the same epilogue as a whole tile.
 // Work item: 32 rows of one split tile; each thread owns 4 adjacent output columns of a row
-// (all S part loads issued before the sums). The plan is derived from the GEMM's grid size
-// (args.grid), so any grid of this kernel sees the same split.
+// (all S part loads issued before the sums). The plan is the GEMM's (same tile count, same P),
+// so any grid of this kernel sees the same split.
 constexpr int kReduceRows = 32;
 
 template <bool GATE_UP, int W>
@@ -476,7 +478,7 @@ __global__ __launch_bounds__(256) void gemm_tail_reduce_kernel(GemmArgs args) {
   __shared__ int tstart[kMaxGroups + 1];
   __shared__ int sm[kMaxWaves + 1];
   const int G = build_tile_table<BM, BNOUT>(args, tstart, sm);
-  const SplitPlan sp = split_plan(tstart[G], args.grid, args.K / BK, args.split_ok);
+  const SplitPlan sp = split_plan(tstart[G], kMaxPersistent, args.K / BK, args.split_ok);
   const int items = sp.L * (BM / kReduceRows);
   for (int it = blockIdx.x; it < items; it += gridDim.x) {
     const int l = it / (BM / kReduceRows), r0 = (it % (BM / kReduceRows)) * kReduceRows;
@@ -864,8 +866,9 @@ hipError_t launch_bf16(const GemmArgs &a0, bool gate_up, int max_rows, int num_c
   if (grid < 1) grid = 1;
   a.grid = grid;
   if (!a.partials) a.split_ok = 0;
-  // at most grid/2 split tiles, BM/kReduceRows reduction items each
-  const int rgrid = grid * (BM / kReduceRows) / 2 + 1;
+  // at most kMaxPersistent/2 split tiles, BM/kReduceRows reduction items each
+  int rgrid = kMaxPersistent * (BM / kReduceRows) / 2 + 1;
+  if (rgrid > 4 * num_cu) rgrid = 4 * num_cu;
   if (gate_up) {
     hipLaunchKernelGGL((gemm_bf16_kernel<true, W>), dim3(grid), dim3(64 * W), 0, st, a);
     if (a.split_ok)

@@ -4,6 +4,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <cstdlib>
 #include <initializer_list>
 #include <mutex>
 
@@ -155,9 +156,17 @@ moe_status check_problem(const moe_problem *pp) {
   const int64_t smax = (int64_t)p.T * (p.d_model > p.d_ff_shared ? p.d_model : p.d_ff_shared);
   if (wmax >= big || amax >= big || smax >= big) return MOE_ERR_UNSUPPORTED;
   // the bf16 GEMM stores one group's output rows (at most T of them) through a buffer
-  // resource with a 32-bit byte range: T * d_model float32 outputs must stay under 4 GiB
-  if (p.dtype == MOE_BF16 && (int64_t)p.T * p.d_model * 4 >= ((int64_t)1 << 32))
-    return MOE_ERR_UNSUPPORTED;
+  // resource with a 32-bit byte range, at byte offsets computed in 32 bits for every row of
+  // the group's last row tile, including up to 255 padding rows past its end: an offset
+  // that wrapped past 2^32 would land back inside the range. So (T + 256) rows of every
+  // output panel (o and o_shared: d_model float32; h and h_shared: d_ff or d_ff_shared bf16)
+  // must stay under 4 GiB.
+  if (p.dtype == MOE_BF16) {
+    int64_t row_bytes = (int64_t)p.d_model * 4;
+    if ((int64_t)p.d_ff * 2 > row_bytes) row_bytes = (int64_t)p.d_ff * 2;
+    if ((int64_t)p.d_ff_shared * 2 > row_bytes) row_bytes = (int64_t)p.d_ff_shared * 2;
+    if (((int64_t)p.T + 256) * row_bytes >= ((int64_t)1 << 32)) return MOE_ERR_UNSUPPORTED;
+  }
   return MOE_OK;
 }
 
@@ -180,11 +189,21 @@ moe_status check_routing_out(const moe_problem &p, const moe_routing *r) {
   return MOE_OK;
 }
 
+// Compute units the persistent grids may fill: the device's count, or fewer when the
+// environment variable MOE_GRID_CUS (read at every call) asks for fewer. No result depends on
+// it (the GEMMs' K-split plan is fixed independently of the grid); the determinism tests use it
+// to run the same problem under different launch shapes.
 int num_cus() {
   int dev = 0, n = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return 256;
-  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
-    return 256;
+  if (hipGetDevice(&dev) != hipSuccess) n = 256;
+  else if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+           n < 1)
+    n = 256;
+  const char *cap = std::getenv("MOE_GRID_CUS");
+  if (cap && *cap) {
+    const int v = std::atoi(cap);
+    if (v >= 1 && v < n) n = v;
+  }
   return n;
 }
 
@@ -235,16 +254,24 @@ moe_routing internal_routing(const Layout &L, char *ws) {
   return r;
 }
 
+// floor(gamma * mean), computed in double and clamped to T*k before the conversion to int: no
+// expert or group can have more candidates than T*k, so a larger capacity keeps everything,
+// and a huge gamma (1e12 meant as "no limit") must not overflow the int
+int clamped_capacity(const moe_problem &p, double mean) {
+  const double c = std::floor((double)p.gamma * mean);
+  const double all = (double)p.T * (double)p.k;
+  return (int)(c < all ? c : all);
+}
+
+// C = floor(gamma * N-bar), N-bar = T*k/E; -1 = no capacity limit
 int capacity_of(const moe_problem &p) {
   if (!(p.gamma > 0.f)) return -1;
-  const double nbar = (double)p.T * (double)p.k / (double)p.E;
-  return (int)std::floor((double)p.gamma * nbar);
+  return clamped_capacity(p, (double)p.T * (double)p.k / (double)p.E);
 }
 
 // C_D = floor(gamma * T*k/D): the token-drop capacity of a device that holds E/D experts
 int group_capacity_of(const moe_problem &p) {
-  const double per_group = (double)p.T * (double)p.k / (double)p.cap_groups;
-  return (int)std::floor((double)p.gamma * per_group);
+  return clamped_capacity(p, (double)p.T * (double)p.k / (double)p.cap_groups);
 }
 
 // ---- the four steps, without validation --------------------------------------------------

@@ -76,9 +76,25 @@ def ws_status(p):
     (dict(routing=1, expand_m=1, gamma=1.0), moe.MOE_ERR_INVALID_ARG),
     (dict(E=64, k=17, cap_groups=2, gamma=1.0), moe.MOE_ERR_UNSUPPORTED),
     (dict(E=64, k=17, expand_m=20, gamma=1.0), moe.MOE_OK),
-    # one expert's float32 GEMM output (up to T rows of d_model) must stay under 4 GiB
+    # one group's GEMM output panel, T rows plus up to 256 padding rows of the last row
+    # tile, is addressed with 32-bit byte offsets: (T + 256) rows of d_model float32 (o) or
+    # of d_ff / d_ff_shared bf16 (h) must stay under 4 GiB. At d_model = 7168 a float32 row
+    # is 28672 B, so T = 149540 is the largest accepted T; before the padding rows were
+    # counted, T = 149761 passed and its padding rows wrapped onto the panel's first rows.
     (dict(T=1 << 18, d_model=4096, k=1), moe.MOE_ERR_UNSUPPORTED),
-    (dict(T=(1 << 18) - 64, d_model=4096, k=1), moe.MOE_OK),
+    (dict(T=(1 << 18) - 64, d_model=4096, k=1), moe.MOE_ERR_UNSUPPORTED),
+    (dict(T=(1 << 18) - 257, d_model=4096, k=1), moe.MOE_OK),
+    (dict(T=149761, d_model=7168, k=1), moe.MOE_ERR_UNSUPPORTED),
+    (dict(T=149541, d_model=7168, k=1), moe.MOE_ERR_UNSUPPORTED),
+    (dict(T=149540, d_model=7168, k=1), moe.MOE_OK),
+    (dict(T=149541, d_model=64, d_ff=14336, k=1), moe.MOE_ERR_UNSUPPORTED),
+    (dict(T=149540, d_model=64, d_ff=14336, k=1), moe.MOE_OK),
+    (dict(T=149541, d_model=64, d_ff=64, d_ff_shared=14336, k=1), moe.MOE_ERR_UNSUPPORTED),
+    (dict(T=149540, d_model=64, d_ff=64, d_ff_shared=14336, k=1), moe.MOE_OK),
+    # a huge capacity factor (1e12 meant as "no limit") is accepted: the capacity is clamped
+    # to T*k before it becomes an int
+    (dict(gamma=1e12), moe.MOE_OK), (dict(gamma=1e12, expand_m=2), moe.MOE_OK),
+    (dict(gamma=1e12, cap_groups=2), moe.MOE_OK),
     # the GEMMs address an operand panel (one expert's weights, the routed rows' activations)
     # with 32-bit byte offsets: each must hold fewer than 2^31 elements
     (dict(d_model=32768, d_ff=65536), moe.MOE_ERR_UNSUPPORTED),

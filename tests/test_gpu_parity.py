@@ -11,7 +11,8 @@ Bars (written here, applied below):
     ulp per element) and must equal the rounding of the float32 output bit for bit;
   - dispatch gather: bit-identical rows.
 Sizes: small shapes that span several tiles with ragged tails and the degenerate cases
-of each selection form; the five named workloads at full size, on sampled tokens.
+of each selection form; capacity buckets past each of the selection kernel's size paths;
+the named workloads at full size, every token compared.
 """
 import numpy as np
 import pytest
@@ -173,6 +174,9 @@ TIE_CASES = [
     # at most 256 tokens: the single-block histogram + scan + scatter
     dict(T=200, E=16, k=2, gamma=0.75, expand_m=3), dict(T=150, E=16, k=4, gamma=0.5, cap_groups=4),
     dict(T=256, E=1024, k=8, gamma=1.0), dict(T=256, E=8, k=2),
+    # a huge capacity factor ("no limit"): the capacity is clamped to T*k, nothing is dropped
+    dict(T=300, E=8, k=2, gamma=1e12), dict(T=300, E=8, k=2, gamma=1e12, expand_m=2),
+    dict(T=300, E=8, k=2, gamma=1e12, cap_groups=2),
 ]
 
 
@@ -263,7 +267,117 @@ def test_routing_stats():
     assert abs(got[2 * E] - ref["balance"]) <= 1e-5 * max(1.0, ref["balance"])
     assert abs(got[2 * E + 1] - ref["max_over_mean"]) <= 1e-5 * ref["max_over_mean"]
     assert got[2 * E + 2] == ref["dropped"]
-    assert got[2 * E + 3] == int((ro["counts"] == 0).sum())
+    assert got[2 * E + 3] == ref["empty"]
+
+
+def test_routing_stats_hand_examples():
+    """moe_routing_stats on the hand-derived examples of tests/golden/hand_oracle_pins.json,
+    the routing computed by moe_route from the given logits: every statistic equals the value
+    worked out by hand (the balance term is the unscaled sum of f_i P_i)."""
+    import json
+    import os
+    from fractions import Fraction
+    import torch
+    import mixture_experts_layer_42_amd as moe
+    gold = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "hand_oracle_pins.json")))
+    ln3 = np.float32(np.log(3.0))
+    for gc in gold["routing_stats"]:
+        T, E, k = gc["T"], gc["E"], gc["k"]
+        cfg = C0.with_(T=T, E=E, k=k, d_model=64, d_ff=64, routing=gc["routing"], gamma=gc["gamma"])
+        l = np.array([[ln3 if v == "ln3" else np.float32(v) for v in row] for row in gc["logits"]],
+                     dtype=np.float32)
+        rb, ws, n = run_route(cfg, dict(x=None, w_router=None, bias=None), logits_in=l)
+        out = torch.empty(2 * E + 4, dtype=torch.float32, device="cuda")
+        moe.moe_routing_stats(moe.problem_of(cfg), rb.struct, out, ws, n)
+        got = out.cpu().numpy().astype(np.float64)
+        fr = lambda v: float(Fraction(v))   # noqa: E731
+        assert rb.counts.cpu().numpy().tolist() == gc["counts"]
+        np.testing.assert_allclose(got[:E], [fr(v) for v in gc["f"]], rtol=0, atol=1e-7)
+        np.testing.assert_allclose(got[E:2 * E], [fr(v) for v in gc["P"]], rtol=0, atol=1e-6)
+        assert abs(got[2 * E] - fr(gc["balance"])) <= 1e-6
+        assert abs(got[2 * E + 1] - fr(gc["max_over_mean"])) <= 1e-6
+        assert got[2 * E + 2] == gc["dropped"] and got[2 * E + 3] == gc["empty"]
+
+
+@pytest.mark.parametrize("name", ["fine-shared-bf16", "expert-choice-bf16", "all-dropped-shared-bf16"])
+def test_combine_against_oracle_combine(name):
+    """moe_combine alone: the GPU's own expert outputs (o_perm, o_shared) and routing, combined
+    on the GPU and by oracle.combine (float64): within float32 summation error."""
+    cfg = SMALL[name]
+    inp = inputs_for(cfg)
+    dev = dev_weights(inp)
+    l = oracle.router_logits(inp.x, inp.w_router, inp.bias)
+    out = run_steps(cfg.with_(y_dtype="f32"), dev, logits_in=l)
+    g = out["rb"].host()
+    N = int(g["offsets"][-1])
+    o = out["o_perm"].cpu().numpy()
+    o_sh = out["o_shared"].cpu().numpy() if out["o_shared"] is not None else None
+    r = dict(tok_ptr=g["tok_ptr"], tok_pos=g["tok_pos"][:N], perm_w=g["perm_w"][:N].astype(np.float64))
+    y_ref = oracle.combine(o[:max(N, 1)], r, cfg.T, o_shared=o_sh)
+    # float32 summation bound: n terms summed with n roundings of at most 2^-24 each, relative
+    # to the sum of the terms' magnitudes (the same combine over |w| and |o|)
+    mag = oracle.combine(np.abs(o[:max(N, 1)]), dict(r, perm_w=np.abs(r["perm_w"])), cfg.T,
+                         o_shared=None if o_sh is None else np.abs(o_sh))
+    n = int(np.diff(g["tok_ptr"]).max()) + 2
+    y = out["y"].cpu().numpy().astype(np.float64)
+    assert (np.abs(y - y_ref) <= n * 2.0 ** -24 * mag + 1e-37).all()
+
+
+# capacity buckets past each size path of the selection kernel: up to 2048 and 4096 keys per
+# bucket in registers, 4097..16384 in registers at 16 keys per thread, beyond that re-read
+# from memory; a router bias sends most pairs to expert 0 (and many to expert 1)
+BIG_BUCKETS = [
+    dict(T=10000, levels=0), dict(T=12000, levels=3), dict(T=40000, levels=0),
+    dict(T=40000, levels=5), dict(T=20000, levels=0, expand_m=1), dict(T=20000, levels=4, cap_groups=1),
+]
+
+
+@pytest.mark.parametrize("case", range(len(BIG_BUCKETS)))
+def test_capacity_large_buckets_bit_exact(case):
+    kw = dict(BIG_BUCKETS[case])
+    levels = kw.pop("levels")
+    cfg = C0.with_(d_model=64, d_ff=64, E=4, k=2, gamma=0.5, **kw)
+    bias = np.array([3.0, 1.5, 0.0, 0.0], dtype=np.float32)
+    if levels:
+        l = (mi.quantised_logits(cfg.T, cfg.E, levels=levels, seed=case) + bias).astype(np.float32)
+    else:
+        l = mi.normal_logits(cfg.T, cfg.E, seed=case, bias=bias)
+    ro = oracle.route(cfg, logits=l)
+    cand = np.bincount(ro["ids"][:, :cfg.k].ravel(), minlength=cfg.E)
+    say(f"[big-bucket] {kw} levels={levels}: candidates per expert {cand.tolist()}, kept "
+        f"{ro['counts'].tolist()}")
+    assert cand.max() > 4096
+    rb, _, _ = run_route(cfg, dict(x=None, w_router=None, bias=None), logits_in=l)
+    _compare_routing(cfg, rb, ro, exact_logits=l)
+
+
+@pytest.mark.parametrize("name", ["collapse-ksplit-bf16", "fine-shared-bf16", "expert-choice-bf16",
+                                  "decode-T48-shared-bf16", "group-capacity-bf16"])
+def test_deterministic_across_launch_shapes(name, monkeypatch):
+    """Runs under different launch shapes (the persistent grids capped at 256, 120, 37 and 8
+    workgroups through MOE_GRID_CUS) give bit-identical routing and output: no result
+    depends on how work is spread over the CUs (the K-split plan is fixed independently of the
+    grid, every sum runs in a fixed order, no decision depends on timing)."""
+    import torch
+    cfg = SMALL[name]
+    inp = inputs_for(cfg)
+    dev = dev_weights(inp)
+    ref_y, ref_rb = None, None
+    for cus in ("", "120", "37", "8"):
+        monkeypatch.setenv("MOE_GRID_CUS", cus)
+        y, rb = run_layer(cfg, dev)
+        h = _meaningful(cfg, rb.host())
+        if ref_y is None:
+            ref_y, ref_h = y, h
+            continue
+        assert torch.equal(_bits_t(y), _bits_t(ref_y)), f"output differs with MOE_GRID_CUS={cus}"
+        for k, v in ref_h.items():
+            assert (_bits(np.asarray(h[k])) == _bits(np.asarray(v))).all(), (k, cus)
+
+
+def _bits_t(t):
+    import torch
+    return t.contiguous().view(torch.int16 if t.element_size() == 2 else torch.int32)
 
 
 # ------------------------------------------------------------------------------ full size
@@ -311,14 +425,20 @@ FULL = ["mixtral-token-choice-bf16", "expert-choice-bf16", "capacity-drop-zipf-b
 
 @pytest.mark.parametrize("name", FULL)
 def test_full_size_layer(name):
-    import torch
     """The named workload at full size, in the launch configuration the bench times
-    (moe_layer_forward). Checks: logits within 1e-5; with the oracle's logits fed in, every
-    routing array bit-identical; y on sampled tokens within 2e-2 of the oracle for both the
-    oracle-logit path and moe_layer_forward (tokens whose decisions moved across a tie
-    within the logit tolerance are listed and excluded, and must be rare)."""
+    (moe_layer_forward), every token compared. Checks: logits within 1e-5; with the
+    oracle's logits fed in, every routing array bit-identical and y of every token within
+    the bar; through moe_layer_forward, decisions equal the oracle's except tokens whose
+    decision sits within the logit tolerance of a tie (listed, explained, rare), and y of
+    every other token within the bar, on a float32 output of the same launch (the arithmetic)
+    and on the bf16 output (its exact rounding). Over the whole output the float32 output is
+    held to 2e-2 of the RMS for token choice; under expert choice, where bf16 rounding alone
+    misses that global figure (tests/test_bar_reading.py), it is held to 2e-2 of the RMS
+    against the oracle's routing evaluated with h rounded to bf16, and the global figures are
+    printed."""
+    import torch
+    from bf16_emulation import h_bf16_layer
     cfg = mi.workload(name)
-    cid = FULL.index(name) + 1
     say(f"[full] {name}: generating inputs")
     inp = inputs_for(cfg)
     dev = dev_weights(inp)
@@ -329,6 +449,8 @@ def test_full_size_layer(name):
     # 1) selection with the oracle's logits, and the rest of the layer on that routing
     steps = run_steps(cfg, dev, logits_in=l)
     _compare_routing(cfg, steps["rb"], ro, exact_logits=l)
+    y_steps = host_f32(steps["y"])
+    del steps
     # 2) the bench's launch configuration
     y_layer, rb = run_layer(cfg, dev)
     g = rb.host()
@@ -339,24 +461,33 @@ def test_full_size_layer(name):
     assert len(diff) <= max(3, cfg.T // 500)
     for t in diff:
         assert _explained(cfg, t, l, ro, len(diff)), f"token {t} routing differs without a tie"
-    rng = np.random.default_rng(cid)
-    sample = np.unique(np.concatenate([[0, cfg.T - 1], rng.choice(cfg.T, 22, replace=False)]))
-    say(f"[full] {name}: oracle FFN on {sample.size} sampled tokens")
-    y_ref, _ = oracle.layer_forward(inp, tokens=sample, routing=ro)
-    ok = np.array([t not in diff for t in sample])
-    # float32 output of the same launch: the arithmetic against the stated bar
+    ok = np.ones(cfg.T, dtype=bool)
+    ok[diff] = False
     cfg32 = cfg.with_(y_dtype="f32")
     y32, _ = run_layer(cfg32, dev, with_routing=False)
-    p32, g32 = check_y(cfg32, host_f32(y32)[sample][ok], y_ref[ok])
-    # bf16 output: exactly the rounding of the float32 output, and within the bf16 bar
-    assert (y_layer.view(torch.int16).cpu().numpy().view(np.uint16)
-            == mi.f32_to_bf16_bits(y32.cpu().numpy())).all()
-    ps, gs = check_y(cfg, host_f32(steps["y"])[sample], y_ref)
-    pl, gl = check_y(cfg, host_f32(y_layer)[sample][ok], y_ref[ok])
+    y32 = y32.cpu().numpy()
+    # bf16 output: exactly the rounding of the float32 output
+    assert (y_layer.view(torch.int16).cpu().numpy().view(np.uint16) == mi.f32_to_bf16_bits(y32)).all()
+    y16 = host_f32(y_layer)
+    del y_layer
+    say(f"[full] {name}: oracle FFN on all {cfg.T} tokens")
+    y_ref, _ = oracle.layer_forward(inp, routing=ro)
+    # float32 output of the same launch: the arithmetic against the bar, every token
+    p32, g32 = check_y(cfg32, y32[ok], y_ref[ok])
+    ps, gs = check_y(cfg, y_steps, y_ref)
+    pl, gl = check_y(cfg, y16[ok], y_ref[ok])
     e_round = rel_err(mi.bf16_to_f32(mi.f32_to_bf16_bits(y_ref.astype(np.float32))), y_ref)
-    say(f"[full] {name}: max|dy|/RMS per-token/global: f32 y {p32:.4f}/{g32:.4f}  bf16 y "
-        f"{pl:.4f}/{gl:.4f} (oracle-logit path {ps:.4f}/{gs:.4f}); exact answer rounded to "
-        f"bf16: {e_round:.4f}")
+    msg = (f"[full] {name}: max|dy|/RMS per-token/global over all tokens: float32 y "
+           f"{p32:.4f}/{g32:.4f}  bf16 y {pl:.4f}/{gl:.4f} (oracle-logit path {ps:.4f}/{gs:.4f}); "
+           f"exact answer rounded to bf16: global {e_round:.4f}; max|y|/RMS "
+           f"{np.abs(y_ref).max() / np.sqrt(np.mean(y_ref ** 2)):.1f}")
+    if cfg.routing == "expert":
+        y_h = h_bf16_layer(inp, ro)
+        e_h = rel_err(y_h, y_ref)
+        g_vs_h = rel_err(y32[ok], y_h[ok])
+        msg += f"; h rounded to bf16: global {e_h:.4f}; float32 y against it: global {g_vs_h:.4f}"
+        assert g_vs_h <= tol_for(cfg), ("global bar against the bf16-h evaluation", g_vs_h)
+    say(msg)
 
 
 def test_operand_offsets_past_2gib():
