@@ -185,6 +185,21 @@ moe_status moe_route(const moe_problem *problem, const void *x, const float *w_r
                      const float *bias, int flags, moe_routing *routing, void *ws,
                      size_t ws_bytes, hipStream_t stream);
 
+/* moe_route without a workspace, for callers that cannot allocate device memory (code under
+ * HIP graph capture, serving loops or harnesses that forbid allocation). Same arguments,
+ * results and errors as moe_route minus ws/ws_bytes: the routing scratch lives in a
+ * library-held device array of 32 MiB, one per GPU the library runs on, held until the
+ * process ends; the call allocates nothing. A problem whose routing scratch exceeds 32 MiB is
+ * rejected with MOE_ERR_WORKSPACE before anything is enqueued. The routing scratch is about
+ * 24*T*S bytes with S = k + expand_m slots per token (S = E and another 4*E*T bytes for
+ * expert choice), plus 6*d_model*E bytes of split router weights for bf16: 16384 tokens with
+ * 128 experts and top-8 need about 5 MiB, the other named workloads less.
+ * Every call on one GPU shares that GPU's array: calls that overlap on one GPU (different
+ * streams, or different host threads) race and must be serialised by the caller. */
+moe_status moe_route_noalloc(const moe_problem *problem, const void *x, const float *w_router,
+                             const float *bias, int flags, moe_routing *routing,
+                             hipStream_t stream);
+
 /* Row gather of the dispatch: x_perm[p] = x[perm_token[p]] for p < offsets[E] (hrletsgo
  * page, basic-structure section: the dispatch that moves each token to its experts;
  * devcy0922 page "Ugh, bandwidth", section on MoE not being a light dense model: token and

@@ -15,5 +15,6 @@ from ._lib import (EXPORTED, LIB_PATH, MOE_BF16, MOE_ERR_HIP, MOE_ERR_INVALID_AR
                    MOE_ROUTE_LOGITS_IN, MOE_STAGE_COUNT, MOE_TOKEN_CHOICE, STAGE_NAMES, MoEError,
                    load, make_problem, make_routing, moe_combine, moe_dispatch, moe_expert_ffn,
                    moe_layer_forward, moe_layer_forward_traced, moe_problem, moe_route,
-                   moe_routing, moe_routing_stats, moe_workspace_bytes, status_str)
+                   moe_route_noalloc, moe_routing, moe_routing_stats, moe_workspace_bytes,
+                   status_str)
 from .buffers import RoutingBuffers, device_tensor, problem_of  # noqa: F401

@@ -21,8 +21,9 @@ MOE_ROUTE_LOGITS_IN = 1
 MOE_STAGE_COUNT = 5
 STAGE_NAMES = ("route", "dispatch", "gate_up", "down", "combine")
 
-EXPORTED = ("moe_workspace_bytes", "moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine",
-            "moe_layer_forward", "moe_layer_forward_traced", "moe_routing_stats", "moe_status_str")
+EXPORTED = ("moe_workspace_bytes", "moe_route", "moe_route_noalloc", "moe_dispatch",
+            "moe_expert_ffn", "moe_combine", "moe_layer_forward", "moe_layer_forward_traced",
+            "moe_routing_stats", "moe_status_str")
 
 
 class MoEError(RuntimeError):
@@ -68,6 +69,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     sig = {
         "moe_workspace_bytes": [P, ctypes.POINTER(SZ)],
         "moe_route": [P, V, V, V, I, R, V, SZ, V],
+        "moe_route_noalloc": [P, V, V, V, I, R, V],
         "moe_dispatch": [P, V, R, V, V],
         "moe_expert_ffn": [P, V, R, V, V, V, V, V, V, V, V, V, V, SZ, V],
         "moe_combine": [P, V, V, R, V, V],
@@ -138,6 +140,12 @@ def moe_route(problem, x, w_router, bias, flags, routing: moe_routing, ws, ws_by
     _check(load().moe_route(ctypes.byref(problem), _p(x), _p(w_router), _p(bias), int(flags),
                             ctypes.byref(routing), _p(ws), int(ws_bytes), _stream(stream)),
            "moe_route")
+
+
+def moe_route_noalloc(problem, x, w_router, bias, flags, routing: moe_routing, stream=None):
+    _check(load().moe_route_noalloc(ctypes.byref(problem), _p(x), _p(w_router), _p(bias),
+                                    int(flags), ctypes.byref(routing), _stream(stream)),
+           "moe_route_noalloc")
 
 
 def moe_dispatch(problem, x, routing: moe_routing, x_perm, stream=None):

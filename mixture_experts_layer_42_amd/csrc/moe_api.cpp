@@ -436,6 +436,69 @@ moe_status layer_forward(const moe_problem *pp, const void *x, const float *w_ro
   return MOE_OK;
 }
 
+// ---- allocation-free routing (moe_route_noalloc) -------------------------------------------
+// The routing scratch of moe_route_noalloc lives in this library-held array instead of a
+// caller's workspace: one copy per GPU the library runs on, held until the process ends. Its
+// routing kernels write every scratch word they later read, so nothing needs clearing between
+// calls; calls that overlap on one GPU share the array and race.
+constexpr size_t kNoAllocScratchBytes = (size_t)32 << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current GPU's copy of `scratch`: looked up with hipGetSymbolAddress on
+// the first call on that device (with that device current), then cached. Host code passes this
+// address, never the array's name, to the kernels.
+hipError_t scratch_ptr(void **out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
+// Bytes of the workspace's routing regions: the layout puts them first, so the routing kernels
+// touch only [0, partials) of a workspace.
+size_t route_scratch_bytes(const moe_problem &p) { return make_layout(p).partials; }
+
+moe_status route_checked(const moe_problem *problem, const void *x, const float *w_router,
+                         const float *bias, int flags, moe_routing *routing, char *ws,
+                         hipStream_t stream) {
+  const moe_problem &p = *problem;
+  moe_status s;
+  if (flags & MOE_ROUTE_LOGITS_IN)
+    s = debug_check({{routing->logits, nz(p.T, p.E), 4, nullptr, 0}}, stream);
+  else
+    s = debug_check({{x, nz(p.T, p.d_model), elt_of(p), nullptr, 0},
+                     {w_router, nz(p.d_model, p.E), 4, nullptr, 0},
+                     {bias, (size_t)p.E, 4, nullptr, 0}},
+                    stream);
+  if (s != MOE_OK) return s;
+  if (do_route(p, x, w_router, bias, flags, *routing, ws, stream) != hipSuccess)
+    return MOE_ERR_HIP;
+  return MOE_OK;
+}
+
+moe_status check_route_args(const moe_problem *problem, const void *x, const float *w_router,
+                            const float *bias, int flags, const moe_routing *routing) {
+  moe_status s = check_problem(problem);
+  if (s != MOE_OK) return s;
+  if (flags & ~MOE_ROUTE_LOGITS_IN) return MOE_ERR_INVALID_ARG;
+  if (!(flags & MOE_ROUTE_LOGITS_IN) && (!ptr_ok(x) || !ptr_ok(w_router) || !opt_ptr_ok(bias)))
+    return MOE_ERR_INVALID_ARG;
+  return check_routing_out(*problem, routing);
+}
+
 }  // namespace
 
 extern "C" {
@@ -451,25 +514,21 @@ moe_status moe_workspace_bytes(const moe_problem *problem, size_t *bytes) {
 moe_status moe_route(const moe_problem *problem, const void *x, const float *w_router,
                      const float *bias, int flags, moe_routing *routing, void *ws,
                      size_t ws_bytes, hipStream_t stream) {
-  moe_status s = check_problem(problem);
+  moe_status s = check_route_args(problem, x, w_router, bias, flags, routing);
   if (s != MOE_OK) return s;
-  const moe_problem &p = *problem;
-  if (flags & ~MOE_ROUTE_LOGITS_IN) return MOE_ERR_INVALID_ARG;
-  if (!(flags & MOE_ROUTE_LOGITS_IN) && (!ptr_ok(x) || !ptr_ok(w_router) || !opt_ptr_ok(bias)))
-    return MOE_ERR_INVALID_ARG;
-  if ((s = check_routing_out(p, routing)) != MOE_OK) return s;
-  if ((s = check_ws(p, ws, ws_bytes)) != MOE_OK) return s;
-  if (flags & MOE_ROUTE_LOGITS_IN)
-    s = debug_check({{routing->logits, nz(p.T, p.E), 4, nullptr, 0}}, stream);
-  else
-    s = debug_check({{x, nz(p.T, p.d_model), elt_of(p), nullptr, 0},
-                     {w_router, nz(p.d_model, p.E), 4, nullptr, 0},
-                     {bias, (size_t)p.E, 4, nullptr, 0}},
-                    stream);
+  if ((s = check_ws(*problem, ws, ws_bytes)) != MOE_OK) return s;
+  return route_checked(problem, x, w_router, bias, flags, routing, (char *)ws, stream);
+}
+
+moe_status moe_route_noalloc(const moe_problem *problem, const void *x, const float *w_router,
+                             const float *bias, int flags, moe_routing *routing,
+                             hipStream_t stream) {
+  moe_status s = check_route_args(problem, x, w_router, bias, flags, routing);
   if (s != MOE_OK) return s;
-  if (do_route(p, x, w_router, bias, flags, *routing, (char *)ws, stream) != hipSuccess)
-    return MOE_ERR_HIP;
-  return MOE_OK;
+  if (route_scratch_bytes(*problem) > kNoAllocScratchBytes) return MOE_ERR_WORKSPACE;
+  void *ws = nullptr;
+  if (scratch_ptr(&ws) != hipSuccess) return MOE_ERR_HIP;
+  return route_checked(problem, x, w_router, bias, flags, routing, (char *)ws, stream);
 }
 
 moe_status moe_dispatch(const moe_problem *problem, const void *x, const moe_routing *routing,

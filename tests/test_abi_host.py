@@ -204,3 +204,20 @@ def test_binding_raises_on_error():
     with pytest.raises(moe.MoEError) as ei:
         moe.moe_workspace_bytes(good(k=99))
     assert ei.value.status == moe.MOE_ERR_INVALID_ARG
+
+
+def test_route_noalloc_rejects_problems_past_its_scratch():
+    """moe_route_noalloc keeps its routing scratch in a 32 MiB library-held array: a problem
+    whose routing scratch is larger is rejected with MOE_ERR_WORKSPACE on the host, before any
+    device call; argument errors are reported as for moe_route."""
+    lib = moe.load()
+    r = routing_struct()
+    big = good(T=1 << 20, k=8, E=8, d_model=64, d_ff=64)   # ~24 * 2^20 * 8 B of candidates
+    st = lib.moe_route_noalloc(ctypes.byref(big), FAKE, FAKE, None, 0, ctypes.byref(r), None)
+    assert st == moe.MOE_ERR_WORKSPACE
+    st = lib.moe_route_noalloc(ctypes.byref(good(k=9)), FAKE, FAKE, None, 0, ctypes.byref(r), None)
+    assert st == moe.MOE_ERR_INVALID_ARG
+    st = lib.moe_route_noalloc(ctypes.byref(good()), None, FAKE, None, 0, ctypes.byref(r), None)
+    assert st == moe.MOE_ERR_INVALID_ARG
+    st = lib.moe_route_noalloc(ctypes.byref(good()), FAKE, FAKE, None, 2, ctypes.byref(r), None)
+    assert st == moe.MOE_ERR_INVALID_ARG

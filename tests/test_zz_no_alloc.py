@@ -1,0 +1,61 @@
+"""moe_route_noalloc (routing scratch in the library's own device array, no workspace)
+against moe_route (caller workspace), through the C ABI: every routing array bit-identical,
+on two calls in a row, the second with a smaller problem, for token choice with a capacity
+drop, the Expanded Drop and expert choice. The arrays the second call leaves must not depend
+on what the first left in the shared scratch."""
+import numpy as np
+import pytest
+
+import moe_inputs as mi
+from gpu_support import dev_weights, inputs_for, run_route, say
+
+pytestmark = pytest.mark.gpu
+
+C0 = mi.TINY
+CASES = [
+    ("capacity-drop-E128", C0.with_(dtype="bf16", T=3000, d_model=256, E=128, k=8, d_ff=64,
+                                    gamma=1.25, bias=("normal", 1.0)),
+     dict(T=700)),
+    ("expanded-drop", C0.with_(dtype="bf16", T=2500, d_model=128, E=8, k=2, d_ff=64, gamma=0.75,
+                               expand_m=2, bias=("zipf", 1.2)),
+     dict(T=300)),
+    ("expert-choice", C0.with_(dtype="bf16", T=4096, d_model=256, E=8, k=2, d_ff=64,
+                               routing="expert"),
+     dict(T=1000)),
+    ("mixtral-shaped-no-drop", mi.MIXTRAL.with_(T=2048, d_ff=64), dict(T=33)),
+]
+
+
+def _noalloc(cfg, dev):
+    import torch
+    import mixture_experts_layer_42_amd as moe
+    prob = moe.problem_of(cfg)
+    rb = moe.RoutingBuffers(prob)
+    moe.moe_route_noalloc(prob, dev["x"], dev["w_router"], dev["bias"], 0, rb.struct)
+    torch.cuda.synchronize()
+    return rb
+
+
+def _same(cfg, a, b):
+    ha, hb = a.host(), b.host()
+    N = int(ha["offsets"][-1])
+    assert N == int(hb["offsets"][-1])
+    keys = ["logits", "counts", "offsets", "tok_ptr"]
+    if cfg.routing == "token":
+        keys += ["topk_ids", "topk_w", "kept"]
+    for k in keys:
+        assert (np.asarray(ha[k]).view(np.uint8) == np.asarray(hb[k]).view(np.uint8)).all(), k
+    for k in ("perm_token", "perm_w", "tok_pos"):
+        assert (np.asarray(ha[k][:N]).view(np.uint8) == np.asarray(hb[k][:N]).view(np.uint8)).all(), k
+
+
+@pytest.mark.parametrize("case", range(len(CASES)))
+def test_route_noalloc_equals_route(case):
+    name, big, small_kw = CASES[case]
+    for cfg in (big, big.with_(**small_kw)):
+        say(f"[noalloc] {name}: T={cfg.T}")
+        inp = inputs_for(cfg)
+        dev = dev_weights(inp)
+        ref, _, _ = run_route(cfg, dev)
+        got = _noalloc(cfg, dev)
+        _same(cfg, got, ref)
