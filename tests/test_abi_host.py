@@ -221,3 +221,19 @@ def test_route_noalloc_rejects_problems_past_its_scratch():
     assert st == moe.MOE_ERR_INVALID_ARG
     st = lib.moe_route_noalloc(ctypes.byref(good()), FAKE, FAKE, None, 2, ctypes.byref(r), None)
     assert st == moe.MOE_ERR_INVALID_ARG
+
+
+def test_peak_library_exports_its_header():
+    """libmoe_peak.so (the achievable-peak microbenchmarks) exports exactly what
+    include/moe_peak.h declares, and rejects bad arguments without launching anything."""
+    from mixture_experts_layer_42_amd import peak
+    text = open(os.path.join(os.path.dirname(HEADER), "moe_peak.h")).read()
+    names = sorted(set(re.findall(r"^int\s+(moe_peak_\w+)\s*\(", text, re.M)))
+    assert names == ["moe_peak_copy", "moe_peak_lds", "moe_peak_mfma"]
+    lib = peak.load()
+    for n in names:
+        assert ctypes.cast(getattr(lib, n), ctypes.c_void_p).value
+    invalid = 1   # hipErrorInvalidValue
+    assert lib.moe_peak_mfma(None, FAKE, FAKE, 1, 1, None) == invalid
+    assert lib.moe_peak_lds(FAKE, 0, 1, None) == invalid
+    assert lib.moe_peak_copy(FAKE, FAKE, 24, 1, None) == invalid
