@@ -79,14 +79,28 @@ struct TopkOut {
   int k, kden, renorm, want_key;
   int32_t *ids;
   float *gates, *keys;
+  int32_t *blk_cnt;   // optional: picks per expert of each workgroup's tokens (E <= 16)
 };
+constexpr int kBlkCountMaxE = 16;   // experts the per-block counts and their dispatch handle
 // logits = x W_r + b; with topk non-null, the router may also run the top-k of every token
-// (same results as launch_topk) and then sets *topk_done
+// (same results as launch_topk) and then sets *topk_done; when it also wrote topk->blk_cnt,
+// *cnt_block is the number of tokens per count block (else 0)
 hipError_t launch_router(int dtype, const void *x, const float *w, const float *bias,
                          float *logits, int T, int d, int E, uint16_t *w3, hipStream_t st,
-                         const TopkOut *topk = nullptr, bool *topk_done = nullptr);
+                         const TopkOut *topk = nullptr, bool *topk_done = nullptr,
+                         int *cnt_block = nullptr);
+// with blk_cnt non-null (E <= 16) the picks per expert of each workgroup's tokens go there and
+// *cnt_block gets the tokens per workgroup
 hipError_t launch_topk(const float *logits, int T, int E, int k, int kden, int renorm,
-                       int want_key, int32_t *ids, float *gates, float *keys, hipStream_t st);
+                       int want_key, int32_t *ids, float *gates, float *keys, hipStream_t st,
+                       int32_t *blk_cnt = nullptr, int *cnt_block = nullptr);
+// token choice without a capacity limit: counts, offsets, permutation and the token CSR in one
+// launch from the per-block counts of the top-k (blocks of bt tokens, bt in {16, 32})
+hipError_t launch_dispatch_blocks(const int32_t *ids, const float *gates, int T, int k, int E,
+                                  const int32_t *blk_cnt, int bt, int32_t *counts,
+                                  int32_t *offsets, int32_t *perm_token, float *perm_w,
+                                  uint8_t *kept, int32_t *tok_ptr, int32_t *tok_pos,
+                                  hipStream_t st);
 // with C < 0 (no capacity) and tok_ptr/tok_pos non-null the token -> rows CSR is written too
 hipError_t launch_token_dispatch(const RouteScratch &s, const int32_t *ids, const float *gates,
                                  int T, int k, int E, int C, int32_t *perm_token, float *perm_w,

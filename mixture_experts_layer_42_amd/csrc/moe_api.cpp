@@ -81,7 +81,7 @@ Layout make_layout(const moe_problem &p) {
   size_t o = 0;
   auto take = [&](size_t bytes) { size_t at = o; o += up(bytes); return at; };
   L.keys = take(T * S * 4);
-  L.blk_cnt = take(nblk * E * 4);
+  L.blk_cnt = take(((T + 15) / 16) * E * 4);   // per 256-token block, or per top-k workgroup
   L.blk_base = take(nblk * E * 4);
   L.cnt_pre = take(E * 4);
   L.off_pre = take((E + 1) * 4);
@@ -283,19 +283,29 @@ hipError_t do_route(const moe_problem &p, const void *x, const float *w_router,
   const RouteScratch s = scratch_of(L, ws);
   hipError_t e;
   const int C = capacity_of(p);
+  // token choice keeping every pair with at most 16 experts: the top-k counts its picks per
+  // workgroup and one launch does the whole dispatch from those counts
+  const bool blk_dispatch = p.routing == MOE_TOKEN_CHOICE && C < 0 && p.expand_m == 0 &&
+                            p.cap_groups == 0 && p.E <= kBlkCountMaxE;
   const TopkOut tk{p.k + p.expand_m, p.k, p.renorm_topk, C >= 0 ? 1 : 0, r.topk_ids, r.topk_w,
-                   s.keys};
+                   s.keys, blk_dispatch ? s.blk_cnt : nullptr};
   bool topk_done = false;
+  int cnt_block = 0;
   if (!(flags & MOE_ROUTE_LOGITS_IN)) {
     e = launch_router(p.dtype == MOE_BF16 ? 1 : 0, x, w_router, bias, r.logits, p.T, p.d_model,
-                      p.E, s.w3, st, p.routing == MOE_TOKEN_CHOICE ? &tk : nullptr, &topk_done);
+                      p.E, s.w3, st, p.routing == MOE_TOKEN_CHOICE ? &tk : nullptr, &topk_done,
+                      &cnt_block);
     if (e != hipSuccess) return e;
   }
   if (p.routing == MOE_TOKEN_CHOICE) {
     if (!topk_done)
       e = launch_topk(r.logits, p.T, p.E, tk.k, tk.kden, tk.renorm, tk.want_key, r.topk_ids,
-                      r.topk_w, s.keys, st);
+                      r.topk_w, s.keys, st, tk.blk_cnt, &cnt_block);
     if (e != hipSuccess) return e;
+    if (blk_dispatch && cnt_block > 0)
+      return launch_dispatch_blocks(r.topk_ids, r.topk_w, p.T, p.k, p.E, s.blk_cnt, cnt_block,
+                                    r.counts, r.offsets, r.perm_token, r.perm_w, r.kept,
+                                    r.tok_ptr, r.tok_pos, st);
     if (p.cap_groups > 0)
       e = launch_group_capacity(s, r.topk_ids, r.topk_w, p.T, p.k, p.E, p.cap_groups,
                                 group_capacity_of(p), r.perm_token, r.perm_w, r.kept, r.counts,

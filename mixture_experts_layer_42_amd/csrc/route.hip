@@ -10,8 +10,9 @@
 //                   lower token; weight = softmax over the column's T tokens
 //   dispatch        per-expert histogram -> exclusive scan -> stable permutation
 //                   (ascending token inside an expert), CSR token -> rows
-// Integer decisions never depend on summation order or atomics: histograms are
-// built from bit masks and popcounts, positions from prefix scans.
+// Integer decisions never depend on summation order or arrival order: histograms are built
+// from bit masks and popcounts or from order-independent LDS integer adds, positions from
+// prefix scans and wave ballots.
 #include <type_traits>
 
 #include "common.h"
@@ -397,39 +398,32 @@ __global__ __launch_bounds__(512) void router_mfma_kernel(const bf16_t *__restri
 }
 
 // ----------------------------------------------------------------------------------------
-// Router, bf16 x and E <= 10, on the matrix cores. The three bf16 parts of W_r are 3E rows
-// of one [32][d] bf16 operand (row p*E + e holds part p of W_r[:, e]; rows 3E..31 are zero),
-// built by router_split_narrow_kernel. A workgroup of 8 waves takes 16 tokens; wave w sums the
-// 64-column units u = w, w+8, ... of d with v_mfma_f32_16x16x32_bf16 (A: 16 token rows of x,
-// B: 2 blocks of 16 W rows), four units' loads in flight. The 8 partial 16 x 32 tiles are
-// added in wave order in LDS, then each logit is (hi + mid) + lo + bias.
+// Router, bf16 x and E <= 10, on the matrix cores, reading the float32 W_r itself. The three
+// bf16 parts of W_r (hi = bf16(w), mid = bf16(w - hi), lo = bf16(w - hi - mid)) form the 3E
+// rows of a 32-row B operand: row p*E + e holds part p of column e, rows 3E..31 are zero. A
+// workgroup of 8 waves takes 16 tokens (32 when T >= 8192); wave w sums its share of the
+// 64-column units of d with v_mfma_f32_16x16x32_bf16 (A: 16 token rows of x, B: the two
+// 16-row halves of the part operand), four units' loads in flight. For each 32-column K step
+// a wave loads the float32 block W_r[j0 .. j0+31][0 .. E) (128 E contiguous bytes, 16 bytes
+// per lane), every lane splits its 4 elements once and writes the parts into an LDS tile of
+// its wave in the operand's layout (32 rows of 32 bf16), and each lane reads its two
+// fragments back with two 16-byte LDS reads: W_r is read as it is, with no separate split
+// pass. The workgroups walk the units in rotated order (workgroup b starts at unit
+// 8 (b mod nu/8)), so that they do not all read the same W_r lines from L2 at the same
+// moment. The 8 partial 16 x 32 tiles are added in wave order in LDS, then each logit is
+// (hi + mid) + lo + bias; every token's sums run in the order its workgroup fixes.
 constexpr int kNarrowRows = 32;
-
-__global__ __launch_bounds__(256) void router_split_narrow_kernel(const float *__restrict__ w,
-                                                                  int d, int E,
-                                                                  bf16_t *__restrict__ w3n) {
-  const size_t n = (size_t)kNarrowRows * d;
-  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) {
-    const int row = (int)(i / d), j = (int)(i % d);
-    const int part = row / E, e = row % E;
-    bf16_t out = 0;
-    if (part < 3) {
-      const float v = w[(size_t)j * E + e];
-      const bf16_t hi = f32_to_bf16(v);
-      const float r1 = v - bf16_to_f32(hi);
-      const bf16_t mid = f32_to_bf16(r1);
-      out = part == 0 ? hi : part == 1 ? mid : f32_to_bf16(r1 - bf16_to_f32(mid));
-    }
-    w3n[(size_t)row * router_w3_ld(d) + j] = out;
-  }
-}
+constexpr int kNarrowMaxE = 10;
+constexpr int kBlkMaxE = kBlkCountMaxE;
+constexpr int kWtRowBytes = 80;   // LDS row stride of a part tile: 64 B of data + 16 B pad
 
 // Token-choice top-k of one token whose E <= 16 logits sit in LDS, computed by one thread
 // with the arithmetic topk_kernel uses for the same E (a group of G = 8 or 16 lanes, one logit
 // per lane): picks by (logit desc, expert asc), gate numerators exp(l - max) over the first
 // pick's logit, the renormalisation mass of the first kden picks in pick order or the full
 // softmax sum in the butterfly order of G lanes, and the routing keys of the capacity forms.
-MOE_DEV void topk_one_token(const float *l, int E, int t, const TopkOut &o) {
+// With cnt (LDS, one int per expert) every pick is also counted there.
+MOE_DEV void topk_one_token(const float *l, int E, int t, const TopkOut &o, int *cnt) {
   const int G = E <= 8 ? 8 : 16;
   uint32_t taken = 0u;
   float mx = 0.f, qsum = 0.f, qn[16];
@@ -444,6 +438,7 @@ MOE_DEV void topk_one_token(const float *l, int E, int t, const TopkOut &o) {
     qn[r] = expf(bv - mx);
     pick[r] = be;
     if (r < o.kden) qsum += qn[r];
+    if (cnt) atomicAdd(&cnt[be], 1);   // LDS integer add: the count does not depend on order
   }
   float denom = qsum;
   if (!o.renorm) {
@@ -466,54 +461,95 @@ MOE_DEV void topk_one_token(const float *l, int E, int t, const TopkOut &o) {
   }
 }
 
-template <int TB>
+template <int TB, int NCH>   // NCH: 16-byte W_r chunks per lane and block (1: E <= 8, 2: E <= 10)
 __global__ __launch_bounds__(512) void router_mfma_narrow_kernel(const bf16_t *__restrict__ x,
-                                                                 const bf16_t *__restrict__ w3n,
+                                                                 const float *__restrict__ w,
                                                                  const float *__restrict__ bias,
                                                                  float *__restrict__ logits,
                                                                  int T, int d, int E,
-                                                                 TopkOut topk) {
-  constexpr int U = 4;          // 64-column units per wave in flight
+                                                                 TopkOut topk,
+                                                                 int32_t *__restrict__ blk_cnt) {
+  // 64-column units per wave in flight: with 16 tokens and E <= 8 the whole share of a
+  // 4096-wide d (8 units) goes out at once, so a wave waits for memory once
+  constexpr int U = (TB == 1 && NCH == 1) ? 8 : 4;
   constexpr int TT = 16 * TB;   // tokens per workgroup
   __shared__ float part[8][TT * kNarrowRows];
+  __shared__ __attribute__((aligned(16))) char wt[8][kNarrowRows * kWtRowBytes];   // per wave
+  __shared__ int cnt[kNarrowMaxE];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int t0 = blockIdx.x * TT;
   const int kq = 8 * (lane >> 4);   // this lane's 8 columns inside a 32-column MFMA step
-  const int ldw = router_w3_ld(d);
+  const int nchunk = 8 * E;         // 16-byte chunks of a 32-column block of W_r
   const bf16_t *xr[TB];
 #pragma unroll
   for (int b = 0; b < TB; ++b) xr[b] = x + (size_t)min(t0 + 16 * b + (lane & 15), T - 1) * d + kq;
-  const bf16_t *b0 = w3n + (size_t)(lane & 15) * ldw + kq;
-  const bf16_t *b1 = w3n + (size_t)(16 + (lane & 15)) * ldw + kq;
-  const bool q_live = 16 + (lane & 15) < 3 * E;   // rows past the three parts are zero
+  char *tile = wt[wv];
+  // the part rows this lane writes: element i of its chunk(s) is W_r[j0 + f / E][f % E],
+  // f = 4 c + i; its part p goes to row p E + f % E, column f / E of the tile
+  // rows 3E..31 stay zero: cleared once
+  for (int i = lane; i < kNarrowRows * kWtRowBytes / 4; i += 64)
+    reinterpret_cast<uint32_t *>(tile)[i] = 0u;
   rf32x4_t acc0[TB], acc1[TB];
 #pragma unroll
   for (int b = 0; b < TB; ++b) acc0[b] = acc1[b] = rf32x4_t{0.f, 0.f, 0.f, 0.f};
   const int nu = d / 64;
+  const int rot = (nu % 8 == 0) ? (int)(blockIdx.x % (unsigned)(nu / 8)) * 8 : 0;
   for (int ub = wv; ub < nu; ub += 8 * U) {
-    rbf16x8_t a[U][TB][2], p[U][2], q[U][2];
+    rbf16x8_t a[U][TB][2];
+    float4 wr[U][2][NCH];   // raw float32 W_r chunks: [unit][half][chunk lane (+ 64)]
 #pragma unroll
     for (int v = 0; v < U; ++v) {
-      const int u = min(ub + 8 * v, nu - 1);   // past the end: reloaded, not used
+      const int u = (min(ub + 8 * v, nu - 1) + rot) % nu;   // past the end: reloaded, not used
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const size_t o = (size_t)u * 64 + h * 32;
 #pragma unroll
         for (int b = 0; b < TB; ++b) a[v][b][h] = *reinterpret_cast<const rbf16x8_t *>(xr[b] + o);
-        p[v][h] = *reinterpret_cast<const rbf16x8_t *>(b0 + o);
-        q[v][h] = q_live ? *reinterpret_cast<const rbf16x8_t *>(b1 + o) : rbf16x8_t{};
+        const float4 *blk = reinterpret_cast<const float4 *>(w + o * E);
+#pragma unroll
+        for (int c2 = 0; c2 < NCH; ++c2)
+          wr[v][h][c2] = lane + 64 * c2 < nchunk ? blk[lane + 64 * c2] : make_float4(0.f, 0.f, 0.f, 0.f);
       }
     }
 #pragma unroll
     for (int v = 0; v < U; ++v) {
       if (ub + 8 * v < nu) {   // wave-uniform
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
+        for (int h = 0; h < 2; ++h) {
+#pragma unroll
+          for (int c2 = 0; c2 < NCH; ++c2) {
+            const int c = lane + 64 * c2;
+            if (c < nchunk) {
+              const float vals[4] = {wr[v][h][c2].x, wr[v][h][c2].y, wr[v][h][c2].z, wr[v][h][c2].w};
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                const int f = 4 * c + i, col = f / E, e = f - col * E;
+                const __bf16 hi = (__bf16)vals[i];
+                const float r1 = vals[i] - (float)hi;
+                const __bf16 mid = (__bf16)r1;
+                const __bf16 lo = (__bf16)(r1 - (float)mid);
+                char *at = tile + e * kWtRowBytes + col * 2;
+                *reinterpret_cast<__bf16 *>(at) = hi;
+                *reinterpret_cast<__bf16 *>(at + E * kWtRowBytes) = mid;
+                *reinterpret_cast<__bf16 *>(at + 2 * E * kWtRowBytes) = lo;
+              }
+            }
+          }
+          // the wave's LDS accesses complete in order: the reads below see the writes above
+          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+          __builtin_amdgcn_wave_barrier();
+          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+          const rbf16x8_t p = *reinterpret_cast<const rbf16x8_t *>(tile + (lane & 15) * kWtRowBytes + kq * 2);
+          const rbf16x8_t q = *reinterpret_cast<const rbf16x8_t *>(tile + (16 + (lane & 15)) * kWtRowBytes + kq * 2);
+          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+          __builtin_amdgcn_wave_barrier();   // every lane has read before the next block lands
+          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
           for (int b = 0; b < TB; ++b) {
-            acc0[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[v][b][h], p[v][h], acc0[b], 0, 0, 0);
-            acc1[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[v][b][h], q[v][h], acc1[b], 0, 0, 0);
+            acc0[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[v][b][h], p, acc0[b], 0, 0, 0);
+            acc1[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[v][b][h], q, acc1[b], 0, 0, 0);
           }
+        }
       }
     }
   }
@@ -526,6 +562,7 @@ __global__ __launch_bounds__(512) void router_mfma_narrow_kernel(const bf16_t *_
       part[wv][r * kNarrowRows + (lane & 15)] = acc0[b][i];
       part[wv][r * kNarrowRows + 16 + (lane & 15)] = acc1[b][i];
     }
+  if (threadIdx.x < kNarrowMaxE) cnt[threadIdx.x] = 0;
   __syncthreads();
   float sum[TB];
 #pragma unroll
@@ -550,7 +587,10 @@ __global__ __launch_bounds__(512) void router_mfma_narrow_kernel(const bf16_t *_
   if (!topk.ids) return;   // block-uniform
   __syncthreads();
   if (threadIdx.x < TT && t0 + (int)threadIdx.x < T)
-    topk_one_token(lg + threadIdx.x * E, E, t0 + threadIdx.x, topk);
+    topk_one_token(lg + threadIdx.x * E, E, t0 + threadIdx.x, topk, blk_cnt ? cnt : nullptr);
+  if (!blk_cnt) return;
+  __syncthreads();
+  if (threadIdx.x < E) blk_cnt[(size_t)blockIdx.x * E + threadIdx.x] = cnt[threadIdx.x];
 }
 
 // ----------------------------------------------------------------------------------------
@@ -564,9 +604,13 @@ __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ log
                                                    int k, int kden, int renorm, int want_key,
                                                    int32_t *__restrict__ ids,
                                                    float *__restrict__ gates,
-                                                   float *__restrict__ keys) {
+                                                   float *__restrict__ keys,
+                                                   int32_t *__restrict__ blk_cnt) {
   extern __shared__ float qsh[];   // [256/G][E] when want_key
+  __shared__ int cnt[kBlkMaxE];    // picks per expert of this workgroup's tokens (blk_cnt)
   const int gl = threadIdx.x % G, gi = threadIdx.x / G;
+  if (blk_cnt && threadIdx.x < E) cnt[threadIdx.x] = 0;
+  if (blk_cnt) __syncthreads();
   const int t = blockIdx.x * (256 / G) + gi;
   const bool live = t < T;
   const int npl = (E + G - 1) / G;   // logits per lane (<= MAXPL)
@@ -602,6 +646,7 @@ __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ log
     if (gl == 0 && live) {
       ids[(size_t)t * k + r] = be;
       gates[(size_t)t * k + r] = q;   // numerator for now
+      if (blk_cnt) atomicAdd(&cnt[be], 1);   // LDS integer add: order does not matter
     }
   }
   float denom = qsum;
@@ -618,6 +663,10 @@ __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ log
   }
   if (gl == 0 && live) {
     for (int r = 0; r < k; ++r) gates[(size_t)t * k + r] = gates[(size_t)t * k + r] / denom;
+  }
+  if (blk_cnt) {   // block-uniform
+    __syncthreads();
+    if (threadIdx.x < E) blk_cnt[(size_t)blockIdx.x * E + threadIdx.x] = cnt[threadIdx.x];
   }
   if (want_key) {
     float *qrow = qsh + gi * E;
@@ -739,6 +788,120 @@ __global__ __launch_bounds__(256) void topk_merge_kernel(const float *__restrict
       for (int r = 0; r < PL; ++r)
         if (r < k) keys[(size_t)t * k + r] = qrow[a[r].e] / S;
     }
+  }
+}
+
+// ----------------------------------------------------------------------------------------
+// Dispatch of token choice without a capacity limit, in one launch, from the per-block expert
+// counts the top-k (inside the narrow router or in topk_kernel) left: blk_cnt[b][e] = picks of
+// expert e among tokens [bt*b, bt*b + bt). Workgroup w takes tokens [256w, 256w + 256) (a
+// whole number of count blocks, bt dividing 256). It sums the count rows of all blocks, and of
+// the blocks before its own, in a fixed order (integer sums), which gives the expert offsets
+// (exclusive scan over experts) and where each expert's rows of its blocks start; a token's
+// rank inside its count block comes from the picks of the block's earlier tokens. Pair (t, j)
+// of expert e goes to offsets[e] + (pairs of e among tokens before t): ascending token inside
+// an expert, as the general dispatch does. Every pair is kept, so token t owns CSR entries
+// t k .. t k + k - 1 in slot order. Workgroup 0 also writes counts and offsets.
+constexpr int kBlkPerWg = 256 / 16;   // count blocks per dispatch workgroup (bt >= 16)
+
+template <int EM>   // experts handled: E <= EM (8 or 16)
+__global__ __launch_bounds__(256) void dispatch_blocks_kernel(
+    const int32_t *__restrict__ ids, const float *__restrict__ gates, int T, int k, int E,
+    const int32_t *__restrict__ blk_cnt, int bt, int32_t *__restrict__ counts,
+    int32_t *__restrict__ offsets, int32_t *__restrict__ perm_token, float *__restrict__ perm_w,
+    uint8_t *__restrict__ kept, int32_t *__restrict__ tok_ptr, int32_t *__restrict__ tok_pos) {
+  __shared__ int wsum[256 / 64][2 * EM];
+  __shared__ int colc[kBlkPerWg][EM];
+  __shared__ int base[kBlkPerWg][EM];
+  __shared__ int off[EM];
+  __shared__ unsigned long long wball[256 / 64][EM];
+  __shared__ int sids[256 * EM];
+  __shared__ float sgate[256 * EM];
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int nblk = (T + bt - 1) / bt;
+  const int t0 = blockIdx.x * 256, b0 = t0 / bt;
+  const int nb = min(256 / bt, nblk - b0);   // count blocks of this workgroup
+  const int t = t0 + threadIdx.x;
+  // this workgroup's picks and gates (contiguous rows) and its blocks' count rows: their
+  // loads go out first and travel while the other blocks' counts are summed
+  const int nown = (min(T, t0 + 256) - t0) * k;
+  for (int i = threadIdx.x; i < nown; i += 256) {
+    sids[i] = ids[(size_t)t0 * k + i];
+    sgate[i] = gates[(size_t)t0 * k + i];
+  }
+  {
+    const int eb = threadIdx.x % EM, bb = threadIdx.x / EM;
+    if (bb < kBlkPerWg)
+      colc[bb][eb] = (eb < E && bb < nb) ? blk_cnt[(size_t)(b0 + bb) * E + eb] : 0;
+  }
+  // per expert: picks of all blocks (va) and of the blocks before b0 (vp); thread i adds rows
+  // i, i + 256, ... (integer sums: the order does not change them)
+  int va[EM], vp[EM];
+#pragma unroll
+  for (int e = 0; e < EM; ++e) va[e] = vp[e] = 0;
+  for (int r = threadIdx.x; r < nblk; r += 256) {
+    int c[EM];
+#pragma unroll
+    for (int e = 0; e < EM; ++e) c[e] = blk_cnt[(size_t)r * E + min(e, E - 1)];
+#pragma unroll
+    for (int e = 0; e < EM; ++e) {
+      const int ce = e < E ? c[e] : 0;
+      va[e] += ce;
+      vp[e] += r < b0 ? ce : 0;
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < EM; ++e) {
+    const int a = wave_sum_int(va[e]), b = wave_sum_int(vp[e]);
+    if (lane == 0) { wsum[wid][e] = a; wsum[wid][EM + e] = b; }
+  }
+  __syncthreads();
+  // expert offsets (exclusive scan over experts), where this workgroup's blocks start inside
+  // every expert, and each wave's expert masks for the ranks
+  if (threadIdx.x == 0) {
+    int run = 0;
+    for (int e = 0; e < E; ++e) {
+      const int all = wsum[0][e] + wsum[1][e] + wsum[2][e] + wsum[3][e];
+      off[e] = run;
+      if (blockIdx.x == 0) { counts[e] = all; offsets[e] = run; }
+      run += all;
+    }
+    if (blockIdx.x == 0) offsets[E] = run;
+  }
+  if (threadIdx.x < E) {
+    const int e = threadIdx.x;
+    int run = wsum[0][EM + e] + wsum[1][EM + e] + wsum[2][EM + e] + wsum[3][EM + e];
+#pragma unroll
+    for (int b = 0; b < kBlkPerWg; ++b) {
+      base[b][e] = run;
+      run += colc[b][e];
+    }
+  }
+  uint32_t mine = 0u;   // experts this token picked
+  if (t < T)
+    for (int j = 0; j < k; ++j) mine |= 1u << sids[threadIdx.x * k + j];
+#pragma unroll
+  for (int e = 0; e < EM; ++e) {
+    const unsigned long long m = __ballot((mine >> e) & 1u);
+    if (lane == 0) wball[wid][e] = m;
+  }
+  __syncthreads();
+  if (t >= T) return;
+  // each pair's position: pairs of its expert among the earlier tokens of its count block
+  // (count blocks of 16 or 32 tokens lie inside one wave: a ballot gives them)
+  const int lb = threadIdx.x / bt;
+  const int first_lane = lane - (threadIdx.x % bt);
+  const unsigned long long before = ((1ull << lane) - 1ull) & ~((1ull << first_lane) - 1ull);
+  tok_ptr[t] = t * k;
+  if (t == T - 1) tok_ptr[T] = T * k;
+  for (int j = 0; j < k; ++j) {
+    const int e = sids[threadIdx.x * k + j];
+    const int rank = __popcll(wball[wid][e] & before);
+    const int pos = off[e] + base[lb][e] + rank;
+    perm_token[pos] = t;
+    perm_w[pos] = sgate[threadIdx.x * k + j];
+    tok_pos[(size_t)t * k + j] = pos;
+    if (kept) kept[(size_t)t * k + j] = 1;
   }
 }
 
@@ -1340,28 +1503,28 @@ bool router_narrow_mfma(int dtype, int d, int E) {
 }
 
 size_t router_w3_bytes(int dtype, int d, int E) {
-  if (router_narrow_mfma(dtype, d, E)) return (size_t)kNarrowRows * router_w3_ld(d) * 2;
+  if (router_narrow_mfma(dtype, d, E)) return 0;   // splits W_r in registers
   if (dtype == 1 && E > 8 && d % 64 == 0) return 3 * (size_t)router_epad(E) * router_w3_ld(d) * 2;
   return 0;
 }
 
 hipError_t launch_router(int dtype, const void *x, const float *w, const float *bias,
                          float *logits, int T, int d, int E, bf16_t *w3, hipStream_t st,
-                         const TopkOut *topk, bool *topk_done) {
+                         const TopkOut *topk, bool *topk_done, int *cnt_block) {
   if (topk_done) *topk_done = false;
+  if (cnt_block) *cnt_block = 0;
   if (router_narrow_mfma(dtype, d, E)) {
-    const TopkOut tk = topk ? *topk : TopkOut{0, 0, 0, 0, nullptr, nullptr, nullptr};
+    const TopkOut tk = topk ? *topk : TopkOut{0, 0, 0, 0, nullptr, nullptr, nullptr, nullptr};
     if (topk && topk_done) *topk_done = true;
-    const size_t n = (size_t)kNarrowRows * d;
-    int g = (int)((n + 255) / 256);
-    if (g > 1024) g = 1024;
-    hipLaunchKernelGGL(router_split_narrow_kernel, dim3(g), dim3(256), 0, st, w, d, E, w3);
-    if (T >= 16 * 2 * 256)   // two token blocks per workgroup halve the W-part reads
-      hipLaunchKernelGGL(router_mfma_narrow_kernel<2>, dim3((T + 31) / 32), dim3(512), 0, st,
-                         (const bf16_t *)x, w3, bias, logits, T, d, E, tk);
-    else
-      hipLaunchKernelGGL(router_mfma_narrow_kernel<1>, dim3((T + 15) / 16), dim3(512), 0, st,
-                         (const bf16_t *)x, w3, bias, logits, T, d, E, tk);
+    const int tb = T >= 16 * 2 * 256 ? 2 : 1;   // two token blocks per workgroup halve the W reads
+    if (tk.blk_cnt && cnt_block) *cnt_block = 16 * tb;
+#define MOE_NARROW(TBB, NCHH) hipLaunchKernelGGL((router_mfma_narrow_kernel<TBB, NCHH>),          \
+                                               dim3((T + 16 * TBB - 1) / (16 * TBB)), dim3(512), 0, \
+                                               st, (const bf16_t *)x, w, bias, logits, T, d, E, tk, \
+                                               tk.blk_cnt)
+    if (tb == 2) { if (E <= 8) MOE_NARROW(2, 1); else MOE_NARROW(2, 2); }
+    else { if (E <= 8) MOE_NARROW(1, 1); else MOE_NARROW(1, 2); }
+#undef MOE_NARROW
     return hipGetLastError();
   }
   if (dtype == 1 && E > 8 && d % 64 == 0) {
@@ -1394,7 +1557,10 @@ hipError_t launch_router(int dtype, const void *x, const float *w, const float *
 }
 
 hipError_t launch_topk(const float *logits, int T, int E, int k, int kden, int renorm,
-                       int want_key, int32_t *ids, float *gates, float *keys, hipStream_t st) {
+                       int want_key, int32_t *ids, float *gates, float *keys, hipStream_t st,
+                       int32_t *blk_cnt, int *cnt_block) {
+  if (cnt_block) *cnt_block = 0;
+  if (E > kBlkMaxE) blk_cnt = nullptr;
   // G lanes per token, each holding up to PL logits: narrow rows keep one logit per lane;
   // up to 128 experts use 16 lanes x 8 (16 tokens per block): merged sorted lists for
   // k = 5..8, else a 4-step butterfly per pick
@@ -1406,8 +1572,10 @@ hipError_t launch_topk(const float *logits, int T, int E, int k, int kden, int r
   const int tpb = 256 / G;
   const size_t sh = want_key ? (size_t)tpb * E * sizeof(float) : 0;
   dim3 grid((T + tpb - 1) / tpb);
+  if (blk_cnt && cnt_block) *cnt_block = tpb;   // E <= 16: G = 8 or 16, one logit per lane
 #define MOE_TOPK(GG, PL) hipLaunchKernelGGL((topk_kernel<GG, PL>), grid, dim3(256), sh, st, logits, \
-                                            T, E, k, kden, renorm, want_key, ids, gates, keys)
+                                            T, E, k, kden, renorm, want_key, ids, gates, keys, \
+                                            blk_cnt)
   if (E <= 8) MOE_TOPK(8, 1);
   else if (E <= 16) MOE_TOPK(16, 1);
   else if (E <= 32) MOE_TOPK(32, 1);
@@ -1462,6 +1630,24 @@ void assign_pairs(const RouteScratch &s, const int32_t *ids, const float *gates,
 }
 
 }  // namespace
+
+hipError_t launch_dispatch_blocks(const int32_t *ids, const float *gates, int T, int k, int E,
+                                  const int32_t *blk_cnt, int bt, int32_t *counts,
+                                  int32_t *offsets, int32_t *perm_token, float *perm_w,
+                                  uint8_t *kept, int32_t *tok_ptr, int32_t *tok_pos,
+                                  hipStream_t st) {
+  if (E > kBlkMaxE || bt < 256 / kBlkPerWg || bt > 64 || 256 % bt != 0)
+    return hipErrorInvalidValue;
+  if (E <= 8)
+    hipLaunchKernelGGL(dispatch_blocks_kernel<8>, dim3((T + 255) / 256), dim3(256), 0, st, ids,
+                       gates, T, k, E, blk_cnt, bt, counts, offsets, perm_token, perm_w, kept,
+                       tok_ptr, tok_pos);
+  else
+    hipLaunchKernelGGL(dispatch_blocks_kernel<16>, dim3((T + 255) / 256), dim3(256), 0, st, ids,
+                       gates, T, k, E, blk_cnt, bt, counts, offsets, perm_token, perm_w, kept,
+                       tok_ptr, tok_pos);
+  return hipGetLastError();
+}
 
 hipError_t launch_token_dispatch(const RouteScratch &s, const int32_t *ids, const float *gates,
                                  int T, int k, int E, int C, int32_t *perm_token, float *perm_w,
