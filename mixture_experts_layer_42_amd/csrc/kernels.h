@@ -94,13 +94,32 @@ hipError_t launch_router(int dtype, const void *x, const float *w, const float *
 hipError_t launch_topk(const float *logits, int T, int E, int k, int kden, int renorm,
                        int want_key, int32_t *ids, float *gates, float *keys, hipStream_t st,
                        int32_t *blk_cnt = nullptr, int *cnt_block = nullptr);
-// token choice without a capacity limit: counts, offsets, permutation and the token CSR in one
-// launch from the per-block counts of the top-k (blocks of bt tokens, bt in {16, 32})
+// Outputs of the one-launch dispatch from per-block top-k counts (E <= 16). Final mode (token
+// choice without a capacity limit): counts, offsets, perm_token, perm_w, the token CSR and
+// kept (optional). Candidate mode (cand_slot non-null, before a capacity selection): counts /
+// offsets are the candidates per expert, perm_token / perm_w / cand_slot / cand_key the
+// candidate lists (routing keys read from keys), cnt_fin / off_fin the counts and offsets
+// capped at C.
+struct BlkDispatchOut {
+  int32_t *counts, *offsets, *perm_token;
+  float *perm_w;
+  uint8_t *kept;
+  int32_t *tok_ptr, *tok_pos;
+  const float *keys;
+  int32_t *cand_slot;
+  float *cand_key;
+  int32_t *cnt_fin, *off_fin;
+  int C;
+};
+// one launch from the per-block counts of the top-k (blocks of bt tokens, bt in {16, 32})
 hipError_t launch_dispatch_blocks(const int32_t *ids, const float *gates, int T, int k, int E,
-                                  const int32_t *blk_cnt, int bt, int32_t *counts,
-                                  int32_t *offsets, int32_t *perm_token, float *perm_w,
-                                  uint8_t *kept, int32_t *tok_ptr, int32_t *tok_pos,
+                                  const int32_t *blk_cnt, int bt, const BlkDispatchOut &o,
                                   hipStream_t st);
+// capacity selection of candidate lists already grouped per expert (cnt_pre / off_pre), final
+// mode: the kept rows to perm_token / perm_w at off_fin, slot_pos and kept per (token, slot)
+hipError_t launch_cap_select_final(const RouteScratch &s, int E, int C, int S, int32_t *perm_token,
+                                   float *perm_w, uint8_t *kept, const int32_t *off_fin,
+                                   hipStream_t st);
 // with C < 0 (no capacity) and tok_ptr/tok_pos non-null the token -> rows CSR is written too
 hipError_t launch_token_dispatch(const RouteScratch &s, const int32_t *ids, const float *gates,
                                  int T, int k, int E, int C, int32_t *perm_token, float *perm_w,

@@ -283,9 +283,10 @@ hipError_t do_route(const moe_problem &p, const void *x, const float *w_router,
   const RouteScratch s = scratch_of(L, ws);
   hipError_t e;
   const int C = capacity_of(p);
-  // token choice keeping every pair with at most 16 experts: the top-k counts its picks per
-  // workgroup and one launch does the whole dispatch from those counts
-  const bool blk_dispatch = p.routing == MOE_TOKEN_CHOICE && C < 0 && p.expand_m == 0 &&
+  // token choice with at most 16 experts (plain, or with the per-expert token drop): the top-k
+  // counts its picks per workgroup and one launch does the dispatch from those counts (with a
+  // capacity: the candidate lists the selection reads)
+  const bool blk_dispatch = p.routing == MOE_TOKEN_CHOICE && p.expand_m == 0 &&
                             p.cap_groups == 0 && p.E <= kBlkCountMaxE;
   const TopkOut tk{p.k + p.expand_m, p.k, p.renorm_topk, C >= 0 ? 1 : 0, r.topk_ids, r.topk_w,
                    s.keys, blk_dispatch ? s.blk_cnt : nullptr};
@@ -302,10 +303,24 @@ hipError_t do_route(const moe_problem &p, const void *x, const float *w_router,
       e = launch_topk(r.logits, p.T, p.E, tk.k, tk.kden, tk.renorm, tk.want_key, r.topk_ids,
                       r.topk_w, s.keys, st, tk.blk_cnt, &cnt_block);
     if (e != hipSuccess) return e;
-    if (blk_dispatch && cnt_block > 0)
-      return launch_dispatch_blocks(r.topk_ids, r.topk_w, p.T, p.k, p.E, s.blk_cnt, cnt_block,
-                                    r.counts, r.offsets, r.perm_token, r.perm_w, r.kept,
-                                    r.tok_ptr, r.tok_pos, st);
+    if (blk_dispatch && cnt_block > 0) {
+      BlkDispatchOut o{};
+      if (C < 0) {   // every pair kept: the dispatch writes the token CSR as well
+        o.counts = r.counts; o.offsets = r.offsets; o.perm_token = r.perm_token;
+        o.perm_w = r.perm_w; o.kept = r.kept; o.tok_ptr = r.tok_ptr; o.tok_pos = r.tok_pos;
+        return launch_dispatch_blocks(r.topk_ids, r.topk_w, p.T, p.k, p.E, s.blk_cnt, cnt_block,
+                                      o, st);
+      }
+      o.counts = s.cnt_pre; o.offsets = s.off_pre; o.perm_token = s.cand_token;
+      o.perm_w = s.cand_w; o.keys = s.keys; o.cand_slot = s.cand_slot; o.cand_key = s.cand_key;
+      o.cnt_fin = r.counts; o.off_fin = r.offsets; o.C = C;
+      e = launch_dispatch_blocks(r.topk_ids, r.topk_w, p.T, p.k, p.E, s.blk_cnt, cnt_block, o,
+                                 st);
+      if (e != hipSuccess) return e;
+      e = launch_cap_select_final(s, p.E, C, p.k, r.perm_token, r.perm_w, r.kept, r.offsets, st);
+      if (e != hipSuccess) return e;
+      return launch_token_csr(s, p.T, slot_width(p), r.tok_ptr, r.tok_pos, st);
+    }
     if (p.cap_groups > 0)
       e = launch_group_capacity(s, r.topk_ids, r.topk_w, p.T, p.k, p.E, p.cap_groups,
                                 group_capacity_of(p), r.perm_token, r.perm_w, r.kept, r.counts,

@@ -805,11 +805,11 @@ __global__ __launch_bounds__(256) void topk_merge_kernel(const float *__restrict
 constexpr int kBlkPerWg = 256 / 16;   // count blocks per dispatch workgroup (bt >= 16)
 
 template <int EM>   // experts handled: E <= EM (8 or 16)
-__global__ __launch_bounds__(256) void dispatch_blocks_kernel(
-    const int32_t *__restrict__ ids, const float *__restrict__ gates, int T, int k, int E,
-    const int32_t *__restrict__ blk_cnt, int bt, int32_t *__restrict__ counts,
-    int32_t *__restrict__ offsets, int32_t *__restrict__ perm_token, float *__restrict__ perm_w,
-    uint8_t *__restrict__ kept, int32_t *__restrict__ tok_ptr, int32_t *__restrict__ tok_pos) {
+__global__ __launch_bounds__(256) void dispatch_blocks_kernel(const int32_t *__restrict__ ids,
+                                                              const float *__restrict__ gates,
+                                                              int T, int k, int E,
+                                                              const int32_t *__restrict__ blk_cnt,
+                                                              int bt, BlkDispatchOut o) {
   __shared__ int wsum[256 / 64][2 * EM];
   __shared__ int colc[kBlkPerWg][EM];
   __shared__ int base[kBlkPerWg][EM];
@@ -817,6 +817,7 @@ __global__ __launch_bounds__(256) void dispatch_blocks_kernel(
   __shared__ unsigned long long wball[256 / 64][EM];
   __shared__ int sids[256 * EM];
   __shared__ float sgate[256 * EM];
+  const bool cand = o.cand_slot != nullptr;   // candidate lists for the capacity selection
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int nblk = (T + bt - 1) / bt;
   const int t0 = blockIdx.x * 256, b0 = t0 / bt;
@@ -857,16 +858,29 @@ __global__ __launch_bounds__(256) void dispatch_blocks_kernel(
   }
   __syncthreads();
   // expert offsets (exclusive scan over experts), where this workgroup's blocks start inside
-  // every expert, and each wave's expert masks for the ranks
+  // every expert, and each wave's expert masks for the ranks; with candidate lists also the
+  // capacity-capped counts and offsets of the final rows
   if (threadIdx.x == 0) {
-    int run = 0;
+    int run = 0, run_fin = 0;
     for (int e = 0; e < E; ++e) {
       const int all = wsum[0][e] + wsum[1][e] + wsum[2][e] + wsum[3][e];
       off[e] = run;
-      if (blockIdx.x == 0) { counts[e] = all; offsets[e] = run; }
+      if (blockIdx.x == 0) {
+        o.counts[e] = all;
+        o.offsets[e] = run;
+        if (cand) {
+          const int kc = min(all, o.C);
+          o.cnt_fin[e] = kc;
+          o.off_fin[e] = run_fin;
+          run_fin += kc;
+        }
+      }
       run += all;
     }
-    if (blockIdx.x == 0) offsets[E] = run;
+    if (blockIdx.x == 0) {
+      o.offsets[E] = run;
+      if (cand) o.off_fin[E] = run_fin;
+    }
   }
   if (threadIdx.x < E) {
     const int e = threadIdx.x;
@@ -892,16 +906,23 @@ __global__ __launch_bounds__(256) void dispatch_blocks_kernel(
   const int lb = threadIdx.x / bt;
   const int first_lane = lane - (threadIdx.x % bt);
   const unsigned long long before = ((1ull << lane) - 1ull) & ~((1ull << first_lane) - 1ull);
-  tok_ptr[t] = t * k;
-  if (t == T - 1) tok_ptr[T] = T * k;
+  if (!cand) {
+    o.tok_ptr[t] = t * k;
+    if (t == T - 1) o.tok_ptr[T] = T * k;
+  }
   for (int j = 0; j < k; ++j) {
     const int e = sids[threadIdx.x * k + j];
     const int rank = __popcll(wball[wid][e] & before);
     const int pos = off[e] + base[lb][e] + rank;
-    perm_token[pos] = t;
-    perm_w[pos] = sgate[threadIdx.x * k + j];
-    tok_pos[(size_t)t * k + j] = pos;
-    if (kept) kept[(size_t)t * k + j] = 1;
+    o.perm_token[pos] = t;
+    o.perm_w[pos] = sgate[threadIdx.x * k + j];
+    if (cand) {
+      o.cand_slot[pos] = j;
+      o.cand_key[pos] = o.keys[(size_t)t * k + j];
+    } else {
+      o.tok_pos[(size_t)t * k + j] = pos;
+      if (o.kept) o.kept[(size_t)t * k + j] = 1;
+    }
   }
 }
 
@@ -1383,6 +1404,79 @@ __global__ __launch_bounds__(1024) void ec_select_kernel(const float *__restrict
   }
 }
 
+// The same selection with the column held in registers (T <= 1024 KPT): thread tid owns
+// tokens tid + 1024 j (chunk j), so ranks taken chunk by chunk, threads in order, follow
+// ascending token. One pass reads the column; the radix selection and the ordered
+// compaction (two vector scans) work on registers and LDS only.
+template <int KPT>
+__global__ __launch_bounds__(1024) void ec_select_regs_kernel(const float *__restrict__ logits,
+                                                              int T, int E, int c,
+                                                              int32_t *__restrict__ perm_token,
+                                                              float *__restrict__ perm_w,
+                                                              int32_t *__restrict__ slot_pos,
+                                                              int32_t *__restrict__ counts,
+                                                              int32_t *__restrict__ offsets) {
+  __shared__ int hist[kSelWaves * 256];
+  __shared__ int sm[kSelWaves * KPT + KPT];
+  __shared__ float fsm[1024 / 64];
+  const int e = blockIdx.x;
+  float v[KPT];
+  uint32_t u[KPT];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) {
+    const int t = threadIdx.x + 1024 * j;
+    v[j] = t < T ? logits[(size_t)t * E + e] : -INFINITY;
+    u[j] = t < T ? float_key(v[j]) : 0u;
+    mx = fmaxf(mx, v[j]);
+  }
+  mx = block_max(mx, fsm);
+  float sum = 0.f;
+#pragma unroll
+  for (int j = 0; j < KPT; ++j)
+    if (threadIdx.x + 1024 * j < T) sum += expf(v[j] - mx);
+  const float Z = block_sum(sum, fsm);
+  const SelectResult sr = block_radix_select_regs<KPT>(u, T, c, hist, sm);
+  int eq[KPT], eq_tot[KPT];
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) eq[j] = (threadIdx.x + 1024 * j < T && u[j] == sr.tau) ? 1 : 0;
+  block_excl_scan_vec<KPT>(eq, sm, eq_tot);
+  int sel[KPT], sel_tot[KPT];
+  int run = 0;
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) {
+    const bool in = threadIdx.x + 1024 * j < T;
+    const bool self = in && (u[j] > sr.tau || (u[j] == sr.tau && run + eq[j] < sr.need_eq));
+    run += eq_tot[j];
+    sel[j] = self ? 1 : 0;
+  }
+  int flag[KPT];
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) flag[j] = sel[j];
+  block_excl_scan_vec<KPT>(sel, sm, sel_tot);
+  run = 0;
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) {
+    const int t = threadIdx.x + 1024 * j;
+    if (t < T) {
+      if (flag[j]) {
+        const int q = e * c + run + sel[j];
+        perm_token[q] = t;
+        perm_w[q] = expf(v[j] - mx) / Z;
+        slot_pos[(size_t)t * E + e] = q;
+      } else {
+        slot_pos[(size_t)t * E + e] = -1;
+      }
+    }
+    run += sel_tot[j];
+  }
+  if (threadIdx.x == 0) {
+    counts[e] = c;
+    offsets[e] = e * c;
+    if (e == E - 1) offsets[E] = E * c;
+  }
+}
+
 // ----------------------------------------------------------------------------------------
 // CSR over tokens from the slot table slot_pos[T, S] (row index or -1): per-block totals,
 // one scan over blocks, then per-token offsets and the row lists in slot order.
@@ -1429,6 +1523,42 @@ __global__ __launch_bounds__(256) void tok_write_kernel(const int32_t *__restric
     tok_ptr[t] = p;
     for (int s = 0; s < S; ++s) {
       const int v = slot_pos[(size_t)t * S + s];
+      if (v >= 0) tok_pos[p++] = v;
+    }
+    if (t == T - 1) tok_ptr[T] = p;
+  }
+}
+
+// The scan and the write in one launch when there are at most kCsrFusedBlocks blocks: each
+// block adds the totals of the blocks before it itself (integer sums, fixed order per thread,
+// then a block-wide sum), instead of a separate scan kernel.
+constexpr int kCsrFusedBlocks = 1024;
+
+__global__ __launch_bounds__(256) void tok_write_fused_kernel(const int32_t *__restrict__ slot_pos,
+                                                              int T, int S,
+                                                              const int32_t *__restrict__ blk_sum,
+                                                              int32_t *__restrict__ tok_ptr,
+                                                              int32_t *__restrict__ tok_pos) {
+  __shared__ int sm[256 / 64 + 1];
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  int c = 0;
+  if (t < T)
+    for (int j = 0; j < S; ++j) c += slot_pos[(size_t)t * S + j] >= 0;
+  int before = 0;
+  for (int b = threadIdx.x; b < (int)blockIdx.x; b += 256) before += blk_sum[b];
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  before = wave_sum_int(before);
+  if (lane == 0) sm[wid] = before;
+  __syncthreads();
+  const int base = sm[0] + sm[1] + sm[2] + sm[3];
+  __syncthreads();
+  int tot;
+  const int ex = block_excl_scan(c, sm, &tot);
+  if (t < T) {
+    int p = base + ex;
+    tok_ptr[t] = p;
+    for (int j = 0; j < S; ++j) {
+      const int v = slot_pos[(size_t)t * S + j];
       if (v >= 0) tok_pos[p++] = v;
     }
     if (t == T - 1) tok_ptr[T] = p;
@@ -1632,20 +1762,25 @@ void assign_pairs(const RouteScratch &s, const int32_t *ids, const float *gates,
 }  // namespace
 
 hipError_t launch_dispatch_blocks(const int32_t *ids, const float *gates, int T, int k, int E,
-                                  const int32_t *blk_cnt, int bt, int32_t *counts,
-                                  int32_t *offsets, int32_t *perm_token, float *perm_w,
-                                  uint8_t *kept, int32_t *tok_ptr, int32_t *tok_pos,
+                                  const int32_t *blk_cnt, int bt, const BlkDispatchOut &o,
                                   hipStream_t st) {
   if (E > kBlkMaxE || bt < 256 / kBlkPerWg || bt > 64 || 256 % bt != 0)
     return hipErrorInvalidValue;
   if (E <= 8)
     hipLaunchKernelGGL(dispatch_blocks_kernel<8>, dim3((T + 255) / 256), dim3(256), 0, st, ids,
-                       gates, T, k, E, blk_cnt, bt, counts, offsets, perm_token, perm_w, kept,
-                       tok_ptr, tok_pos);
+                       gates, T, k, E, blk_cnt, bt, o);
   else
     hipLaunchKernelGGL(dispatch_blocks_kernel<16>, dim3((T + 255) / 256), dim3(256), 0, st, ids,
-                       gates, T, k, E, blk_cnt, bt, counts, offsets, perm_token, perm_w, kept,
-                       tok_ptr, tok_pos);
+                       gates, T, k, E, blk_cnt, bt, o);
+  return hipGetLastError();
+}
+
+hipError_t launch_cap_select_final(const RouteScratch &s, int E, int C, int S, int32_t *perm_token,
+                                   float *perm_w, uint8_t *kept, const int32_t *off_fin,
+                                   hipStream_t st) {
+  hipLaunchKernelGGL(cap_select_kernel, dim3(E), dim3(1024), 0, st, s.cand_token, s.cand_slot,
+                     s.cand_key, s.cand_w, s.cnt_pre, s.off_pre, off_fin, C,
+                     (const int32_t *)nullptr, S, perm_token, perm_w, s.slot_pos, kept);
   return hipGetLastError();
 }
 
@@ -1737,14 +1872,29 @@ hipError_t launch_expanded_drop(const RouteScratch &s, const int32_t *ids, const
 hipError_t launch_expert_choice(const RouteScratch &s, const float *logits, int T, int E, int c,
                                 int32_t *perm_token, float *perm_w, int32_t *counts,
                                 int32_t *offsets, hipStream_t st) {
-  hipLaunchKernelGGL(ec_select_kernel, dim3(E), dim3(1024), 0, st, logits, T, E, c, s.colkeys,
-                     perm_token, perm_w, s.slot_pos, counts, offsets);
+#define MOE_EC(K) hipLaunchKernelGGL((ec_select_regs_kernel<K>), dim3(E), dim3(1024), 0, st, logits, \
+                                     T, E, c, perm_token, perm_w, s.slot_pos, counts, offsets)
+  if (T <= 2048) MOE_EC(2);
+  else if (T <= 4096) MOE_EC(4);
+  else if (T <= 8192) MOE_EC(8);
+  else if (T <= 16384) MOE_EC(16);
+  else
+    hipLaunchKernelGGL(ec_select_kernel, dim3(E), dim3(1024), 0, st, logits, T, E, c, s.colkeys,
+                       perm_token, perm_w, s.slot_pos, counts, offsets);
+#undef MOE_EC
   return hipGetLastError();
 }
 
 hipError_t launch_token_csr(const RouteScratch &s, int T, int S, int32_t *tok_ptr,
                             int32_t *tok_pos, hipStream_t st) {
   const int nblk = (T + 255) / 256;
+  if (nblk <= kCsrFusedBlocks) {   // two launches instead of three
+    hipLaunchKernelGGL(tok_count_kernel, dim3(nblk), dim3(256), 0, st, s.slot_pos, T, S,
+                       s.tok_blk);
+    hipLaunchKernelGGL(tok_write_fused_kernel, dim3(nblk), dim3(256), 0, st, s.slot_pos, T, S,
+                       s.tok_blk, tok_ptr, tok_pos);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(tok_count_kernel, dim3(nblk), dim3(256), 0, st, s.slot_pos, T, S,
                      s.tok_blk);
   hipLaunchKernelGGL(blk_scan_kernel, dim3(1), dim3(1024), 0, st, s.tok_blk, nblk, s.tok_blk_off,
