@@ -23,6 +23,8 @@
 //
 // float32 path (used when the problem dtype is float32): a plain LDS-tiled SIMT GEMM over
 // the same tile list.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -266,55 +268,117 @@ template <int W> MOE_DEV int part_index(int tr, int tc, int MB) {
   return row_part + col_part;
 }
 
-// One unit: a row tile of 64*MB rows x 256 B-columns over K-steps [k_begin, k_begin + nk),
-// stored whole (punit < 0) or as the float32 partial tile punit.
+// A unit of work: a row tile of 64*mb rows x 256 B-columns of group d over K-steps
+// [k_begin, k_begin + nk), stored whole (punit < 0) or as the float32 partial tile punit.
+struct Unit {
+  GroupDesc d;
+  int n_tile, m0, nk, k_begin, punit, mb;
+};
+
+// The fields of a unit are the same in every lane; readfirstlane keeps them in scalar registers
+// (the buffer resources built from its pointers must be scalar operands)
+MOE_DEV int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
+template <typename P> MOE_DEV P *uni_ptr(P *p) {
+  const uint64_t v = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (P *)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
+MOE_DEV void make_uniform(Unit &x) {
+  x.d.A = uni_ptr(x.d.A); x.d.amap = uni_ptr(x.d.amap); x.d.B0 = uni_ptr(x.d.B0);
+  x.d.B1 = uni_ptr(x.d.B1); x.d.C = uni_ptr(x.d.C);
+  x.d.rows = uni(x.d.rows); x.d.N = uni(x.d.N); x.d.K = uni(x.d.K); x.d.lda = uni(x.d.lda);
+  x.d.ldc = uni(x.d.ldc);
+  x.n_tile = uni(x.n_tile); x.m0 = uni(x.m0); x.nk = uni(x.nk); x.k_begin = uni(x.k_begin);
+  x.punit = uni(x.punit); x.mb = uni(x.mb);
+}
+
+// Per-lane byte offsets of a unit's copies from the slice bases (A: MB used, B: B_DMA used).
+struct Offs { uint32_t a[4], b[4]; };
+
+// Loader: wave wv fills A rows wv*TBM/W .. and B rows wv*BN/W .. with copies of 1 KB (8 rows of
+// 128 B); lane L fetches row r0 + L/8, physical chunk L%8, i.e. logical K-chunk
+// (L%8) ^ ((row/2)%8). For gate/up the B tile holds, per wave column wn, WCOLS/2 gate rows then
+// the matching WCOLS/2 up rows (h columns n_tile*128 + wn*WCOLS/2 + j), so the B rows a wave
+// loads are all gate (wv even) or all up (wv odd).
 template <bool GATE_UP, int W, int MB>
-MOE_DEV __attribute__((always_inline)) void gemm_tile(const GemmArgs &args, const GroupDesc &d,
-                                                      Stage &st0, Stage &st1, int n_tile, int m0,
-                                                      int nk, int k_begin, int punit) {
+MOE_DEV void unit_offsets(const Unit &x, Offs &o) {
+  using C = Cfg<W>;
+  static_assert(MB <= 4 && C::B_DMA <= 4, "Offs holds 4 + 4 offsets");
+  constexpr int TBM = 64 * MB;
+  constexpr int A_DMA = TBM * kRowBytes / 1024 / W;
+  const int lane = threadIdx.x & 63;
+  const int wvu = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+#pragma unroll
+  for (int i = 0; i < A_DMA; ++i) {
+    const int r = wvu * (TBM / W) + i * 8 + (lane >> 3);
+    const int c = (lane & 7) ^ ((r >> 1) & 7);
+    int arow = min(x.m0 + r, x.d.rows - 1);
+    if (x.d.amap) arow = x.d.amap[arow];   // dispatch gather folded into the operand load
+    o.a[i] = ((uint32_t)arow * (uint32_t)x.d.lda + c * 8) * 2u;
+  }
+#pragma unroll
+  for (int i = 0; i < C::B_DMA; ++i) {
+    const int r = wvu * (BN / W) + i * 8 + (lane >> 3);
+    const int c = (lane & 7) ^ ((r >> 1) & 7);
+    const int n = GATE_UP ? x.n_tile * (BN / 2) + (wvu >> 1) * (C::WCOLS / 2) +
+                                (r & (C::WCOLS / 2 - 1))
+                          : x.n_tile * BN + r;
+    o.b[i] = ((uint32_t)min(n, x.d.N - 1) * (uint32_t)x.d.K + c * 8) * 2u;
+  }
+}
+
+// Copies of K-slice kt of unit x into stage s.
+template <bool GATE_UP, int W, int MB>
+MOE_DEV void unit_issue(const Unit &x, const Offs &o, Stage &s, int kt) {
+  using C = Cfg<W>;
+  constexpr int A_DMA = 64 * MB * kRowBytes / 1024 / W;
+  const int wvu = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+  const char *Ab = (const char *)x.d.A;
+  const char *Bb = (const char *)((GATE_UP && (wvu & 1)) ? x.d.B1 : x.d.B0);
+  const __amdgpu_buffer_rsrc_t ra = operand_rsrc(Ab), rb = operand_rsrc(Bb);
+  const int aofs = wvu * A_DMA * 1024, bofs = wvu * C::B_DMA * 1024;
+  const int so = (x.k_begin + kt) * kRowBytes;   // K offset of the slice, bytes
+#pragma unroll
+  for (int i = 0; i < A_DMA; ++i) b2lds16(ra, o.a[i], so, s.a + aofs + i * 1024);
+#pragma unroll
+  for (int i = 0; i < C::B_DMA; ++i) b2lds16(rb, o.b[i], so, s.b + bofs + i * 1024);
+}
+
+// The offsets of unit x and the copies of its first slice into st0.
+template <bool GATE_UP, int W>
+MOE_DEV void unit_prefetch(const Unit &x, Offs &o, Stage &st0) {
+  switch (x.mb) {
+    case 4: unit_offsets<GATE_UP, W, 4>(x, o); unit_issue<GATE_UP, W, 4>(x, o, st0, 0); break;
+    case 3: unit_offsets<GATE_UP, W, 3>(x, o); unit_issue<GATE_UP, W, 3>(x, o, st0, 0); break;
+    case 2: unit_offsets<GATE_UP, W, 2>(x, o); unit_issue<GATE_UP, W, 2>(x, o, st0, 0); break;
+    default: unit_offsets<GATE_UP, W, 1>(x, o); unit_issue<GATE_UP, W, 1>(x, o, st0, 0); break;
+  }
+}
+
+// One unit, its first slice already in flight into st0. When the previous unit's epilogue
+// left stores in flight (stores_pending: at least 16 of this wave's, issued after this unit's
+// first copies), the first wait lets up to 16 operations stay outstanding: vector-memory
+// operations complete in issue order, so the copies have landed and only stores remain. After
+// the K loop the next unit's first slice is issued before this unit's epilogue, so its copies
+// travel while the outputs are stored. Returns whether this wave's epilogue left stores in
+// flight.
+template <bool GATE_UP, int W, int MB>
+MOE_DEV __attribute__((always_inline)) bool gemm_tile(const GemmArgs &args, const Unit &x,
+                                                      const Offs &o, Stage &st0, Stage &st1,
+                                                      bool stores_pending, bool has_next,
+                                                      const Unit &nx, Offs &no) {
   using C = Cfg<W>;
   constexpr int NB = C::NB;
   constexpr int TBM = 64 * MB;                    // tile rows
   constexpr int A_DMA = TBM * kRowBytes / 1024 / W;   // A copies per wave per slice
   constexpr int DMA = A_DMA + C::B_DMA;
   constexpr int BNOUT = GATE_UP ? BN / 2 : BN;
+  const GroupDesc &d = x.d;
+  const int n_tile = x.n_tile, m0 = x.m0, nk = x.nk, punit = x.punit;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int wm = wv / C::WN, wn = wv % C::WN;
-  // Loader: wave wv fills A rows wv*TBM/W .. and B rows wv*BN/W .. with copies of 1 KB
-  // (8 rows of 128 B); lane L fetches row r0 + L/8, physical chunk L%8, i.e. logical
-  // K-chunk (L%8) ^ ((row/2)%8). For gate/up the B tile holds, per wave column wn,
-  // WCOLS/2 gate rows then the matching WCOLS/2 up rows (h columns n_tile*128 +
-  // wn*WCOLS/2 + j), so the B rows a wave loads are all gate (wv even) or all up (wv odd).
-  const int wvu = __builtin_amdgcn_readfirstlane(wv);   // wave-uniform, kept in SGPRs
-  const char *Ab = (const char *)d.A;
-  const char *Bb = (const char *)((GATE_UP && (wvu & 1)) ? d.B1 : d.B0);
-  uint32_t aoff[A_DMA], boff[C::B_DMA];   // per-lane byte offsets from the slice bases
-#pragma unroll
-  for (int i = 0; i < A_DMA; ++i) {
-    const int r = wvu * (TBM / W) + i * 8 + (lane >> 3);
-    const int c = (lane & 7) ^ ((r >> 1) & 7);
-    int arow = min(m0 + r, d.rows - 1);
-    if (d.amap) arow = d.amap[arow];   // dispatch gather folded into the operand load
-    aoff[i] = ((uint32_t)arow * (uint32_t)d.lda + c * 8) * 2u;
-  }
-#pragma unroll
-  for (int i = 0; i < C::B_DMA; ++i) {
-    const int r = wvu * (BN / W) + i * 8 + (lane >> 3);
-    const int c = (lane & 7) ^ ((r >> 1) & 7);
-    const int n = GATE_UP ? n_tile * (BN / 2) + (wvu >> 1) * (C::WCOLS / 2) +
-                                (r & (C::WCOLS / 2 - 1))
-                          : n_tile * BN + r;
-    boff[i] = ((uint32_t)min(n, d.N - 1) * (uint32_t)d.K + c * 8) * 2u;
-  }
-  const int aofs = wvu * A_DMA * 1024, bofs = wvu * C::B_DMA * 1024;
-  const __amdgpu_buffer_rsrc_t ra = operand_rsrc(Ab), rb = operand_rsrc(Bb);
-  auto issue = [&](Stage &s, int kt) {
-    const int so = (k_begin + kt) * kRowBytes;   // K offset of the slice, bytes
-#pragma unroll
-    for (int i = 0; i < A_DMA; ++i) b2lds16(ra, aoff[i], so, s.a + aofs + i * 1024);
-#pragma unroll
-    for (int i = 0; i < C::B_DMA; ++i) b2lds16(rb, boff[i], so, s.b + bofs + i * 1024);
-  };
+  auto issue = [&](Stage &s, int kt) { unit_issue<GATE_UP, W, MB>(x, o, s, kt); };
   f32x16_t acc[MB][NB];
 #pragma unroll
   for (int i = 0; i < MB; ++i)
@@ -335,7 +399,7 @@ MOE_DEV __attribute__((always_inline)) void gemm_tile(const GemmArgs &args, cons
   for (int i = 0; i < MB; ++i) fa1[i] = bf16x8_t{};   // "slice -1": contributes 0 * 0
 #pragma unroll
   for (int i = 0; i < NB; ++i) fb1[i] = bf16x8_t{};
-  issue(st0, 0);
+  // (slice 0 was issued into st0 by unit_prefetch)
   // MFMAs of (fa, fb) with the fragment reads of the next sub-step between them
   auto sub = [&](const bf16x8_t (&fa)[MB], const bf16x8_t (&fb)[NB], const Stage &cur, int ks,
                  bf16x8_t (&na)[MB], bf16x8_t (&nb)[NB]) {
@@ -344,9 +408,9 @@ MOE_DEV __attribute__((always_inline)) void gemm_tile(const GemmArgs &args, cons
     sched_sub<MB * NB, 0, MB + NB>();
     sched_fence();
   };
-  auto step = [&](Stage &cur, Stage &refill, int kt) {
+  auto step = [&](Stage &cur, Stage &refill, int kt, auto vm) {
     sched_fence();
-    wait_and_barrier<0>();                 // slice kt has landed
+    wait_and_barrier<decltype(vm)::value>();   // slice kt has landed
     sched_fence();
     issue(refill, min(kt + 1, nk - 1));   // past the end: re-read the last slice
     load_frags<W, MB>(cur, lane, wm, wn, 0, fa0, fb0);
@@ -358,17 +422,23 @@ MOE_DEV __attribute__((always_inline)) void gemm_tile(const GemmArgs &args, cons
     sub(fa0, fb0, cur, 3, fa1, fb1);
   };
   static_assert(kSub == 4 && NSTAGE == 2, "the step above runs four sub-steps, two stages");
-  // Two steps per iteration alternate the stages. The loop body is one branch-free block,
-  // so the compiler's wait counts stay exact inside it; an odd last step follows it.
-  int kt = 0;
+  using V0 = std::integral_constant<int, 0>;
+  using V16 = std::integral_constant<int, 16>;
+  // The first step (stores of the previous unit may still be in flight), then two steps per
+  // iteration alternating the stages. The loop body is one branch-free block, so the
+  // compiler's wait counts stay exact inside it; an odd last step follows it.
+  if (stores_pending) step(st0, st1, 0, V16{});
+  else step(st0, st1, 0, V0{});
+  int kt = 1;
   for (; kt + 2 <= nk; kt += 2) {
-    step(st0, st1, kt);
-    step(st1, st0, kt + 1);
+    step(st1, st0, kt, V0{});
+    step(st0, st1, kt + 1, V0{});
   }
-  if (kt < nk) step(st0, st1, kt);
+  if (kt < nk) step(st1, st0, kt, V0{});
   mfma_block<W, MB>(fa1, fb1, acc);   // last sub-step of the last slice
   wait_vm_lgkm<0, 15>();   // the surplus copy of the last step
   __syncthreads();   // every wave is done with every stage before the next tile's loads
+  if (has_next) unit_prefetch<GATE_UP, W>(nx, no, st0);
   if (punit >= 0) {
     // K-part of a split tile: the raw accumulators in register order (wave, mb, nb, i,
     // lane), so each store is 256 contiguous bytes; the reduction maps them back
@@ -379,7 +449,7 @@ MOE_DEV __attribute__((always_inline)) void gemm_tile(const GemmArgs &args, cons
       for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) Pt[((mb * NB + nb) * 16 + i) * 64] = acc[mb][nb][i];
-    return;
+    return true;   // MB * NB * 16 >= 32 stores
   }
   // epilogue: h in bf16 (it feeds the next bf16 GEMM), o in float32. Lane (c, r4) holds
   // column c of rows r4*4 + {0..3} + 8j of each 32 x 32 block. Stores go through a buffer
@@ -424,6 +494,7 @@ MOE_DEV __attribute__((always_inline)) void gemm_tile(const GemmArgs &args, cons
       roff += ((i & 3) == 3 ? 5u : 1u) * rowb;
       asm volatile("" : "+v"(roff));
     }
+  return nbv > 0;   // MB * 16 * nbv >= 16 stores
 }
 
 template <bool GATE_UP, int W>
@@ -437,7 +508,9 @@ __global__ __launch_bounds__(64 * W, 1) void gemm_bf16_kernel(GemmArgs args) {
 
   const SplitPlan sp = split_plan(total, kMaxPersistent, args.K / BK, args.split_ok);
   const int units = sp.full + sp.L * sp.S;
-  for (int u = xcd_virtual_block(); u < units; u += gridDim.x) {
+  // unit u of the list: its tile (or K-part of a split tile), group, position and K range
+  auto unit_at = [&](int u) {
+    Unit x;
     int tile = u, part = 0, nparts = 1;
     if (u >= sp.full) {
       tile = sp.full + (u - sp.full) / sp.S;
@@ -445,20 +518,37 @@ __global__ __launch_bounds__(64 * W, 1) void gemm_bf16_kernel(GemmArgs args) {
       nparts = sp.S;
     }
     const int g = find_group(tstart, G, tile);
-    const GroupDesc d = group_desc(args, g);
+    x.d = group_desc(args, g);
     const int local = tile - tstart[g];
-    const int mt = (d.rows + BM - 1) / BM;
-    const int n_tile = local / mt, m_tile = local % mt;
-    const int m0 = m_tile * BM;
-    const int nk = (d.K / BK) / nparts;   // K-steps of this unit
-    const int k_begin = part * nk;         // first K-step of this unit
-    const int punit = nparts > 1 ? u - sp.full : -1;
-    switch (tile_mb(d.rows - m0)) {
-      case 4: gemm_tile<GATE_UP, W, 4>(args, d, st0, st1, n_tile, m0, nk, k_begin, punit); break;
-      case 3: gemm_tile<GATE_UP, W, 3>(args, d, st0, st1, n_tile, m0, nk, k_begin, punit); break;
-      case 2: gemm_tile<GATE_UP, W, 2>(args, d, st0, st1, n_tile, m0, nk, k_begin, punit); break;
-      default: gemm_tile<GATE_UP, W, 1>(args, d, st0, st1, n_tile, m0, nk, k_begin, punit); break;
+    const int mt = (x.d.rows + BM - 1) / BM;
+    x.n_tile = local / mt;
+    x.m0 = (local % mt) * BM;
+    x.nk = (x.d.K / BK) / nparts;   // K-steps of this unit
+    x.k_begin = part * x.nk;         // first K-step of this unit
+    x.punit = nparts > 1 ? u - sp.full : -1;
+    x.mb = tile_mb(x.d.rows - x.m0);
+    make_uniform(x);
+    return x;
+  };
+  int u = xcd_virtual_block();
+  if (u >= units) return;   // workgroup-uniform
+  Unit cur = unit_at(u);
+  Offs co;
+  unit_prefetch<GATE_UP, W>(cur, co, st0);
+  bool pending = false;
+  for (; u < units; u += gridDim.x) {
+    const bool has_next = u + (int)gridDim.x < units;
+    const Unit nx = has_next ? unit_at(u + gridDim.x) : cur;
+    Offs no = co;
+    switch (cur.mb) {
+      case 4: pending = gemm_tile<GATE_UP, W, 4>(args, cur, co, st0, st1, pending, has_next, nx, no); break;
+      case 3: pending = gemm_tile<GATE_UP, W, 3>(args, cur, co, st0, st1, pending, has_next, nx, no); break;
+      case 2: pending = gemm_tile<GATE_UP, W, 2>(args, cur, co, st0, st1, pending, has_next, nx, no); break;
+      default: pending = gemm_tile<GATE_UP, W, 1>(args, cur, co, st0, st1, pending, has_next, nx, no); break;
     }
+    cur = nx;
+    make_uniform(cur);
+    co = no;
   }
 }
 
