@@ -869,11 +869,15 @@ __global__ __launch_bounds__(256) void gemm_skinny_reduce_kernel(GemmArgs args) 
 }
 
 // ----------------------------------------------------------------------------------------
-// float32 SIMT kernel: 64 x 64 output tile, K step 16, 256 threads with 4 x 4 outputs each
-// (gate/up keeps a gate and an up accumulator per output).
+// float32 SIMT kernel: 64 x 64 output tile, K steps of 32, 256 threads with 4 x 4 outputs each
+// (gate/up keeps a gate and an up accumulator per output). Each thread holds 8 elements of every
+// operand tile; the next K step's elements are loaded into registers while the current step's
+// FMAs run, so a K step waits for memory only when the loads take longer than the FMAs. Every
+// output sums over k in ascending order.
 template <bool GATE_UP>
 __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs args) {
-  constexpr int TM = 64, TN = 64, TK = 16;
+  constexpr int TM = 64, TN = 64, TK = 32;
+  constexpr int LPT = TM * TK / 256;   // elements of one operand tile per thread
   __shared__ float As[TK][TM + 4];
   __shared__ float Bs[2][TK][TN + 4];
   __shared__ int tstart[kMaxGroups + 1];
@@ -889,6 +893,19 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs args) {
     const int n0 = (local / mt) * TN, m0 = (local % mt) * TM;
     const float *A = (const float *)d.A;
     const float *B0 = (const float *)d.B0, *B1 = (const float *)d.B1;
+    float ra[LPT], rb0[LPT], rb1[LPT];
+    // element q of this thread: row (tid + 256 q) / TK, column (tid + 256 q) % TK of the tile
+    auto load = [&](int k0) {
+#pragma unroll
+      for (int q = 0; q < LPT; ++q) {
+        const int idx = (int)threadIdx.x + 256 * q, r = idx / TK, c = idx % TK;
+        const int m = m0 + r, k = k0 + c, n = n0 + r;
+        ra[q] = (m < d.rows && k < d.K) ? A[(size_t)(d.amap ? d.amap[m] : m) * d.lda + k] : 0.f;
+        const bool ok = n < d.N && k < d.K;
+        rb0[q] = ok ? B0[(size_t)n * d.K + k] : 0.f;
+        rb1[q] = (GATE_UP && ok) ? B1[(size_t)n * d.K + k] : 0.f;
+      }
+    };
     float acc[2][4][4];
 #pragma unroll
     for (int h = 0; h < 2; ++h)
@@ -896,17 +913,18 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs args) {
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[h][i][j] = 0.f;
+    load(0);
     for (int k0 = 0; k0 < d.K; k0 += TK) {
-      __syncthreads();
-      for (int idx = threadIdx.x; idx < TM * TK; idx += 256) {
-        const int r = idx / TK, c = idx % TK, m = m0 + r, k = k0 + c;
-        As[c][r] = (m < d.rows && k < d.K) ? A[(size_t)(d.amap ? d.amap[m] : m) * d.lda + k] : 0.f;
-        const int n = n0 + r;
-        const bool ok = n < d.N && k < d.K;
-        Bs[0][c][r] = ok ? B0[(size_t)n * d.K + k] : 0.f;
-        if (GATE_UP) Bs[1][c][r] = ok ? B1[(size_t)n * d.K + k] : 0.f;
+      __syncthreads();   // every thread is done with the previous step's tiles
+#pragma unroll
+      for (int q = 0; q < LPT; ++q) {
+        const int idx = (int)threadIdx.x + 256 * q, r = idx / TK, c = idx % TK;
+        As[c][r] = ra[q];
+        Bs[0][c][r] = rb0[q];
+        if (GATE_UP) Bs[1][c][r] = rb1[q];
       }
       __syncthreads();
+      if (k0 + TK < d.K) load(k0 + TK);   // in flight during the FMAs below
 #pragma unroll
       for (int c = 0; c < TK; ++c) {
         float av[4], bv[4], uv[4];

@@ -1283,6 +1283,10 @@ __global__ __launch_bounds__(1024) void cap_select_kernel(
     }
     if (kept) kept[ij] = (uint8_t)self;
   };
+  if (!drop) {   // every candidate stays, in list order: its rank is its index
+    for (int i = threadIdx.x; i < n; i += blockDim.x) emit(i, true, i);
+    return;
+  }
   // thread tid owns candidates tid + 1024 c (chunk c): keys in registers; the ranks of each
   // chunk come from one vector scan over the block, chunks in order
   auto in_regs = [&](auto kpt) {
