@@ -1637,7 +1637,7 @@ bool router_narrow_mfma(int dtype, int d, int E) {
 }
 
 size_t router_w3_bytes(int dtype, int d, int E) {
-  if (router_narrow_mfma(dtype, d, E)) return 0;   // splits W_r in registers
+  if (router_narrow_mfma(dtype, d, E)) return 0;   // splits W_r in LDS itself
   if (dtype == 1 && E > 8 && d % 64 == 0) return 3 * (size_t)router_epad(E) * router_w3_ld(d) * 2;
   return 0;
 }
