@@ -19,7 +19,6 @@ from __future__ import annotations
 
 import argparse
 import json
-import math
 import os
 import sys
 import time
@@ -123,10 +122,11 @@ def cpu_baseline(inp, sample_tokens=0, target_s=20.0):
                 dt = timed(sample_tokens)
     reps = 1
     if sample_tokens == T and dt < 10.0:
-        # the whole workload is quicker than the bound: repeat it to time ~10 s of work
-        reps = int(min(5, math.ceil(10.0 / max(dt, 1e-3))))
-        if reps > 1:
-            dt = sum(timed(T) for _ in range(reps))
+        # the whole workload is quicker than the bound: repeat it until ~10 s of work is timed
+        reps, dt = 0, 0.0
+        while dt < 10.0 and reps < 100000:
+            dt += timed(T)
+            reps += 1
     what = (f"all {T} tokens, {reps} runs" if reps > 1 else
             f"first {sample_tokens} of {T} tokens (routing over all {T})")
     return {"value": round(reps * sample_tokens / dt, 2), "unit": "tokens/s", "cores": int(threads),
