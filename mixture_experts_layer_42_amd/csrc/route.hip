@@ -402,62 +402,78 @@ __global__ __launch_bounds__(512) void router_mfma_kernel(const bf16_t *__restri
 // bf16 parts of W_r (hi = bf16(w), mid = bf16(w - hi), lo = bf16(w - hi - mid)) form the 3E
 // rows of a 32-row B operand: row p*E + e holds part p of column e, rows 3E..31 are zero. A
 // workgroup of 8 waves takes 16 tokens (32 when T >= 8192); wave w sums its share of the
-// 64-column units of d with v_mfma_f32_16x16x32_bf16 (A: 16 token rows of x, B: the two
-// 16-row halves of the part operand), four units' loads in flight. For each 32-column K step
-// a wave loads the float32 block W_r[j0 .. j0+31][0 .. E) (128 E contiguous bytes, 16 bytes
-// per lane), every lane splits its 4 elements once and writes the parts into an LDS tile of
-// its wave in the operand's layout (32 rows of 32 bf16), and each lane reads its two
-// fragments back with two 16-byte LDS reads: W_r is read as it is, with no separate split
-// pass. The workgroups walk the units in rotated order (workgroup b starts at unit
-// 8 (b mod nu/8)), so that they do not all read the same W_r lines from L2 at the same
-// moment. The 8 partial 16 x 32 tiles are added in wave order in LDS, then each logit is
-// (hi + mid) + lo + bias; every token's sums run in the order its workgroup fixes.
+// 64-column units of d (units w, w + 8, ...) with v_mfma_f32_16x16x32_bf16 (A: 16 token rows
+// of x, B: the two 16-row halves of the part operand). For each unit a wave loads the two
+// float32 blocks W_r[j0 .. j0+31][0 .. E) of its 32-column K steps (128 E contiguous bytes
+// each, 16 bytes per lane), every lane splits its 4 elements of each once and writes the parts
+// into the wave's two LDS tiles in the operand's layout (32 rows of 32 bf16), and each lane
+// reads its four fragments back with 16-byte LDS reads: W_r is read as it is, with no separate
+// split pass, and one LDS round trip serves a whole unit. The loads run kNarrowRing units ahead
+// of the arithmetic in a ring of registers: a slot's next unit is requested as soon as its
+// current unit is consumed, so a wave keeps issuing loads while it splits and multiplies
+// instead of issuing all of them first (a CU's load pipe takes one 16-byte-per-lane load every
+// few cycles, and a wave that issued its whole share up front left its arithmetic waiting
+// behind the queue: Mixtral-shaped route stage 28.1 -> 25.1 us with a ring of 2 units; 4 and 6
+// units measured slower than 2, and 1 slower still). Rows past T, W_r chunks past the block and
+// units past the end are buffer loads beyond the buffer, which return zeros and read nothing.
+// The workgroups walk the units in rotated order (workgroup b starts at unit 8 (b mod nu/8)),
+// so that they do not all read the same W_r lines from L2 at the same moment. The 8 partial
+// 16 x 32 tiles are added in wave order in LDS, then each logit is (hi + mid) + lo + bias;
+// every token's sums run in the order its workgroup fixes.
 constexpr int kNarrowRows = 32;
 constexpr int kNarrowMaxE = 10;
+constexpr int kNarrowRing = 2;    // units in flight per wave
 constexpr int kBlkMaxE = kBlkCountMaxE;
 constexpr int kWtRowBytes = 80;   // LDS row stride of a part tile: 64 B of data + 16 B pad
+constexpr int kNarrowTileBytes = kNarrowRows * kWtRowBytes;
 
-// Token-choice top-k of one token whose E <= 16 logits sit in LDS, computed by one thread
-// with the arithmetic topk_kernel uses for the same E (a group of G = 8 or 16 lanes, one logit
-// per lane): picks by (logit desc, expert asc), gate numerators exp(l - max) over the first
-// pick's logit, the renormalisation mass of the first kden picks in pick order or the full
-// softmax sum in the butterfly order of G lanes, and the routing keys of the capacity forms.
-// With cnt (LDS, one int per expert) every pick is also counted there.
-MOE_DEV void topk_one_token(const float *l, int E, int t, const TopkOut &o, int *cnt) {
-  const int G = E <= 8 ? 8 : 16;
-  uint32_t taken = 0u;
-  float mx = 0.f, qsum = 0.f, qn[16];
-  int pick[16];
-  for (int r = 0; r < o.k; ++r) {
-    float bv = -INFINITY;
-    int be = -1;
-    for (int e = 0; e < E; ++e)
-      if (!((taken >> e) & 1u) && (be < 0 || l[e] > bv)) { bv = l[e]; be = e; }
-    taken |= 1u << be;
+// Token-choice top-k of one token on a group of G lanes (G = 8 for E <= 8, else 16), lane gl
+// holding expert gl's logit (-inf past E), with topk_kernel's arithmetic for the same E and G:
+// k rounds of group argmax by (logit desc, expert asc) in the same butterfly, gate numerators
+// exp(l - max) over the first pick's logit, the renormalisation mass of the first kden picks in
+// pick order or the full softmax sum in butterfly order, and the routing keys of the capacity
+// forms (q_e = rexp_spec(l_e - max), S = q_0 + q_1 + ... left to right, key = q_e / S). Lane r
+// of the group keeps pick r and writes it. With cnt (LDS, one int per expert) every pick is
+// also counted there. Every lane of the group must call this (the butterflies use them all).
+template <int G>
+MOE_DEV void topk_lanes(float lv, int gl, bool live, int t, int E, const TopkOut &o, int *cnt) {
+  const int lane = threadIdx.x & 63, g0 = lane - gl;   // first lane of this group
+  bool taken = false;
+  float mx = 0.f, qsum = 0.f, myq = 0.f;
+  int myid = 0;
+  for (int r = 0; r < o.k; ++r) {   // o.k is uniform: every lane runs the same rounds
+    float bv = (gl < E && !taken) ? lv : -INFINITY;
+    int be = (gl < E && !taken) ? gl : 0x7fffffff;
+#pragma unroll
+    for (int s = G / 2; s > 0; s >>= 1) {
+      const float ov = __shfl_xor(bv, s, 64);
+      const int oe = __shfl_xor(be, s, 64);
+      if (ov > bv || (ov == bv && oe < be)) { bv = ov; be = oe; }
+    }
     if (r == 0) mx = bv;
-    qn[r] = expf(bv - mx);
-    pick[r] = be;
-    if (r < o.kden) qsum += qn[r];
-    if (cnt) atomicAdd(&cnt[be], 1);   // LDS integer add: the count does not depend on order
+    if (be == gl) taken = true;
+    const float q = expf(bv - mx);
+    if (r < o.kden) qsum += q;
+    if (gl == r) { myq = q; myid = be; }
+    if (gl == r && live && cnt) atomicAdd(&cnt[be], 1);   // LDS integer add: order-free
   }
   float denom = qsum;
   if (!o.renorm) {
-    float sv[16];
-    for (int g = 0; g < G; ++g) sv[g] = g < E ? expf(l[g] - mx) : 0.f;
-    for (int d = G / 2; d > 0; d >>= 1)
-      for (int g = 0; g < d; ++g) sv[g] = sv[g] + sv[g + d];   // lane 0 of the butterfly
-    denom = sv[0];
+    float s = gl < E ? expf(lv - mx) : 0.f;
+#pragma unroll
+    for (int d = G / 2; d > 0; d >>= 1) s += __shfl_xor(s, d, 64);
+    denom = s;
   }
-  for (int r = 0; r < o.k; ++r) {
-    o.ids[(size_t)t * o.k + r] = pick[r];
-    o.gates[(size_t)t * o.k + r] = qn[r] / denom;
+  if (gl < o.k && live) {
+    o.ids[(size_t)t * o.k + gl] = myid;
+    o.gates[(size_t)t * o.k + gl] = myq / denom;
   }
   if (o.want_key) {
-    float q[16];
-    for (int e = 0; e < E; ++e) q[e] = rexp_spec(__fsub_rn(l[e], mx));
-    float S = q[0];
-    for (int e = 1; e < E; ++e) S = __fadd_rn(S, q[e]);
-    for (int r = 0; r < o.k; ++r) o.keys[(size_t)t * o.k + r] = q[pick[r]] / S;
+    const float qv = gl < E ? rexp_spec(__fsub_rn(lv, mx)) : 0.f;
+    float S = __shfl(qv, g0, 64);
+    for (int e = 1; e < E; ++e) S = __fadd_rn(S, __shfl(qv, g0 + e, 64));
+    const float qp = __shfl(qv, g0 + (gl < o.k ? myid : 0), 64);
+    if (gl < o.k && live) o.keys[(size_t)t * o.k + gl] = qp / S;
   }
 }
 
@@ -469,88 +485,116 @@ __global__ __launch_bounds__(512) void router_mfma_narrow_kernel(const bf16_t *_
                                                                  int T, int d, int E,
                                                                  TopkOut topk,
                                                                  int32_t *__restrict__ blk_cnt) {
-  // 64-column units per wave in flight: with 16 tokens and E <= 8 the whole share of a
-  // 4096-wide d (8 units) goes out at once, so a wave waits for memory once
-  constexpr int U = (TB == 1 && NCH == 1) ? 8 : 4;
+  constexpr int U = kNarrowRing;
   constexpr int TT = 16 * TB;   // tokens per workgroup
   __shared__ float part[8][TT * kNarrowRows];
-  __shared__ __attribute__((aligned(16))) char wt[8][kNarrowRows * kWtRowBytes];   // per wave
+  __shared__ __attribute__((aligned(16))) char wt[8][2 * kNarrowTileBytes];   // two per wave
   __shared__ int cnt[kNarrowMaxE];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int t0 = blockIdx.x * TT;
   const int kq = 8 * (lane >> 4);   // this lane's 8 columns inside a 32-column MFMA step
   const int nchunk = 8 * E;         // 16-byte chunks of a 32-column block of W_r
-  const bf16_t *xr[TB];
+  // buffer loads: a lane whose row is past T, whose W_r chunk is past the block, or whose unit
+  // is past the end gets an offset beyond the buffer, which returns zeros and reads nothing
+  constexpr uint32_t kOut = 0x80000000u;
+  const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<bf16_t *>(x), (short)0, (int)((uint32_t)T * (uint32_t)d * 2u), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float *>(w), (short)0, (int)((uint32_t)d * (uint32_t)E * 4u), 0x00020000);
+  uint32_t xoff[TB];
 #pragma unroll
-  for (int b = 0; b < TB; ++b) xr[b] = x + (size_t)min(t0 + 16 * b + (lane & 15), T - 1) * d + kq;
+  for (int b = 0; b < TB; ++b) {
+    const int tr = t0 + 16 * b + (lane & 15);
+    xoff[b] = tr < T ? ((uint32_t)tr * (uint32_t)d + (uint32_t)kq) * 2u : kOut;
+  }
   char *tile = wt[wv];
   // the part rows this lane writes: element i of its chunk(s) is W_r[j0 + f / E][f % E],
   // f = 4 c + i; its part p goes to row p E + f % E, column f / E of the tile
   // rows 3E..31 stay zero: cleared once
-  for (int i = lane; i < kNarrowRows * kWtRowBytes / 4; i += 64)
+  for (int i = lane; i < 2 * kNarrowTileBytes / 4; i += 64)
     reinterpret_cast<uint32_t *>(tile)[i] = 0u;
+  if (threadIdx.x < kNarrowMaxE) cnt[threadIdx.x] = 0;
   rf32x4_t acc0[TB], acc1[TB];
 #pragma unroll
   for (int b = 0; b < TB; ++b) acc0[b] = acc1[b] = rf32x4_t{0.f, 0.f, 0.f, 0.f};
   const int nu = d / 64;
   const int rot = (nu % 8 == 0) ? (int)(blockIdx.x % (unsigned)(nu / 8)) * 8 : 0;
-  for (int ub = wv; ub < nu; ub += 8 * U) {
-    rbf16x8_t a[U][TB][2];
-    float4 wr[U][2][NCH];   // raw float32 W_r chunks: [unit][half][chunk lane (+ 64)]
+  rbf16x8_t a[U][TB][2];
+  float4 wr[U][2][NCH];   // raw float32 W_r chunks: [slot][half][chunk lane (+ 64)]
+  // loads of unit ui into ring slot v (none past the end: ui >= nu reads nothing)
+  auto issue = [&](int v, int ui) {
+    const bool live = ui < nu;   // wave-uniform
+    const int u = live ? (ui + rot) % nu : 0;
 #pragma unroll
-    for (int v = 0; v < U; ++v) {
-      const int u = (min(ub + 8 * v, nu - 1) + rot) % nu;   // past the end: reloaded, not used
+    for (int h = 0; h < 2; ++h) {
+      const uint32_t o = (uint32_t)u * 64u + (uint32_t)h * 32u;   // first column of the block
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const size_t o = (size_t)u * 64 + h * 32;
+      for (int b = 0; b < TB; ++b)
+        a[v][b][h] = __builtin_bit_cast(rbf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(
+            rx, live && xoff[b] != kOut ? xoff[b] + o * 2u : kOut, 0, 0));
 #pragma unroll
-        for (int b = 0; b < TB; ++b) a[v][b][h] = *reinterpret_cast<const rbf16x8_t *>(xr[b] + o);
-        const float4 *blk = reinterpret_cast<const float4 *>(w + o * E);
-#pragma unroll
-        for (int c2 = 0; c2 < NCH; ++c2)
-          wr[v][h][c2] = lane + 64 * c2 < nchunk ? blk[lane + 64 * c2] : make_float4(0.f, 0.f, 0.f, 0.f);
+      for (int c2 = 0; c2 < NCH; ++c2) {
+        const int c = lane + 64 * c2;
+        wr[v][h][c2] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(
+            rw, live && c < nchunk ? o * (uint32_t)E * 4u + (uint32_t)c * 16u : kOut, 0, 0));
       }
     }
+  };
+  // split both W_r blocks of slot v into the wave's two tiles, then multiply
+  auto consume = [&](int v) {
 #pragma unroll
-    for (int v = 0; v < U; ++v) {
-      if (ub + 8 * v < nu) {   // wave-uniform
+    for (int h = 0; h < 2; ++h) {
+      char *th = tile + h * kNarrowTileBytes;
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
+      for (int c2 = 0; c2 < NCH; ++c2) {
+        const int c = lane + 64 * c2;
+        if (c < nchunk) {
+          const float vals[4] = {wr[v][h][c2].x, wr[v][h][c2].y, wr[v][h][c2].z, wr[v][h][c2].w};
 #pragma unroll
-          for (int c2 = 0; c2 < NCH; ++c2) {
-            const int c = lane + 64 * c2;
-            if (c < nchunk) {
-              const float vals[4] = {wr[v][h][c2].x, wr[v][h][c2].y, wr[v][h][c2].z, wr[v][h][c2].w};
-#pragma unroll
-              for (int i = 0; i < 4; ++i) {
-                const int f = 4 * c + i, col = f / E, e = f - col * E;
-                const __bf16 hi = (__bf16)vals[i];
-                const float r1 = vals[i] - (float)hi;
-                const __bf16 mid = (__bf16)r1;
-                const __bf16 lo = (__bf16)(r1 - (float)mid);
-                char *at = tile + e * kWtRowBytes + col * 2;
-                *reinterpret_cast<__bf16 *>(at) = hi;
-                *reinterpret_cast<__bf16 *>(at + E * kWtRowBytes) = mid;
-                *reinterpret_cast<__bf16 *>(at + 2 * E * kWtRowBytes) = lo;
-              }
-            }
-          }
-          // the wave's LDS accesses complete in order: the reads below see the writes above
-          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-          __builtin_amdgcn_wave_barrier();
-          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-          const rbf16x8_t p = *reinterpret_cast<const rbf16x8_t *>(tile + (lane & 15) * kWtRowBytes + kq * 2);
-          const rbf16x8_t q = *reinterpret_cast<const rbf16x8_t *>(tile + (16 + (lane & 15)) * kWtRowBytes + kq * 2);
-          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-          __builtin_amdgcn_wave_barrier();   // every lane has read before the next block lands
-          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-#pragma unroll
-          for (int b = 0; b < TB; ++b) {
-            acc0[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[v][b][h], p, acc0[b], 0, 0, 0);
-            acc1[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[v][b][h], q, acc1[b], 0, 0, 0);
+          for (int i = 0; i < 4; ++i) {
+            const int f = 4 * c + i, col = f / E, e = f - col * E;
+            const __bf16 hi = (__bf16)vals[i];
+            const float r1 = vals[i] - (float)hi;
+            const __bf16 mid = (__bf16)r1;
+            const __bf16 lo = (__bf16)(r1 - (float)mid);
+            char *at = th + e * kWtRowBytes + col * 2;
+            *reinterpret_cast<__bf16 *>(at) = hi;
+            *reinterpret_cast<__bf16 *>(at + E * kWtRowBytes) = mid;
+            *reinterpret_cast<__bf16 *>(at + 2 * E * kWtRowBytes) = lo;
           }
         }
       }
+    }
+    // the wave's LDS accesses complete in order: the reads below see the writes above
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    rbf16x8_t p[2], q[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const char *th = tile + h * kNarrowTileBytes;
+      p[h] = *reinterpret_cast<const rbf16x8_t *>(th + (lane & 15) * kWtRowBytes + kq * 2);
+      q[h] = *reinterpret_cast<const rbf16x8_t *>(th + (16 + (lane & 15)) * kWtRowBytes + kq * 2);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();   // every lane has read before the next blocks land
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int b = 0; b < TB; ++b) {
+        acc0[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[v][b][h], p[h], acc0[b], 0, 0, 0);
+        acc1[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[v][b][h], q[h], acc1[b], 0, 0, 0);
+      }
+  };
+#pragma unroll
+  for (int v = 0; v < U; ++v) issue(v, wv + 8 * v);
+  for (int ub = wv; ub < nu; ub += 8 * U) {
+#pragma unroll
+    for (int v = 0; v < U; ++v) {
+      const int ui = ub + 8 * v;
+      if (ui < nu) consume(v);   // wave-uniform
+      issue(v, ui + 8 * U);
     }
   }
   // lane l holds rows 4*(l/16) + i, column l%16 of each 16 x 16 block
@@ -562,7 +606,6 @@ __global__ __launch_bounds__(512) void router_mfma_narrow_kernel(const bf16_t *_
       part[wv][r * kNarrowRows + (lane & 15)] = acc0[b][i];
       part[wv][r * kNarrowRows + 16 + (lane & 15)] = acc1[b][i];
     }
-  if (threadIdx.x < kNarrowMaxE) cnt[threadIdx.x] = 0;
   __syncthreads();
   float sum[TB];
 #pragma unroll
@@ -586,8 +629,16 @@ __global__ __launch_bounds__(512) void router_mfma_narrow_kernel(const bf16_t *_
   }
   if (!topk.ids) return;   // block-uniform
   __syncthreads();
-  if (threadIdx.x < TT && t0 + (int)threadIdx.x < T)
-    topk_one_token(lg + threadIdx.x * E, E, t0 + threadIdx.x, topk, blk_cnt ? cnt : nullptr);
+  int *cp = blk_cnt ? cnt : nullptr;
+  if (E <= 8) {
+    const int gi = threadIdx.x / 8, gl = threadIdx.x % 8;
+    if (gi < TT)   // whole groups of 8 lanes
+      topk_lanes<8>(gl < E ? lg[gi * E + gl] : -INFINITY, gl, t0 + gi < T, t0 + gi, E, topk, cp);
+  } else {
+    const int gi = threadIdx.x / 16, gl = threadIdx.x % 16;
+    if (gi < TT)
+      topk_lanes<16>(gl < E ? lg[gi * E + gl] : -INFINITY, gl, t0 + gi < T, t0 + gi, E, topk, cp);
+  }
   if (!blk_cnt) return;
   __syncthreads();
   if (threadIdx.x < E) blk_cnt[(size_t)blockIdx.x * E + threadIdx.x] = cnt[threadIdx.x];
