@@ -397,6 +397,123 @@ __global__ __launch_bounds__(512) void router_mfma_kernel(const bf16_t *__restri
   }
 }
 
+// Wide router for E_pad a multiple of 128: a workgroup of 8 waves takes 128 tokens x 64
+// experts (grid.y walks groups of 64 experts), so a K step moves 16 KB of x and 24 KB of W
+// parts into the CU instead of 8 KB and 48 KB (flop per byte 77 instead of 55: the 64-token
+// kernel above is bound by the CU's load pipe, and the fine-grained layer's router took 34 us
+// with x in the last-level cache, 53 us with x in HBM). Both operands go global -> LDS with
+// 16-byte buffer loads into LDS (rows of 128 B, chunks XOR-swizzled by row/2 as above): x in
+// a ring of 4 stages issued 3 K steps ahead (it streams from HBM), the W parts in a ring of 3
+// issued 2 steps ahead (they stay in L2). Wave w computes tokens 64 (w / 4) .. + 63 against
+// expert block w % 4 (16 experts), all three parts, so hi, mid and lo meet in its registers
+// and every logit sums its K steps in the same order as the 64-token kernel. Rows past T and
+// past E_pad are loads beyond the buffer (zeros, no memory traffic).
+constexpr int kRwTM = 128, kRwEN = 64;
+constexpr int kRwXBytes = kRwTM * 128;       // one K step of x: 128 rows x 64 bf16
+constexpr int kRwWBytes = 3 * kRwEN * 128;   // one K step of W: 3 parts x 64 rows x 64 bf16
+constexpr int kRwXStages = 4, kRwWStages = 3;
+
+MOE_DEV void rw_copy(__amdgpu_buffer_rsrc_t r, char *lds, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (rlds_void_t *)lds, 16, (int)voff, 0, 0, 0);
+}
+
+__global__ __launch_bounds__(512) void router_mfma128_kernel(const bf16_t *__restrict__ x,
+                                                             const bf16_t *__restrict__ w3,
+                                                             const float *__restrict__ bias,
+                                                             float *__restrict__ logits, int T,
+                                                             int d, int E, int E_pad) {
+  __shared__ __attribute__((aligned(16))) char lds[kRwXStages * kRwXBytes + kRwWStages * kRwWBytes];
+  constexpr uint32_t kOut = 0x80000000u;   // offset beyond either buffer
+  const int lane = threadIdx.x & 63;
+  const int wvu = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int t0 = blockIdx.x * kRwTM, eg = blockIdx.y * kRwEN;
+  const int tq = wvu >> 2, eb = wvu & 3;
+  const uint32_t ldw = (uint32_t)router_w3_ld(d), plane = (uint32_t)E_pad * ldw;
+  const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<bf16_t *>(x), (short)0, (int)((uint32_t)T * (uint32_t)d * 2u), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<bf16_t *>(w3), (short)0, (int)(3u * plane * 2u), 0x00020000);
+  // byte offsets (K step 0) of this lane's 16-byte chunks: x rows 16 w + 8 c + lane/8 (c < 2),
+  // W stage rows 24 w + 8 c + lane/8 (c < 3), stage row R = part * 64 + expert
+  uint32_t xo[2], wo[3];
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    const int r = 16 * wvu + 8 * c + (lane >> 3);
+    xo[c] = t0 + r < T ? ((uint32_t)(t0 + r) * (uint32_t)d + 8u * ((lane & 7) ^ ((r >> 1) & 7))) * 2u : kOut;
+  }
+#pragma unroll
+  for (int c = 0; c < 3; ++c) {
+    const int R = 24 * wvu + 8 * c + (lane >> 3), p = R >> 6, e = eg + (R & 63);
+    wo[c] = e < E_pad ? ((uint32_t)p * plane + (uint32_t)e * ldw + 8u * ((lane & 7) ^ ((R >> 1) & 7))) * 2u : kOut;
+  }
+  auto issue_x = [&](int kc) {
+    char *dst = lds + (kc & 3) * kRwXBytes + wvu * 2048;
+#pragma unroll
+    for (int c = 0; c < 2; ++c) rw_copy(rx, dst + c * 1024, xo[c] == kOut ? kOut : xo[c] + (uint32_t)kc * 128u);
+  };
+  auto issue_w = [&](int kc) {
+    char *dst = lds + kRwXStages * kRwXBytes + (kc % 3) * kRwWBytes + wvu * 3072;
+#pragma unroll
+    for (int c = 0; c < 3; ++c) rw_copy(rw, dst + c * 1024, wo[c] == kOut ? kOut : wo[c] + (uint32_t)kc * 128u);
+  };
+  rf32x4_t acc[3][4];
+#pragma unroll
+  for (int p = 0; p < 3; ++p)
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) acc[p][tb] = rf32x4_t{0.f, 0.f, 0.f, 0.f};
+  const int nk = d / 64;
+  // issue order: x0, x1, x2, W0, W1 here, then at step s W(s+2) and x(s+3). Loads complete in
+  // issue order, so at step s, with s >= 2 and s + 2 < nk, the copies issued after W(s) are
+  // x(s+1), W(s+1) and x(s+2): waiting until at most 7 are in flight leaves W(s) and x(s)
+  // landed. Other steps wait for everything.
+  issue_x(0);
+  if (nk > 1) issue_x(1);
+  if (nk > 2) issue_x(2);
+  issue_w(0);
+  if (nk > 1) issue_w(1);
+  for (int kc = 0; kc < nk; ++kc) {
+    if (kc >= 2 && kc + 2 < nk)
+      __builtin_amdgcn_s_waitcnt((7 & 15) | (0 << 14) | (7 << 4) | (0xF << 8));
+    else
+      __builtin_amdgcn_s_waitcnt((0 & 15) | (0 << 14) | (7 << 4) | (0xF << 8));
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    if (kc + 2 < nk) issue_w(kc + 2);
+    if (kc + 3 < nk) issue_x(kc + 3);
+    __builtin_amdgcn_sched_barrier(0);   // the prefetch goes out before the MFMAs
+    const char *xs = lds + (kc & 3) * kRwXBytes;
+    const char *ws = lds + kRwXStages * kRwXBytes + (kc % 3) * kRwWBytes;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      rbf16x8_t a[4], b[3];
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb)
+        a[tb] = *reinterpret_cast<const rbf16x8_t *>(xs + rswz(tq * 64 + tb * 16 + (lane & 15), 4 * h + (lane >> 4)));
+#pragma unroll
+      for (int p = 0; p < 3; ++p)
+        b[p] = *reinterpret_cast<const rbf16x8_t *>(ws + rswz(p * 64 + eb * 16 + (lane & 15), 4 * h + (lane >> 4)));
+#pragma unroll
+      for (int p = 0; p < 3; ++p)
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb)
+          acc[p][tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[tb], b[p], acc[p][tb], 0, 0, 0);
+    }
+  }
+  // lane l holds tokens 4 (l/16) + i of each block of 16, expert l % 16 of the wave's block
+  const int e = eg + eb * 16 + (lane & 15);
+  if (e >= E) return;
+  const float bv = bias ? bias[e] : 0.f;
+#pragma unroll
+  for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = t0 + tq * 64 + tb * 16 + 4 * (lane >> 4) + i;
+      if (t < T) logits[(size_t)t * E + e] = ((acc[0][tb][i] + acc[1][tb][i]) + acc[2][tb][i]) + bv;
+    }
+}
+
 // ----------------------------------------------------------------------------------------
 // Router, bf16 x and E <= 10, on the matrix cores, reading the float32 W_r itself. The three
 // bf16 parts of W_r (hi = bf16(w), mid = bf16(w - hi), lo = bf16(w - hi - mid)) form the 3E
@@ -1719,9 +1836,15 @@ hipError_t launch_router(int dtype, const void *x, const float *w, const float *
     int g = (int)((n + 255) / 256);
     if (g > 2048) g = 2048;
     hipLaunchKernelGGL(router_split_kernel, dim3(g), dim3(256), 0, st, w, d, E, E_pad, w3);
-    const dim3 grid((T + 63) / 64, (E_pad + 127) / 128);
-    hipLaunchKernelGGL(router_mfma_kernel, grid, dim3(512), 0, st, (const bf16_t *)x, w3, bias,
-                       logits, T, d, E, E_pad);
+    if (E_pad % 128 == 0) {   // same workgroup count as 64 x 128 tiles, fewer bytes per CU
+      const dim3 grid((T + kRwTM - 1) / kRwTM, E_pad / kRwEN);
+      hipLaunchKernelGGL(router_mfma128_kernel, grid, dim3(512), 0, st, (const bf16_t *)x, w3,
+                         bias, logits, T, d, E, E_pad);
+    } else {
+      const dim3 grid((T + 63) / 64, (E_pad + 127) / 128);
+      hipLaunchKernelGGL(router_mfma_kernel, grid, dim3(512), 0, st, (const bf16_t *)x, w3, bias,
+                         logits, T, d, E, E_pad);
+    }
     return hipGetLastError();
   }
   // SIMT float32 routers (bf16 problems, whose d is a multiple of 64, never get here)
