@@ -1364,10 +1364,21 @@ MOE_DEV SelectResult block_radix_select(GetKey get, int n, int want, int *hist, 
   for (int shift = 24; shift >= 0; shift -= 8) {
     for (int i = threadIdx.x; i < kSelWaves * 256; i += blockDim.x) hist[i] = 0;
     __syncthreads();
+    uint32_t cd = 0u;   // runs of equal digits, one atomic each (see block_radix_select_regs)
+    int cc = 0;
     for (int i = threadIdx.x; i < n; i += blockDim.x) {
       const uint32_t u = get(i);
-      if ((u & pmask) == prefix) atomicAdd(&wh[(u >> shift) & 255u], 1);
+      if ((u & pmask) == prefix) {
+        const uint32_t dg = (u >> shift) & 255u;
+        if (cc && dg != cd) {
+          atomicAdd(&wh[cd], cc);
+          cc = 0;
+        }
+        cd = dg;
+        ++cc;
+      }
     }
+    if (cc) atomicAdd(&wh[cd], cc);
     __syncthreads();
     // thread b looks at bin 255-b: inclusive scan from the top bin down
     const int b = threadIdx.x;
@@ -1394,10 +1405,23 @@ MOE_DEV SelectResult block_radix_select_regs(const uint32_t (&u)[KPT], int n, in
   for (int shift = 24; shift >= 0; shift -= 8) {
     for (int i = threadIdx.x; i < kSelWaves * 256; i += blockDim.x) hist[i] = 0;
     __syncthreads();
+    // a thread adds runs of equal digits among its keys with one atomic each: the keys of one
+    // bucket share their leading bytes, so in the first passes a thread's keys mostly fall in
+    // one bin and 64 lanes adding 1 to the same LDS word, key after key, serialise
+    uint32_t cd = 0u;
+    int cc = 0;
 #pragma unroll
     for (int j = 0; j < KPT; ++j)
-      if (threadIdx.x + j * 1024 < n && (u[j] & pmask) == prefix)
-        atomicAdd(&wh[(u[j] >> shift) & 255u], 1);
+      if (threadIdx.x + j * 1024 < n && (u[j] & pmask) == prefix) {
+        const uint32_t dg = (u[j] >> shift) & 255u;
+        if (cc && dg != cd) {
+          atomicAdd(&wh[cd], cc);
+          cc = 0;
+        }
+        cd = dg;
+        ++cc;
+      }
+    if (cc) atomicAdd(&wh[cd], cc);
     __syncthreads();
     const int b = threadIdx.x;
     const int h = sum_wave_hists(hist, b);
