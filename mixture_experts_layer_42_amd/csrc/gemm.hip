@@ -641,10 +641,10 @@ __global__ __launch_bounds__(256) void gemm_tail_reduce_kernel(GemmArgs args) {
 // read once, so the GEMM is bound by streaming the weights from HBM; a 256-row tile would
 // spend its MFMAs on padding. A unit is 32*MB rows x 256 B-columns x one K part of a group;
 // 4 waves own 64 B-columns each (for gate/up 32 gate and the matching 32 up columns), K in
-// slices of 64 through three LDS stages. K is cut into S parts only as far as needed for about
-// one unit per CU (longer units keep the copy pipeline full: fewer parts measured faster than
-// a thousand short units); with S > 1 each unit writes float32 sums to the partial buffer
-// and gemm_skinny_reduce_kernel adds the parts in order.
+// slices of 64 through three LDS stages. K is cut into S parts only as far as the rule in
+// skinny_plan asks (about one or two units per CU: longer units keep the copy pipeline full,
+// and a thousand short units measured slower); with S > 1 each unit writes float32 sums to
+// the partial buffer and gemm_skinny_reduce_kernel adds the parts in order.
 struct SkinnyPlan { int mb, S, nt, snt, pitch; };
 
 SkinnyPlan skinny_plan(const GemmArgs &a, bool gate_up) {
@@ -657,10 +657,19 @@ SkinnyPlan skinny_plan(const GemmArgs &a, bool gate_up) {
   const int used = a.E < a.rcap ? a.E : a.rcap;   // groups that can receive rows
   const int tiles = used * sp.nt + sp.snt;
   const int nk = a.K / BK, snk = a.s_rows > 0 ? a.sK / BK : nk;
+  // K parts: about one unit per CU, two per CU when there are fewer than 128 weight tiles, and
+  // at least two parts for a gate/up GEMM whose groups hold at most 4 rows (measured on the
+  // Mixtral-shaped weights, one box: down GEMM at T=2 94 -> 76 us and T=1 60 -> 56 us with the
+  // larger target, where 512 units of T=4 and T=8 measured slower than 256; gate/up at T=2
+  // 142 -> 130 us and at T=4 196 -> 176 us with two parts, while T=8 measured 254 -> 264 us
+  // and T=64 no better)
+  const int target = tiles < 128 ? 512 : 256;
+  auto can_split = [&](int s) {   // parts of at least two slices that divide both K ranges
+    return s <= 16 && nk % s == 0 && snk % s == 0 && nk / s >= 2 && snk / s >= 2;
+  };
   int S = 1;
-  while (S < 16 && tiles * S < 256 && nk % (2 * S) == 0 && snk % (2 * S) == 0 &&
-         nk / (2 * S) >= 2 && snk / (2 * S) >= 2)
-    S *= 2;
+  while (tiles * S < target && can_split(2 * S)) S *= 2;
+  if (gate_up && a.max_group_rows <= 4 && S < 2 && can_split(2)) S = 2;
   sp.S = S;
   const int nmax = a.s_rows > 0 && a.sN > a.N ? a.sN : a.N;
   sp.pitch = (gate_up ? 2 : 1) * nmax;
