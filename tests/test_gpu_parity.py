@@ -32,6 +32,10 @@ SMALL = {
                               bias=("zipf", 1.2)),
     "fine-shared-bf16": C0.with_(dtype="bf16", T=333, d_model=192, E=128, k=8, d_ff=128,
                                  d_ff_shared=64, gamma=1.25, bias=("normal", 1.0)),
+    # 200 experts (padded to 256): the 128-token x 64-expert router on four expert groups, with
+    # enough K steps (d_model 1024) for its steady-state copy waits
+    "wide-E200-bf16": C0.with_(dtype="bf16", T=333, d_model=1024, E=200, k=6, d_ff=64,
+                               gamma=1.25, bias=("normal", 1.0)),
     "expert-choice-bf16": C0.with_(dtype="bf16", T=1000, routing="expert"),
     "expert-choice-bf16-yf32": C0.with_(dtype="bf16", y_dtype="f32", T=1000, routing="expert"),
     "ragged-bf16-yf32": C0.with_(dtype="bf16", y_dtype="f32", T=300, d_model=256, d_ff=320,
