@@ -540,6 +540,7 @@ __global__ __launch_bounds__(512) void router_mfma128_kernel(const bf16_t *__res
 constexpr int kNarrowRows = 32;
 constexpr int kNarrowMaxE = 10;
 constexpr int kNarrowRing = 2;    // units in flight per wave
+constexpr int kNarrowWaves = 8;   // waves per workgroup (16 measured no faster)
 constexpr int kBlkMaxE = kBlkCountMaxE;
 constexpr int kWtRowBytes = 80;   // LDS row stride of a part tile: 64 B of data + 16 B pad
 constexpr int kNarrowTileBytes = kNarrowRows * kWtRowBytes;
@@ -595,7 +596,7 @@ MOE_DEV void topk_lanes(float lv, int gl, bool live, int t, int E, const TopkOut
 }
 
 template <int TB, int NCH>   // NCH: 16-byte W_r chunks per lane and block (1: E <= 8, 2: E <= 10)
-__global__ __launch_bounds__(512) void router_mfma_narrow_kernel(const bf16_t *__restrict__ x,
+__global__ __launch_bounds__(64 * kNarrowWaves) void router_mfma_narrow_kernel(const bf16_t *__restrict__ x,
                                                                  const float *__restrict__ w,
                                                                  const float *__restrict__ bias,
                                                                  float *__restrict__ logits,
@@ -604,8 +605,9 @@ __global__ __launch_bounds__(512) void router_mfma_narrow_kernel(const bf16_t *_
                                                                  int32_t *__restrict__ blk_cnt) {
   constexpr int U = kNarrowRing;
   constexpr int TT = 16 * TB;   // tokens per workgroup
-  __shared__ float part[8][TT * kNarrowRows];
-  __shared__ __attribute__((aligned(16))) char wt[8][2 * kNarrowTileBytes];   // two per wave
+  constexpr int NW = kNarrowWaves, NT = 64 * NW;
+  __shared__ float part[NW][TT * kNarrowRows];
+  __shared__ __attribute__((aligned(16))) char wt[NW][2 * kNarrowTileBytes];   // two per wave
   __shared__ int cnt[kNarrowMaxE];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int t0 = blockIdx.x * TT;
@@ -705,13 +707,13 @@ __global__ __launch_bounds__(512) void router_mfma_narrow_kernel(const bf16_t *_
       }
   };
 #pragma unroll
-  for (int v = 0; v < U; ++v) issue(v, wv + 8 * v);
-  for (int ub = wv; ub < nu; ub += 8 * U) {
+  for (int v = 0; v < U; ++v) issue(v, wv + NW * v);
+  for (int ub = wv; ub < nu; ub += NW * U) {
 #pragma unroll
     for (int v = 0; v < U; ++v) {
-      const int ui = ub + 8 * v;
+      const int ui = ub + NW * v;
       if (ui < nu) consume(v);   // wave-uniform
-      issue(v, ui + 8 * U);
+      issue(v, ui + NW * U);
     }
   }
   // lane l holds rows 4*(l/16) + i, column l%16 of each 16 x 16 block
@@ -724,20 +726,24 @@ __global__ __launch_bounds__(512) void router_mfma_narrow_kernel(const bf16_t *_
       part[wv][r * kNarrowRows + 16 + (lane & 15)] = acc1[b][i];
     }
   __syncthreads();
-  float sum[TB];
+  constexpr int NS = (TT * kNarrowRows + NT - 1) / NT;   // sums per thread
+  float sum[NS];
 #pragma unroll
-  for (int b = 0; b < TB; ++b) {
-    const int idx = b * 512 + threadIdx.x;   // token * 32 + row
-    sum[b] = part[0][idx];
+  for (int j = 0; j < NS; ++j) {
+    const int idx = j * NT + threadIdx.x;   // token * 32 + row
+    if (idx < TT * kNarrowRows) {
+      sum[j] = part[0][idx];
 #pragma unroll
-    for (int q = 1; q < 8; ++q) sum[b] += part[q][idx];
+      for (int q = 1; q < NW; ++q) sum[j] += part[q][idx];
+    }
   }
   __syncthreads();
 #pragma unroll
-  for (int b = 0; b < TB; ++b) part[0][b * 512 + threadIdx.x] = sum[b];
+  for (int j = 0; j < NS; ++j)
+    if (j * NT + (int)threadIdx.x < TT * kNarrowRows) part[0][j * NT + threadIdx.x] = sum[j];
   __syncthreads();
   float *lg = &part[1][0];   // [TT][E] final logits for the fused top-k
-  for (int i = threadIdx.x; i < TT * E; i += 512) {
+  for (int i = threadIdx.x; i < TT * E; i += NT) {
     const int r = i / E, e = i % E, t = t0 + r;
     const float *sr = &part[0][r * kNarrowRows];
     const float v = ((sr[e] + sr[E + e]) + sr[2 * E + e]) + (bias ? bias[e] : 0.f);
@@ -1845,7 +1851,7 @@ hipError_t launch_router(int dtype, const void *x, const float *w, const float *
     const int tb = T >= 16 * 2 * 256 ? 2 : 1;   // two token blocks per workgroup halve the W reads
     if (tk.blk_cnt && cnt_block) *cnt_block = 16 * tb;
 #define MOE_NARROW(TBB, NCHH) hipLaunchKernelGGL((router_mfma_narrow_kernel<TBB, NCHH>),          \
-                                               dim3((T + 16 * TBB - 1) / (16 * TBB)), dim3(512), 0, \
+                                               dim3((T + 16 * TBB - 1) / (16 * TBB)), dim3(64 * kNarrowWaves), 0, \
                                                st, (const bf16_t *)x, w, bias, logits, T, d, E, tk, \
                                                tk.blk_cnt)
     if (tb == 2) { if (E <= 8) MOE_NARROW(2, 1); else MOE_NARROW(2, 2); }
