@@ -24,10 +24,11 @@ is a fixed float32 encoding (the routing-score spec below). Steps:
      expert choice  each expert keeps the c = floor(k*T/E) tokens with the
                     largest logit in its column (ties: lower token first);
                     weight = softmax over the T tokens of that column
-                    (hrletsgo page, Mixture-of-Tokens section). Parity
-                    unpinned for this weight: no page fixes the softmax axis,
-                    so it rests on the workload's wording; the selection
-                    itself is pinned against brute-force subsets
+                    (hrletsgo page, Mixture-of-Tokens section). The axis of
+                    this softmax is a reading (no page fixes it; the workload
+                    names a softmax over tokens); its computation is pinned by
+                    a hand example and by scipy's softmax over each column,
+                    and the selection against brute-force subsets
      capacity drop  after token choice, an expert with more than
                     C = floor(gamma * T*k/E) candidates keeps the C with the
                     highest routing score p32 (ties: lower token first); dropped
@@ -80,8 +81,9 @@ invariants fixed by the pages (exactly k per token, exactly c per expert,
 no expert above C, dropped pairs never outrank kept ones), agreement of the per-row
 route (expert_rows_ffn + combine) with the per-token one (layer_forward), and an
 exhaustive check of rexp against the float64 exponential over every float32 in [-87, 0].
-Parity unpinned: the expert-choice combine weight's axis (see above) and the Zipf bias
-mapping of the skewed workload, which rests on its stated ~40% share only.
+Readings rather than pins: the expert-choice weight's softmax axis (see above) and the Zipf
+bias mapping of the skewed workload's inputs (checked against its stated ~40% share); every
+function here has a pin of its own.
 """
 from __future__ import annotations
 
