@@ -646,6 +646,7 @@ __global__ __launch_bounds__(256) void gemm_tail_reduce_kernel(GemmArgs args) {
 // and a thousand short units measured slower); with S > 1 each unit writes float32 sums to
 // the partial buffer and gemm_skinny_reduce_kernel adds the parts in order.
 struct SkinnyPlan { int mb, S, nt, snt, pitch; };
+constexpr int kSkinnyMaxParts = 16;
 
 SkinnyPlan skinny_plan(const GemmArgs &a, bool gate_up) {
   SkinnyPlan sp{0, 1, 0, 0, 0};
@@ -665,7 +666,7 @@ SkinnyPlan skinny_plan(const GemmArgs &a, bool gate_up) {
   // and T=64 no better)
   const int target = tiles < 128 ? 512 : 256;
   auto can_split = [&](int s) {   // parts of at least two slices that divide both K ranges
-    return s <= 16 && nk % s == 0 && snk % s == 0 && nk / s >= 2 && snk / s >= 2;
+    return s <= kSkinnyMaxParts && nk % s == 0 && snk % s == 0 && nk / s >= 2 && snk / s >= 2;
   };
   int S = 1;
   while (tiles * S < target && can_split(2 * S)) S *= 2;
@@ -849,14 +850,22 @@ __global__ __launch_bounds__(256) void gemm_skinny_reduce_kernel(GemmArgs args) 
     (void)ldc;
     if (c >= N) continue;
     const float *P = args.partials + (size_t)prow * pitch + c;
+    // every part's loads go out before the sums, which run in part order from 0
     if (GATE_UP) {
+      float4 gp[kSkinnyMaxParts], up[kSkinnyMaxParts];
+#pragma unroll
+      for (int p = 0; p < kSkinnyMaxParts; ++p)
+        if (p < S) {
+          gp[p] = *(const float4 *)(P + p * part);
+          up[p] = *(const float4 *)(P + p * part + pitch / 2);
+        }
       float4 gs = make_float4(0.f, 0.f, 0.f, 0.f), us = gs;
-      for (int p = 0; p < S; ++p) {
-        const float4 gp = *(const float4 *)(P + p * part);
-        const float4 up = *(const float4 *)(P + p * part + pitch / 2);
-        gs.x += gp.x; gs.y += gp.y; gs.z += gp.z; gs.w += gp.w;
-        us.x += up.x; us.y += up.y; us.z += up.z; us.w += up.w;
-      }
+#pragma unroll
+      for (int p = 0; p < kSkinnyMaxParts; ++p)
+        if (p < S) {
+          gs.x += gp[p].x; gs.y += gp[p].y; gs.z += gp[p].z; gs.w += gp[p].w;
+          us.x += up[p].x; us.y += up[p].y; us.z += up[p].z; us.w += up[p].w;
+        }
       const float gv[4] = {gs.x, gs.y, gs.z, gs.w}, uv[4] = {us.x, us.y, us.z, us.w};
       uint32_t pk[2];
 #pragma unroll
@@ -867,12 +876,75 @@ __global__ __launch_bounds__(256) void gemm_skinny_reduce_kernel(GemmArgs args) 
       }
       *(uint2 *)((bf16_t *)C + c) = make_uint2(pk[0], pk[1]);
     } else {
+      float4 pp[kSkinnyMaxParts];
+#pragma unroll
+      for (int p = 0; p < kSkinnyMaxParts; ++p)
+        if (p < S) pp[p] = *(const float4 *)(P + p * part);
       float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-      for (int p = 0; p < S; ++p) {
-        const float4 pp = *(const float4 *)(P + p * part);
-        v.x += pp.x; v.y += pp.y; v.z += pp.z; v.w += pp.w;
-      }
+#pragma unroll
+      for (int p = 0; p < kSkinnyMaxParts; ++p)
+        if (p < S) { v.x += pp[p].x; v.y += pp[p].y; v.z += pp[p].z; v.w += pp[p].w; }
       *(float4 *)((float *)C + c) = v;
+    }
+  }
+}
+
+// Decode-shaped layer: the skinny down GEMM's K parts summed (as gemm_skinny_reduce_kernel
+// does) straight into the weighted combine (as combine_kernel does), one launch instead of
+// two. Thread (t, c) takes 4 output columns of token t: it forms each o row of the token from
+// its parts in part order, adds it into the token's sum in CSR order with the pair's gate
+// (rows in pairs, the second of an odd count with gate 0, as the combine does), then the
+// shared expert's row likewise, and writes y once: the operations and their order are the two
+// kernels', so y is bit for bit theirs.
+template <typename TY>
+__global__ __launch_bounds__(256) void skinny_down_combine_kernel(GemmArgs args,
+                                                                  const int32_t *__restrict__ tok_ptr,
+                                                                  const int32_t *__restrict__ tok_pos,
+                                                                  const float *__restrict__ perm_w,
+                                                                  TY *__restrict__ y, int T, int d) {
+  const int S = args.sk_S, pitch = args.sk_pitch;
+  const size_t part = (size_t)(args.rcap + args.s_rows) * pitch;
+  const int q = d / 4;   // column quads per row
+  auto row_sum = [&](int prow, int c) {   // o[prow][c .. c+3] from its K parts
+    // every part's load goes out before the sums (S <= kSkinnyMaxParts)
+    const float *P = args.partials + (size_t)prow * pitch + c;
+    float4 u[kSkinnyMaxParts];
+#pragma unroll
+    for (int k = 0; k < kSkinnyMaxParts; ++k)
+      if (k < S) u[k] = *(const float4 *)(P + k * part);
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);   // from 0, as the reduction kernel sums
+#pragma unroll
+    for (int k = 0; k < kSkinnyMaxParts; ++k)
+      if (k < S) { v.x += u[k].x; v.y += u[k].y; v.z += u[k].z; v.w += u[k].w; }
+    return v;
+  };
+  for (int it = blockIdx.x * blockDim.x + threadIdx.x; it < T * q; it += gridDim.x * blockDim.x) {
+    const int t = it / q, c = (it % q) * 4;
+    const int b = tok_ptr[t], n = tok_ptr[t + 1] - b;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int j = 0; j < n; j += 2) {
+      const int p0 = tok_pos[b + j];
+      const bool two = j + 1 < n;
+      const int p1 = two ? tok_pos[b + j + 1] : p0;
+      const float w0 = perm_w[p0], w1 = two ? perm_w[p1] : 0.f;
+      const float4 v0 = row_sum(p0, c), v1 = row_sum(p1, c);
+      acc.x = fmaf(w0, v0.x, acc.x); acc.y = fmaf(w0, v0.y, acc.y);
+      acc.z = fmaf(w0, v0.z, acc.z); acc.w = fmaf(w0, v0.w, acc.w);
+      acc.x = fmaf(w1, v1.x, acc.x); acc.y = fmaf(w1, v1.y, acc.y);
+      acc.z = fmaf(w1, v1.z, acc.z); acc.w = fmaf(w1, v1.w, acc.w);
+    }
+    if (args.s_rows > 0) {
+      const float4 v = row_sum(args.rcap + t, c);
+      acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+    }
+    TY *yp = y + (size_t)t * d + c;
+    if constexpr (sizeof(TY) == 2) {
+      uint2 pk;
+      pk.x = (uint32_t)f32_to_bf16(acc.x) | ((uint32_t)f32_to_bf16(acc.y) << 16);
+      pk.y = (uint32_t)f32_to_bf16(acc.z) | ((uint32_t)f32_to_bf16(acc.w) << 16);
+      *reinterpret_cast<uint2 *>(yp) = pk;
+    } else {
+      *reinterpret_cast<float4 *>(yp) = acc;
     }
   }
 }
@@ -1006,7 +1078,7 @@ hipError_t launch_bf16(const GemmArgs &a0, bool gate_up, int max_rows, int num_c
 }
 
 hipError_t launch_skinny(const GemmArgs &a0, bool gate_up, const SkinnyPlan &sp, int num_cu,
-                         hipStream_t st) {
+                         hipStream_t st, bool defer_reduce = false) {
   GemmArgs a = a0;
   a.sk_S = sp.S;
   a.sk_pitch = sp.pitch;
@@ -1027,7 +1099,7 @@ hipError_t launch_skinny(const GemmArgs &a0, bool gate_up, const SkinnyPlan &sp,
     else
       hipLaunchKernelGGL((gemm_skinny_kernel<false, 2>), dim3(grid), dim3(256), 0, st, a);
   }
-  if (sp.S > 1) {
+  if (sp.S > 1 && !defer_reduce) {
     const long items = (long)(a.rcap + a.s_rows) * (gate_up ? sp.pitch / 2 : sp.pitch) / 4;
     long rg = (items + 255) / 256;
     if (rg > 4 * num_cu) rg = 4 * num_cu;
@@ -1040,11 +1112,38 @@ hipError_t launch_skinny(const GemmArgs &a0, bool gate_up, const SkinnyPlan &sp,
   return hipGetLastError();
 }
 
+bool skinny_split_down(const GemmArgs &a) {
+  if (a.elt != 2 || !a.partials) return false;
+  const SkinnyPlan sp = skinny_plan(a, false);
+  return sp.mb != 0 && sp.S > 1;
+}
+
+hipError_t launch_skinny_down_combine(const GemmArgs &a0, int y_elt, const int32_t *tok_ptr,
+                                      const int32_t *tok_pos, const float *perm_w, void *y,
+                                      int T, int d, int num_cu, hipStream_t st) {
+  const SkinnyPlan sp = skinny_plan(a0, false);
+  if (!sp.mb || sp.S < 2 || !a0.partials) return hipErrorInvalidValue;
+  GemmArgs a = a0;
+  a.sk_S = sp.S;
+  a.sk_pitch = sp.pitch;
+  const long items = (long)T * d / 4;
+  long rg = (items + 255) / 256;
+  if (rg > 4 * num_cu) rg = 4 * num_cu;
+  if (rg < 1) rg = 1;
+  if (y_elt == 2)
+    hipLaunchKernelGGL(skinny_down_combine_kernel<bf16_t>, dim3(rg), dim3(256), 0, st, a, tok_ptr,
+                       tok_pos, perm_w, (bf16_t *)y, T, d);
+  else
+    hipLaunchKernelGGL(skinny_down_combine_kernel<float>, dim3(rg), dim3(256), 0, st, a, tok_ptr,
+                       tok_pos, perm_w, (float *)y, T, d);
+  return hipGetLastError();
+}
+
 hipError_t launch_gemm(const GemmArgs &a, bool gate_up, int max_rows, int num_cu,
-                       hipStream_t st) {
+                       hipStream_t st, bool defer_skinny_reduce) {
   if (a.elt == 2) {
     const SkinnyPlan sp = skinny_plan(a, gate_up);
-    if (sp.mb) return launch_skinny(a, gate_up, sp, num_cu, st);
+    if (sp.mb) return launch_skinny(a, gate_up, sp, num_cu, st, defer_skinny_reduce);
     return launch_bf16<MOE_GEMM_WAVES>(a, gate_up, max_rows, num_cu, st);
   }
   int grid = gemm_tiles_upper(a, 64, 64, max_rows);

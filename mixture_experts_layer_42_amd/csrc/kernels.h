@@ -146,8 +146,17 @@ hipError_t launch_gather(int elt, const void *x, const int32_t *perm_token,
 hipError_t launch_combine(int y_elt, const float *o, const float *o_shared,
                           const int32_t *tok_ptr, const int32_t *tok_pos, const float *perm_w,
                           void *y, int T, int d, int max_rows, hipStream_t st);
+// defer_skinny_reduce: on the skinny path with K parts, leave the parts unsummed for
+// launch_skinny_down_combine (down GEMM only)
 hipError_t launch_gemm(const GemmArgs &a, bool gate_up, int max_rows, int num_cu,
-                       hipStream_t st);
+                       hipStream_t st, bool defer_skinny_reduce = false);
+// whether the down GEMM a takes the skinny path with its K range cut into parts
+bool skinny_split_down(const GemmArgs &a);
+// after launch_gemm(a, false, ..., defer_skinny_reduce = true): the parts' sum and the
+// weighted combine into y (y_elt 2: bf16, 4: float32) in one launch
+hipError_t launch_skinny_down_combine(const GemmArgs &a, int y_elt, const int32_t *tok_ptr,
+                                      const int32_t *tok_pos, const float *perm_w, void *y,
+                                      int T, int d, int num_cu, hipStream_t st);
 hipError_t gemm_setup_attributes();
 
 }  // namespace moe

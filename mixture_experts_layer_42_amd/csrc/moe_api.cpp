@@ -377,14 +377,21 @@ hipError_t do_gate_up(const moe_problem &p, const void *x_perm, const moe_routin
   return launch_gemm(a, true, (int)rows_cap(p), num_cus(), st);
 }
 
-hipError_t do_down(const moe_problem &p, const moe_routing &r, const void *w_down,
-                   const void *ws_down, void *o_perm, void *o_shared, char *ws, hipStream_t st) {
+GemmArgs down_args(const moe_problem &p, const moe_routing &r, const void *w_down,
+                   const void *ws_down, void *o_perm, void *o_shared, char *ws) {
   const Layout L = make_layout(p);
   GemmArgs a = gemm_args(p, r, false, ws + L.h, w_down, nullptr, o_perm, ws + L.h_shared,
                          ws_down, nullptr, o_shared);
   a.partials = p.dtype == MOE_BF16 ? (float *)(ws + L.partials) : nullptr;
   a.split_ok = (p.d_ff_shared == 0 || p.d_ff_shared == p.d_ff) ? 1 : 0;   // one K for all groups
-  return launch_gemm(a, false, (int)rows_cap(p), num_cus(), st);
+  return a;
+}
+
+hipError_t do_down(const moe_problem &p, const moe_routing &r, const void *w_down,
+                   const void *ws_down, void *o_perm, void *o_shared, char *ws, hipStream_t st,
+                   bool defer_skinny_reduce = false) {
+  const GemmArgs a = down_args(p, r, w_down, ws_down, o_perm, o_shared, ws);
+  return launch_gemm(a, false, (int)rows_cap(p), num_cus(), st, defer_skinny_reduce);
 }
 
 hipError_t do_combine(const moe_problem &p, const void *o_perm, const void *o_shared,
@@ -454,9 +461,17 @@ moe_status layer_forward(const moe_problem *pp, const void *x, const float *w_ro
   MOE_TRY(mark(MOE_STAGE_GATE_UP));
   MOE_TRY(do_gate_up(p, nullptr, r, w_gate, w_up, x, ws_gate, ws_up, w, st));
   MOE_TRY(mark(MOE_STAGE_DOWN));
-  MOE_TRY(do_down(p, r, w_down, ws_down, w + L.o_perm, w + L.o_shared, w, st));
+  // decode-shaped batches whose down GEMM cuts K into parts: the parts' sum goes straight
+  // into the combine (one launch fewer; o is never written)
+  const GemmArgs da = down_args(p, r, w_down, ws_down, w + L.o_perm, w + L.o_shared, w);
+  const bool fuse = skinny_split_down(da);
+  MOE_TRY(do_down(p, r, w_down, ws_down, w + L.o_perm, w + L.o_shared, w, st, fuse));
   MOE_TRY(mark(MOE_STAGE_COMBINE));
-  MOE_TRY(do_combine(p, w + L.o_perm, w + L.o_shared, r, y, st));
+  if (fuse)
+    MOE_TRY(launch_skinny_down_combine(da, p.y_dtype == MOE_BF16 ? 2 : 4, r.tok_ptr, r.tok_pos,
+                                       r.perm_w, y, p.T, p.d_model, num_cus(), st));
+  else
+    MOE_TRY(do_combine(p, w + L.o_perm, w + L.o_shared, r, y, st));
   MOE_TRY(mark(MOE_STAGE_COUNT));
   return MOE_OK;
 }

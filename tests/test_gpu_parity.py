@@ -234,10 +234,14 @@ def test_layer_forward_small(name):
     check_y(cfg, host_f32(y), y_ref)
 
 
-@pytest.mark.parametrize("name", ["ragged-bf16", "fine-shared-bf16", "expert-choice-bf16"])
+@pytest.mark.parametrize("name", ["ragged-bf16", "fine-shared-bf16", "expert-choice-bf16",
+                                  "decode-T8-bf16", "decode-T48-shared-bf16",
+                                  "decode-T1-E64-bf16"])
 def test_layer_forward_deterministic_and_equal_to_steps(name):
     """Two runs give bit-identical routing and output; the one-call layer equals the four
-    separate entry points bit for bit (same kernels, no atomics in any decision or sum)."""
+    separate entry points bit for bit (the same arithmetic in the same order, no atomics in
+    any decision or sum; for decode shapes the layer sums the down GEMM's K parts inside the
+    combine, the separate entry points in their own kernel)."""
     import torch
     cfg = SMALL[name]
     inp = inputs_for(cfg)
