@@ -62,6 +62,9 @@ MOE_DEV int wave_incl_scan(int v) {
   return v;
 }
 
+// sum over the 64 lanes of a wave with the DPP scan above (lane 63 holds the total)
+MOE_DEV int wave_sum_dpp(int v) { return __builtin_amdgcn_readlane(wave_incl_scan(v), 63); }
+
 // Block-wide exclusive scan of one int per thread; returns the exclusive prefix and
 // writes the block total to *total. `smem` needs blockDim.x/64 + 1 ints. Contains barriers.
 MOE_DEV int block_excl_scan(int v, int *smem, int *total) {

@@ -997,8 +997,15 @@ __global__ __launch_bounds__(256) void dispatch_blocks_kernel(const int32_t *__r
   const int t0 = blockIdx.x * 256, b0 = t0 / bt;
   const int nb = min(256 / bt, nblk - b0);   // count blocks of this workgroup
   const int t = t0 + threadIdx.x;
-  // this workgroup's picks and gates (contiguous rows) and its blocks' count rows: their
-  // loads go out first and travel while the other blocks' counts are summed
+  // the first count row of this thread (the rows of every block, written by the top-k just
+  // before on any XCD, are the longest wait): its loads go out first, then this workgroup's
+  // picks and gates (contiguous rows) and its blocks' count rows, so that the waits overlap
+  int c0[EM];
+  {
+    const int r = threadIdx.x;
+#pragma unroll
+    for (int e = 0; e < EM; ++e) c0[e] = r < nblk ? blk_cnt[(size_t)r * E + min(e, E - 1)] : 0;
+  }
   const int nown = (min(T, t0 + 256) - t0) * k;
   for (int i = threadIdx.x; i < nown; i += 256) {
     sids[i] = ids[(size_t)t0 * k + i];
@@ -1013,8 +1020,12 @@ __global__ __launch_bounds__(256) void dispatch_blocks_kernel(const int32_t *__r
   // i, i + 256, ... (integer sums: the order does not change them)
   int va[EM], vp[EM];
 #pragma unroll
-  for (int e = 0; e < EM; ++e) va[e] = vp[e] = 0;
-  for (int r = threadIdx.x; r < nblk; r += 256) {
+  for (int e = 0; e < EM; ++e) {
+    const int ce = (e < E && (int)threadIdx.x < nblk) ? c0[e] : 0;
+    va[e] = ce;
+    vp[e] = (int)threadIdx.x < b0 ? ce : 0;
+  }
+  for (int r = threadIdx.x + 256; r < nblk; r += 256) {
     int c[EM];
 #pragma unroll
     for (int e = 0; e < EM; ++e) c[e] = blk_cnt[(size_t)r * E + min(e, E - 1)];
@@ -1027,7 +1038,7 @@ __global__ __launch_bounds__(256) void dispatch_blocks_kernel(const int32_t *__r
   }
 #pragma unroll
   for (int e = 0; e < EM; ++e) {
-    const int a = wave_sum_int(va[e]), b = wave_sum_int(vp[e]);
+    const int a = wave_sum_dpp(va[e]), b = wave_sum_dpp(vp[e]);
     if (lane == 0) { wsum[wid][e] = a; wsum[wid][EM + e] = b; }
   }
   __syncthreads();
