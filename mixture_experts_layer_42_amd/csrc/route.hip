@@ -1126,23 +1126,47 @@ struct PairSel {
 };
 
 constexpr int kMaxSlots = 16;   // pairs of one token in one bucket are tracked up to k <= 16
+constexpr int kSlotBatch = 8;   // slots of a token whose loads are issued together
+
+// Buckets of slots j .. j + kSlotBatch - 1 of token t (-1: past j1, or not kept), all loads
+// issued before any is used.
+MOE_DEV void slot_buckets(const int32_t *ids, const PairSel &f, int t, int j,
+                          int (&bk)[kSlotBatch]) {
+#pragma unroll
+  for (int i = 0; i < kSlotBatch; ++i) {
+    int b = -1;
+    if (j + i < f.j1) {
+      const size_t ij = (size_t)t * f.S + j + i;
+      const int id = ids[ij];
+      const bool kp = !f.kept || f.kept[ij];
+      b = kp ? (f.gs == 1 ? id : id / f.gs) : -1;
+    }
+    bk[i] = b;
+  }
+}
 
 MOE_DEV void build_masks(uint32_t *mask, const int32_t *ids, const PairSel &f, int T, int B) {
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  int bk[kSlotBatch];   // the first batch travels while the masks are cleared
+  if (t < T) slot_buckets(ids, f, t, f.j0, bk);
   for (int i = threadIdx.x; i < B * f.mult * 8; i += blockDim.x) mask[i] = 0u;
   __syncthreads();
-  const int t = blockIdx.x * 256 + threadIdx.x;
   if (t < T) {
     int seen[kMaxSlots];
     int ns = 0;
-    for (int j = f.j0; j < f.j1; ++j) {
-      if (f.kept && !f.kept[(size_t)t * f.S + j]) continue;
-      const int b = ids[(size_t)t * f.S + j] / f.gs;
-      int c = 0;
-      if (f.mult > 1) {
-        for (int q = 0; q < ns; ++q) c += seen[q] == b;
-        seen[ns++] = b;
+    for (int j = f.j0; j < f.j1; j += kSlotBatch) {
+      if (j > f.j0) slot_buckets(ids, f, t, j, bk);
+#pragma unroll
+      for (int i = 0; i < kSlotBatch; ++i) {
+        const int b = bk[i];
+        if (b < 0) continue;
+        int c = 0;
+        if (f.mult > 1) {
+          for (int q = 0; q < ns; ++q) c += seen[q] == b;
+          seen[ns++] = b;
+        }
+        atomicOr(&mask[(b * f.mult + c) * 8 + (threadIdx.x >> 5)], 1u << (threadIdx.x & 31));
       }
-      atomicOr(&mask[(b * f.mult + c) * 8 + (threadIdx.x >> 5)], 1u << (threadIdx.x & 31));
     }
   }
   __syncthreads();
@@ -1206,8 +1230,9 @@ __global__ __launch_bounds__(1024) void assign_scan_kernel(const int32_t *__rest
   }
 }
 
-// Stable scatter: pair (t, j) of bucket b goes to off[b] + base[b] + (its rank in the
-// block), base = this block's offsets inside the buckets (null: 0, a single block).
+// Stable scatter: pair (t, j) of bucket b goes to off[b] + (its rank in the block), off[b]
+// being where bucket b's rows of this block start (the bucket's offset plus the rows of the
+// earlier blocks in it), held in LDS.
 // Candidate mode writes (token, slot, key) lists for cap_select; final mode writes the
 // dispatch arrays, and marks the slots in [j0, j1) that were not taken with -1. When every
 // slot of every token is kept (no capacity limit), final mode can also write the token ->
@@ -1215,12 +1240,11 @@ __global__ __launch_bounds__(1024) void assign_scan_kernel(const int32_t *__rest
 // Expects the block's masks (build_masks) in `mask`.
 MOE_DEV void scatter_block(const uint32_t *mask, const int32_t *__restrict__ ids,
                            const float *__restrict__ gates, const float *__restrict__ keys, int T,
-                           const PairSel &f, const int32_t *off, const int32_t *base,
-                           int candidates, int32_t *__restrict__ out_token,
-                           float *__restrict__ out_w, int32_t *__restrict__ out_slot,
-                           float *__restrict__ out_key, int32_t *__restrict__ slot_pos,
-                           uint8_t *__restrict__ kept_out, int32_t *__restrict__ csr_ptr,
-                           int32_t *__restrict__ csr_pos) {
+                           const PairSel &f, const int32_t *off, int candidates,
+                           int32_t *__restrict__ out_token, float *__restrict__ out_w,
+                           int32_t *__restrict__ out_slot, float *__restrict__ out_key,
+                           int32_t *__restrict__ slot_pos, uint8_t *__restrict__ kept_out,
+                           int32_t *__restrict__ csr_ptr, int32_t *__restrict__ csr_pos) {
   const int t = blockIdx.x * 256 + threadIdx.x;
   if (t >= T) return;
   if (csr_ptr) {   // every pair kept, in slot order: token t's rows are CSR entries t*S ..
@@ -1228,38 +1252,60 @@ MOE_DEV void scatter_block(const uint32_t *mask, const int32_t *__restrict__ ids
     if (t == T - 1) csr_ptr[T] = T * f.S;
   }
   const int word = threadIdx.x >> 5, bit = threadIdx.x & 31;
+  const bool want_w = !candidates || out_w;
   int seen[kMaxSlots];
   int ns = 0;
-  for (int j = f.j0; j < f.j1; ++j) {
-    const size_t ij = (size_t)t * f.S + j;
-    if (f.kept && !f.kept[ij]) {
-      if (!candidates) slot_pos[ij] = -1;
-      continue;
+  for (int j = f.j0; j < f.j1; j += kSlotBatch) {
+    // the batch's buckets, gates and keys are loaded before any is used
+    int bk[kSlotBatch];
+    float gv[kSlotBatch], kv[kSlotBatch];
+    slot_buckets(ids, f, t, j, bk);
+#pragma unroll
+    for (int i = 0; i < kSlotBatch; ++i) {
+      const size_t ij = (size_t)t * f.S + j + i;
+      const bool in = j + i < f.j1;
+      gv[i] = (in && want_w) ? gates[ij] : 0.f;
+      kv[i] = (in && candidates) ? keys[ij] : 0.f;
     }
-    const int b = ids[ij] / f.gs;
-    int c = 0;
-    if (f.mult > 1) {
-      for (int q = 0; q < ns; ++q) c += seen[q] == b;
-      seen[ns++] = b;
-    }
-    int rank = c;
-    for (int m = 0; m < f.mult; ++m) {
-      const uint32_t *mk = mask + (b * f.mult + m) * 8;
-      rank += __popc(mk[word] & ((1u << bit) - 1u));
-      for (int w = 0; w < word; ++w) rank += __popc(mk[w]);
-    }
-    const int pos = off[b] + (base ? base[b] : 0) + rank;
-    if (candidates) {
-      out_token[pos] = t;
-      out_slot[pos] = j;
-      out_key[pos] = keys[ij];
-      if (out_w) out_w[pos] = gates[ij];   // the pair's gate rides along with its key
-    } else {
-      out_token[pos] = t;
-      out_w[pos] = gates[ij];
-      slot_pos[ij] = pos;
-      if (kept_out) kept_out[ij] = 1;
-      if (csr_pos) csr_pos[ij] = pos;
+#pragma unroll
+    for (int i = 0; i < kSlotBatch; ++i) {
+      if (j + i >= f.j1) break;
+      const size_t ij = (size_t)t * f.S + j + i;
+      const int b = bk[i];
+      if (b < 0) {   // not kept
+        if (!candidates) slot_pos[ij] = -1;
+        continue;
+      }
+      int c = 0;
+      if (f.mult > 1) {
+        for (int q = 0; q < ns; ++q) c += seen[q] == b;
+        seen[ns++] = b;
+      }
+      // rank: pairs of the bucket among the block's earlier tokens (the 8 mask words of the
+      // bucket in two 16-byte LDS reads), then the token's own earlier pairs in it
+      int rank = c;
+      for (int m = 0; m < f.mult; ++m) {
+        const uint4 *mk = reinterpret_cast<const uint4 *>(mask + (b * f.mult + m) * 8);
+        const uint4 lo = mk[0], hi = mk[1];
+        const uint32_t w[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+          rank += q < word ? __popc(w[q]) : (q == word ? __popc(w[q] & ((1u << bit) - 1u)) : 0);
+      }
+      const int pos = off[b] + rank;
+      const int jj = j + i;
+      if (candidates) {
+        out_token[pos] = t;
+        out_slot[pos] = jj;
+        out_key[pos] = kv[i];
+        if (out_w) out_w[pos] = gv[i];   // the pair's gate rides along with its key
+      } else {
+        out_token[pos] = t;
+        out_w[pos] = gv[i];
+        slot_pos[ij] = pos;
+        if (kept_out) kept_out[ij] = 1;
+        if (csr_pos) csr_pos[ij] = pos;
+      }
     }
   }
 }
@@ -1272,9 +1318,14 @@ __global__ __launch_bounds__(256) void assign_scatter_kernel(
     int32_t *__restrict__ slot_pos, uint8_t *__restrict__ kept_out, int32_t *__restrict__ csr_ptr,
     int32_t *__restrict__ csr_pos) {
   extern __shared__ uint32_t mask[];
+  // where each bucket's rows of this block start (bucket offset + the block's base), in LDS;
+  // build_masks' barriers order these writes before the scatter reads them
+  int32_t *soff = reinterpret_cast<int32_t *>(mask + (size_t)B * f.mult * 8);
+  const int32_t *bb = blk_base + (size_t)blockIdx.x * B;
+  for (int b = threadIdx.x; b < B; b += blockDim.x) soff[b] = off[b] + bb[b];
   build_masks(mask, ids, f, T, B);
-  scatter_block(mask, ids, gates, keys, T, f, off, blk_base + (size_t)blockIdx.x * B, candidates,
-                out_token, out_w, out_slot, out_key, slot_pos, kept_out, csr_ptr, csr_pos);
+  scatter_block(mask, ids, gates, keys, T, f, soff, candidates, out_token, out_w, out_slot,
+                out_key, slot_pos, kept_out, csr_ptr, csr_pos);
 }
 
 // All three steps for at most 256 tokens (one block): masks, bucket counts and offsets (as
@@ -1325,8 +1376,8 @@ __global__ __launch_bounds__(256) void assign_single_kernel(
     if (threadIdx.x == 0) off_fin[B] = tot;
   }
   __syncthreads();
-  scatter_block(mask, ids, gates, keys, T, f, soff, nullptr, candidates, out_token, out_w, out_slot,
-                out_key, slot_pos, kept_out, csr_ptr, csr_pos);
+  scatter_block(mask, ids, gates, keys, T, f, soff, candidates, out_token, out_w, out_slot, out_key,
+                slot_pos, kept_out, csr_ptr, csr_pos);
 }
 
 // Expanded drop, between its two selections: a token that lost some of its first k picks
@@ -1948,6 +1999,7 @@ void assign_pairs(const RouteScratch &s, const int32_t *ids, const float *gates,
                   int32_t *csr_ptr = nullptr, int32_t *csr_pos = nullptr) {
   const int nblk = (T + 255) / 256;
   const size_t msh = (size_t)B * f.mult * 8 * sizeof(uint32_t);
+  const size_t msh_sc = msh + (size_t)B * 4;   // + the bucket starts of the scatter
   int32_t *cnt = candidates ? s.cnt_pre : counts, *off = candidates ? s.off_pre : offsets;
   if (nblk == 1) {   // one launch instead of three
     if (candidates)
@@ -1967,12 +2019,12 @@ void assign_pairs(const RouteScratch &s, const int32_t *ids, const float *gates,
   hipLaunchKernelGGL(assign_scan_kernel, dim3(1), dim3(1024), 0, st, s.blk_cnt, nblk, B, -1,
                      s.blk_base, cnt, off, (int32_t *)nullptr, (int32_t *)nullptr);
   if (candidates)
-    hipLaunchKernelGGL(assign_scatter_kernel, dim3(nblk), dim3(256), msh, st, ids, gates, s.keys,
+    hipLaunchKernelGGL(assign_scatter_kernel, dim3(nblk), dim3(256), msh_sc, st, ids, gates, s.keys,
                        T, f, B, off, s.blk_base, 1, s.cand_token, s.cand_w, s.cand_slot,
                        s.cand_key, (int32_t *)nullptr, (uint8_t *)nullptr, (int32_t *)nullptr,
                        (int32_t *)nullptr);
   else
-    hipLaunchKernelGGL(assign_scatter_kernel, dim3(nblk), dim3(256), msh, st, ids, gates,
+    hipLaunchKernelGGL(assign_scatter_kernel, dim3(nblk), dim3(256), msh_sc, st, ids, gates,
                        (const float *)nullptr, T, f, B, off, s.blk_base, 0, perm_token, perm_w,
                        (int32_t *)nullptr, (float *)nullptr, s.slot_pos, kept_out, csr_ptr,
                        csr_pos);
@@ -2015,6 +2067,7 @@ hipError_t launch_token_dispatch(const RouteScratch &s, const int32_t *ids, cons
     return hipGetLastError();
   }
   const size_t msh = (size_t)E * 8 * sizeof(uint32_t);
+  const size_t msh_sc = msh + (size_t)E * 4;   // + the bucket starts of the scatter
   if (nblk == 1) {   // one launch instead of three
     hipLaunchKernelGGL(assign_single_kernel, dim3(1), dim3(256), msh + (size_t)E * 4, st, ids,
                        gates, s.keys, T, all, E, C, s.cnt_pre, s.off_pre, counts, offsets, 1,
@@ -2025,7 +2078,7 @@ hipError_t launch_token_dispatch(const RouteScratch &s, const int32_t *ids, cons
                        s.blk_cnt);
     hipLaunchKernelGGL(assign_scan_kernel, dim3(1), dim3(1024), 0, st, s.blk_cnt, nblk, E, C,
                        s.blk_base, s.cnt_pre, s.off_pre, counts, offsets);
-    hipLaunchKernelGGL(assign_scatter_kernel, dim3(nblk), dim3(256), msh, st, ids, gates, s.keys,
+    hipLaunchKernelGGL(assign_scatter_kernel, dim3(nblk), dim3(256), msh_sc, st, ids, gates, s.keys,
                        T, all, E, s.off_pre, s.blk_base, 1, s.cand_token, s.cand_w,
                        s.cand_slot, s.cand_key, (int32_t *)nullptr, (uint8_t *)nullptr,
                        (int32_t *)nullptr, (int32_t *)nullptr);
@@ -2060,13 +2113,14 @@ hipError_t launch_expanded_drop(const RouteScratch &s, const int32_t *ids, const
                                 hipStream_t st) {
   const int S = k + m, nblk = (T + 255) / 256;
   const size_t msh = (size_t)E * 8 * sizeof(uint32_t);
+  const size_t msh_sc = msh + (size_t)E * 4;   // + the bucket starts of the scatter
   // 1. token drop over the first k slots (flags); counts <- kept top-k pairs per expert
   const PairSel top{nullptr, S, 0, k, 1, 1};
   hipLaunchKernelGGL(assign_count_kernel, dim3(nblk), dim3(256), msh, st, ids, T, top, E,
                      s.blk_cnt);
   hipLaunchKernelGGL(assign_scan_kernel, dim3(1), dim3(1024), 0, st, s.blk_cnt, nblk, E, C,
                      s.blk_base, s.cnt_pre, s.off_pre, counts, offsets);
-  hipLaunchKernelGGL(assign_scatter_kernel, dim3(nblk), dim3(256), msh, st, ids, gates, s.keys, T,
+  hipLaunchKernelGGL(assign_scatter_kernel, dim3(nblk), dim3(256), msh_sc, st, ids, gates, s.keys, T,
                      top, E, s.off_pre, s.blk_base, 1, s.cand_token, s.cand_w,
                      s.cand_slot, s.cand_key, (int32_t *)nullptr, (uint8_t *)nullptr,
                      (int32_t *)nullptr, (int32_t *)nullptr);
