@@ -181,6 +181,10 @@ TIE_CASES = [
     # a huge capacity factor ("no limit"): the capacity is clamped to T*k, nothing is dropped
     dict(T=300, E=8, k=2, gamma=1e12), dict(T=300, E=8, k=2, gamma=1e12, expand_m=2),
     dict(T=300, E=8, k=2, gamma=1e12, cap_groups=2),
+    # more than 8 slots per token in the histogram + scatter (slot loads go in batches of 8):
+    # every pair kept, a capacity, the extra candidates of Expanded Drop, group capacity
+    dict(T=700, E=32, k=12), dict(T=700, E=32, k=12, gamma=0.8),
+    dict(T=600, E=32, k=4, gamma=0.5, expand_m=12), dict(T=500, E=32, k=12, gamma=1.25, cap_groups=4),
 ]
 
 
