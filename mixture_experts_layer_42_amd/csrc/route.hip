@@ -863,17 +863,26 @@ __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ log
 
 // Token-choice top-k for 33..128 experts and k <= 8, by merging instead of k rounds of group
 // argmax. A group of 16 lanes handles one token, lane i holding experts i, i+16, ... (8 each).
-// Each lane sorts its 8 (logit, expert) pairs by (logit desc, expert asc) with a 19-comparator
+// A (logit, expert) pair is one 64-bit key, the order-preserving image of the logit above
+// the complement of the expert index, so that "larger key" is the total order (logit desc,
+// expert asc) and a compare-exchange is one 64-bit compare and two selects (the two zeros
+// share a key, as they compare equal). Each lane sorts its 8 keys with a 19-comparator
 // network; then, for partner distance 8, 4, 2, 1, it takes the partner's sorted list, keeps
-// the better of A[i] and B[7-i] (a bitonic sequence holding the top 8 of both lists) and
+// the larger of A[i] and B[7-i] (a bitonic sequence holding the top 8 of both lists) and
 // sorts that with a 12-comparator bitonic merge. The order is total, so after four merges
 // every lane of the group holds the same sorted top 8: the picks in order. Gates and routing
 // keys follow topk_kernel's arithmetic exactly.
-struct KE { float v; int e; };
-MOE_DEV bool ke_before(const KE &a, const KE &b) { return a.v > b.v || (a.v == b.v && a.e < b.e); }
-MOE_DEV void ke_ce(KE &a, KE &b) {
-  const bool keep = ke_before(a, b);
-  const KE lo = keep ? b : a;
+MOE_DEV uint64_t pick_key(float v, int e) {
+  return ((uint64_t)float_key(v) << 32) | (uint32_t)~(uint32_t)e;
+}
+MOE_DEV float pick_value(uint64_t k) {   // the logit back (a zero comes back as +0)
+  const uint32_t u = (uint32_t)(k >> 32);
+  return __uint_as_float((u & 0x80000000u) ? (u & 0x7fffffffu) : ~u);
+}
+MOE_DEV int pick_expert(uint64_t k) { return (int)~(uint32_t)k; }
+MOE_DEV void key_ce(uint64_t &a, uint64_t &b) {   // a <- the larger, b <- the smaller
+  const bool keep = a > b;
+  const uint64_t lo = keep ? b : a;
   a = keep ? a : b;
   b = lo;
 }
@@ -889,42 +898,46 @@ __global__ __launch_bounds__(256) void topk_merge_kernel(const float *__restrict
   const int t = blockIdx.x * (256 / G) + gi;
   const bool live = t < T;
   float lv[PL];
-  KE a[PL];
+  uint64_t a[PL];
 #pragma unroll
   for (int i = 0; i < PL; ++i) {
     const int e = gl + i * G;
     lv[i] = (live && e < E) ? logits[(size_t)t * E + e] : -INFINITY;
-    a[i] = KE{lv[i], e < E ? e : 0x7fffffff};
+    a[i] = pick_key(lv[i], e < E ? e : 0x7fffffff);
   }
-  // sort the lane's 8 pairs (Batcher's odd-even merge sort)
-  ke_ce(a[0], a[1]); ke_ce(a[2], a[3]); ke_ce(a[4], a[5]); ke_ce(a[6], a[7]);
-  ke_ce(a[0], a[2]); ke_ce(a[1], a[3]); ke_ce(a[4], a[6]); ke_ce(a[5], a[7]);
-  ke_ce(a[1], a[2]); ke_ce(a[5], a[6]);
-  ke_ce(a[0], a[4]); ke_ce(a[1], a[5]); ke_ce(a[2], a[6]); ke_ce(a[3], a[7]);
-  ke_ce(a[2], a[4]); ke_ce(a[3], a[5]);
-  ke_ce(a[1], a[2]); ke_ce(a[3], a[4]); ke_ce(a[5], a[6]);
+  // sort the lane's 8 keys, largest first (Batcher's odd-even merge sort)
+  key_ce(a[0], a[1]); key_ce(a[2], a[3]); key_ce(a[4], a[5]); key_ce(a[6], a[7]);
+  key_ce(a[0], a[2]); key_ce(a[1], a[3]); key_ce(a[4], a[6]); key_ce(a[5], a[7]);
+  key_ce(a[1], a[2]); key_ce(a[5], a[6]);
+  key_ce(a[0], a[4]); key_ce(a[1], a[5]); key_ce(a[2], a[6]); key_ce(a[3], a[7]);
+  key_ce(a[2], a[4]); key_ce(a[3], a[5]);
+  key_ce(a[1], a[2]); key_ce(a[3], a[4]); key_ce(a[5], a[6]);
 #pragma unroll
   for (int o = G / 2; o > 0; o >>= 1) {
-    KE b[PL];
+    uint64_t b[PL];
 #pragma unroll
     for (int i = 0; i < PL; ++i) {
-      b[i].v = __shfl_xor(a[i].v, o, 64);
-      b[i].e = __shfl_xor(a[i].e, o, 64);
+      const uint32_t hi = __shfl_xor((uint32_t)(a[i] >> 32), o, 64);
+      const uint32_t lo = __shfl_xor((uint32_t)a[i], o, 64);
+      b[i] = ((uint64_t)hi << 32) | lo;
     }
 #pragma unroll
     for (int i = 0; i < PL; ++i)
-      if (!ke_before(a[i], b[PL - 1 - i])) a[i] = b[PL - 1 - i];
+      if (b[PL - 1 - i] > a[i]) a[i] = b[PL - 1 - i];
 #pragma unroll
     for (int dd = PL / 2; dd > 0; dd >>= 1)
 #pragma unroll
       for (int i = 0; i < PL; ++i)
-        if ((i & dd) == 0) ke_ce(a[i], a[i + dd]);
+        if ((i & dd) == 0) key_ce(a[i], a[i + dd]);
   }
-  const float mx = a[0].v;
+  float av[PL];
+#pragma unroll
+  for (int r = 0; r < PL; ++r) av[r] = pick_value(a[r]);
+  const float mx = av[0];
   float qn[PL], qsum = 0.f;
 #pragma unroll
   for (int r = 0; r < PL; ++r) {
-    qn[r] = expf(a[r].v - mx);
+    qn[r] = expf(av[r] - mx);
     if (r < k && r < kden) qsum += qn[r];
   }
   float denom = qsum;
@@ -943,7 +956,7 @@ __global__ __launch_bounds__(256) void topk_merge_kernel(const float *__restrict
 #pragma unroll
     for (int r = 0; r < PL; ++r)
       if (r < k) {
-        ids[(size_t)t * k + r] = a[r].e;
+        ids[(size_t)t * k + r] = pick_expert(a[r]);
         gates[(size_t)t * k + r] = qn[r] / denom;
       }
   }
@@ -960,7 +973,7 @@ __global__ __launch_bounds__(256) void topk_merge_kernel(const float *__restrict
       for (int e = 1; e < E; ++e) S = __fadd_rn(S, qrow[e]);
 #pragma unroll
       for (int r = 0; r < PL; ++r)
-        if (r < k) keys[(size_t)t * k + r] = qrow[a[r].e] / S;
+        if (r < k) keys[(size_t)t * k + r] = qrow[pick_expert(a[r])] / S;
     }
   }
 }
