@@ -20,7 +20,7 @@ struct RouteScratch {
   float *cand_key;      // [T*S]
   float *cand_w;        // [T*S] gate of each candidate
   int32_t *slot_pos;    // [T*S] row of (token, slot) or -1; S = k + m (token choice) or E
-  uint32_t *colkeys;    // [E*T] expert-choice column keys
+  uint32_t *colkeys;    // [E*T] expert-choice column keys (or the transposed logits)
   int32_t *tok_blk;     // [nblk] per-block row counts of the token CSR
   int32_t *tok_blk_off; // [nblk]
   float *stats_part;    // [nblk*E]
@@ -82,13 +82,20 @@ struct TopkOut {
   int32_t *blk_cnt;   // optional: picks per expert of each workgroup's tokens (E <= 16)
 };
 constexpr int kBlkCountMaxE = 16;   // experts the per-block counts and their dispatch handle
+// Optional extra output of the router for expert choice: the logits transposed ([E][T]).
+struct RouterExtra {
+  float *logits_t;
+};
 // logits = x W_r + b; with topk non-null, the router may also run the top-k of every token
 // (same results as launch_topk) and then sets *topk_done; when it also wrote topk->blk_cnt,
-// *cnt_block is the number of tokens per count block (else 0)
+// *cnt_block is the number of tokens per count block (else 0). With ex non-null, the
+// matrix-core router for at most 10 experts also writes ex's outputs and sets *ex_done
+// (other routers leave them and set it false).
 hipError_t launch_router(int dtype, const void *x, const float *w, const float *bias,
                          float *logits, int T, int d, int E, uint16_t *w3, hipStream_t st,
                          const TopkOut *topk = nullptr, bool *topk_done = nullptr,
-                         int *cnt_block = nullptr);
+                         int *cnt_block = nullptr, const RouterExtra *ex = nullptr,
+                         bool *ex_done = nullptr);
 // with blk_cnt non-null (E <= 16) the picks per expert of each workgroup's tokens go there and
 // *cnt_block gets the tokens per workgroup
 hipError_t launch_topk(const float *logits, int T, int E, int k, int kden, int renorm,
@@ -133,9 +140,11 @@ hipError_t launch_expanded_drop(const RouteScratch &s, const int32_t *ids, const
                                 int T, int k, int m, int E, int C, int32_t *perm_token,
                                 float *perm_w, uint8_t *kept, int32_t *counts, int32_t *offsets,
                                 hipStream_t st);
+// Expert choice. With logits_t (the logits transposed, [E][T]) the selection reads each
+// expert's column as one contiguous row.
 hipError_t launch_expert_choice(const RouteScratch &s, const float *logits, int T, int E, int c,
                                 int32_t *perm_token, float *perm_w, int32_t *counts,
-                                int32_t *offsets, hipStream_t st);
+                                int32_t *offsets, hipStream_t st, const float *logits_t = nullptr);
 hipError_t launch_token_csr(const RouteScratch &s, int T, int S, int32_t *tok_ptr,
                             int32_t *tok_pos, hipStream_t st);
 hipError_t launch_stats(const float *logits, const int32_t *counts, const int32_t *offsets, int T,

@@ -290,12 +290,15 @@ hipError_t do_route(const moe_problem &p, const void *x, const float *w_router,
                             p.cap_groups == 0 && p.E <= kBlkCountMaxE;
   const TopkOut tk{p.k + p.expand_m, p.k, p.renorm_topk, C >= 0 ? 1 : 0, r.topk_ids, r.topk_w,
                    s.keys, blk_dispatch ? s.blk_cnt : nullptr};
-  bool topk_done = false;
+  bool topk_done = false, ex_done = false;
   int cnt_block = 0;
+  // expert choice: the router may also write the logits transposed (the selection's column
+  // reads)
+  const RouterExtra ex{(float *)s.colkeys};
   if (!(flags & MOE_ROUTE_LOGITS_IN)) {
     e = launch_router(p.dtype == MOE_BF16 ? 1 : 0, x, w_router, bias, r.logits, p.T, p.d_model,
                       p.E, s.w3, st, p.routing == MOE_TOKEN_CHOICE ? &tk : nullptr, &topk_done,
-                      &cnt_block);
+                      &cnt_block, p.routing == MOE_EXPERT_CHOICE ? &ex : nullptr, &ex_done);
     if (e != hipSuccess) return e;
   }
   if (p.routing == MOE_TOKEN_CHOICE) {
@@ -339,7 +342,7 @@ hipError_t do_route(const moe_problem &p, const void *x, const float *w_router,
   } else {
     const int c = (int)(((int64_t)p.k * p.T) / p.E);
     e = launch_expert_choice(s, r.logits, p.T, p.E, c, r.perm_token, r.perm_w, r.counts,
-                             r.offsets, st);
+                             r.offsets, st, ex_done ? ex.logits_t : nullptr);
     if (e != hipSuccess) return e;
   }
   return launch_token_csr(s, p.T, slot_width(p), r.tok_ptr, r.tok_pos, st);

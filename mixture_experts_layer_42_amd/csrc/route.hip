@@ -602,7 +602,8 @@ __global__ __launch_bounds__(64 * kNarrowWaves) void router_mfma_narrow_kernel(c
                                                                  float *__restrict__ logits,
                                                                  int T, int d, int E,
                                                                  TopkOut topk,
-                                                                 int32_t *__restrict__ blk_cnt) {
+                                                                 int32_t *__restrict__ blk_cnt,
+                                                                 RouterExtra ex) {
   constexpr int U = kNarrowRing;
   constexpr int TT = 16 * TB;   // tokens per workgroup
   constexpr int NW = kNarrowWaves, NT = 64 * NW;
@@ -749,6 +750,13 @@ __global__ __launch_bounds__(64 * kNarrowWaves) void router_mfma_narrow_kernel(c
     const float v = ((sr[e] + sr[E + e]) + sr[2 * E + e]) + (bias ? bias[e] : 0.f);
     lg[i] = v;
     if (t < T) logits[(size_t)t * E + e] = v;
+  }
+  if (ex.logits_t) {   // expert choice: the same logits transposed, expert-major rows of T
+    __syncthreads();
+    for (int i = threadIdx.x; i < TT * E; i += NT) {
+      const int e = i / TT, r = i - e * TT, t = t0 + r;
+      if (t < T) ex.logits_t[(size_t)e * T + t] = lg[r * E + e];
+    }
   }
   if (!topk.ids) return;   // block-uniform
   __syncthreads();
@@ -1683,8 +1691,9 @@ __global__ __launch_bounds__(1024) void ec_select_kernel(const float *__restrict
 
 // The same selection with the column held in registers (T <= 1024 KPT): thread tid owns
 // tokens tid + 1024 j (chunk j), so ranks taken chunk by chunk, threads in order, follow
-// ascending token. One pass reads the column; the radix selection and the ordered
-// compaction (two vector scans) work on registers and LDS only.
+// ascending token. One pass reads the column (from the transposed logits when given: one
+// contiguous row); the radix selection and the ordered compaction (two vector scans) work on
+// registers and LDS only.
 template <int KPT>
 __global__ __launch_bounds__(1024) void ec_select_regs_kernel(const float *__restrict__ logits,
                                                               int T, int E, int c,
@@ -1692,7 +1701,8 @@ __global__ __launch_bounds__(1024) void ec_select_regs_kernel(const float *__res
                                                               float *__restrict__ perm_w,
                                                               int32_t *__restrict__ slot_pos,
                                                               int32_t *__restrict__ counts,
-                                                              int32_t *__restrict__ offsets) {
+                                                              int32_t *__restrict__ offsets,
+                                                              const float *__restrict__ logits_t) {
   __shared__ int hist[kSelWaves * 256];
   __shared__ int sm[kSelWaves * KPT + KPT];
   __shared__ float fsm[1024 / 64];
@@ -1703,7 +1713,7 @@ __global__ __launch_bounds__(1024) void ec_select_regs_kernel(const float *__res
 #pragma unroll
   for (int j = 0; j < KPT; ++j) {
     const int t = threadIdx.x + 1024 * j;
-    v[j] = t < T ? logits[(size_t)t * E + e] : -INFINITY;
+    v[j] = t < T ? (logits_t ? logits_t[(size_t)e * T + t] : logits[(size_t)t * E + e]) : -INFINITY;
     u[j] = t < T ? float_key(v[j]) : 0u;
     mx = fmaxf(mx, v[j]);
   }
@@ -1917,18 +1927,22 @@ size_t router_w3_bytes(int dtype, int d, int E) {
 
 hipError_t launch_router(int dtype, const void *x, const float *w, const float *bias,
                          float *logits, int T, int d, int E, bf16_t *w3, hipStream_t st,
-                         const TopkOut *topk, bool *topk_done, int *cnt_block) {
+                         const TopkOut *topk, bool *topk_done, int *cnt_block,
+                         const RouterExtra *ex, bool *ex_done) {
   if (topk_done) *topk_done = false;
   if (cnt_block) *cnt_block = 0;
+  if (ex_done) *ex_done = false;
   if (router_narrow_mfma(dtype, d, E)) {
     const TopkOut tk = topk ? *topk : TopkOut{0, 0, 0, 0, nullptr, nullptr, nullptr, nullptr};
     if (topk && topk_done) *topk_done = true;
+    const RouterExtra rx = ex ? *ex : RouterExtra{nullptr};
+    if (ex && ex_done) *ex_done = true;
     const int tb = T >= 16 * 2 * 256 ? 2 : 1;   // two token blocks per workgroup halve the W reads
     if (tk.blk_cnt && cnt_block) *cnt_block = 16 * tb;
 #define MOE_NARROW(TBB, NCHH) hipLaunchKernelGGL((router_mfma_narrow_kernel<TBB, NCHH>),          \
                                                dim3((T + 16 * TBB - 1) / (16 * TBB)), dim3(64 * kNarrowWaves), 0, \
                                                st, (const bf16_t *)x, w, bias, logits, T, d, E, tk, \
-                                               tk.blk_cnt)
+                                               tk.blk_cnt, rx)
     if (tb == 2) { if (E <= 8) MOE_NARROW(2, 1); else MOE_NARROW(2, 2); }
     else { if (E <= 8) MOE_NARROW(1, 1); else MOE_NARROW(1, 2); }
 #undef MOE_NARROW
@@ -2157,9 +2171,11 @@ hipError_t launch_expanded_drop(const RouteScratch &s, const int32_t *ids, const
 
 hipError_t launch_expert_choice(const RouteScratch &s, const float *logits, int T, int E, int c,
                                 int32_t *perm_token, float *perm_w, int32_t *counts,
-                                int32_t *offsets, hipStream_t st) {
+                                int32_t *offsets, hipStream_t st, const float *logits_t) {
+  if (T > 16384) logits_t = nullptr;
 #define MOE_EC(K) hipLaunchKernelGGL((ec_select_regs_kernel<K>), dim3(E), dim3(1024), 0, st, logits, \
-                                     T, E, c, perm_token, perm_w, s.slot_pos, counts, offsets)
+                                     T, E, c, perm_token, perm_w, s.slot_pos, counts, offsets,   \
+                                     logits_t)
   if (T <= 2048) MOE_EC(2);
   else if (T <= 4096) MOE_EC(4);
   else if (T <= 8192) MOE_EC(8);
