@@ -90,12 +90,16 @@ struct RouterExtra {
 // (same results as launch_topk) and then sets *topk_done; when it also wrote topk->blk_cnt,
 // *cnt_block is the number of tokens per count block (else 0). With ex non-null, the
 // matrix-core router for at most 10 experts also writes ex's outputs and sets *ex_done
-// (other routers leave them and set it false).
+// (other routers leave them and set it false). With disp non-null (final mode, the
+// BlkDispatchOut of launch_dispatch_blocks) and at most 16 tokens, that router also writes
+// the dispatch itself and sets *disp_done.
+struct BlkDispatchOut;
 hipError_t launch_router(int dtype, const void *x, const float *w, const float *bias,
                          float *logits, int T, int d, int E, uint16_t *w3, hipStream_t st,
                          const TopkOut *topk = nullptr, bool *topk_done = nullptr,
                          int *cnt_block = nullptr, const RouterExtra *ex = nullptr,
-                         bool *ex_done = nullptr);
+                         bool *ex_done = nullptr, const BlkDispatchOut *disp = nullptr,
+                         bool *disp_done = nullptr);
 // with blk_cnt non-null (E <= 16) the picks per expert of each workgroup's tokens go there and
 // *cnt_block gets the tokens per workgroup
 hipError_t launch_topk(const float *logits, int T, int E, int k, int kden, int renorm,

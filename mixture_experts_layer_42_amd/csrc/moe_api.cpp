@@ -290,15 +290,23 @@ hipError_t do_route(const moe_problem &p, const void *x, const float *w_router,
                             p.cap_groups == 0 && p.E <= kBlkCountMaxE;
   const TopkOut tk{p.k + p.expand_m, p.k, p.renorm_topk, C >= 0 ? 1 : 0, r.topk_ids, r.topk_w,
                    s.keys, blk_dispatch ? s.blk_cnt : nullptr};
-  bool topk_done = false, ex_done = false;
+  bool topk_done = false, ex_done = false, disp_done = false;
   int cnt_block = 0;
+  // token choice without a capacity limit: the dispatch outputs (final mode), which the router
+  // writes itself when one workgroup holds every token
+  BlkDispatchOut fin{};
+  if (blk_dispatch && C < 0) {
+    fin.counts = r.counts; fin.offsets = r.offsets; fin.perm_token = r.perm_token;
+    fin.perm_w = r.perm_w; fin.kept = r.kept; fin.tok_ptr = r.tok_ptr; fin.tok_pos = r.tok_pos;
+  }
   // expert choice: the router may also write the logits transposed (the selection's column
   // reads)
   const RouterExtra ex{(float *)s.colkeys};
   if (!(flags & MOE_ROUTE_LOGITS_IN)) {
     e = launch_router(p.dtype == MOE_BF16 ? 1 : 0, x, w_router, bias, r.logits, p.T, p.d_model,
                       p.E, s.w3, st, p.routing == MOE_TOKEN_CHOICE ? &tk : nullptr, &topk_done,
-                      &cnt_block, p.routing == MOE_EXPERT_CHOICE ? &ex : nullptr, &ex_done);
+                      &cnt_block, p.routing == MOE_EXPERT_CHOICE ? &ex : nullptr, &ex_done,
+                      blk_dispatch && C < 0 ? &fin : nullptr, &disp_done);
     if (e != hipSuccess) return e;
   }
   if (p.routing == MOE_TOKEN_CHOICE) {
@@ -309,10 +317,9 @@ hipError_t do_route(const moe_problem &p, const void *x, const float *w_router,
     if (blk_dispatch && cnt_block > 0) {
       BlkDispatchOut o{};
       if (C < 0) {   // every pair kept: the dispatch writes the token CSR as well
-        o.counts = r.counts; o.offsets = r.offsets; o.perm_token = r.perm_token;
-        o.perm_w = r.perm_w; o.kept = r.kept; o.tok_ptr = r.tok_ptr; o.tok_pos = r.tok_pos;
+        if (disp_done) return hipSuccess;   // the router did it
         return launch_dispatch_blocks(r.topk_ids, r.topk_w, p.T, p.k, p.E, s.blk_cnt, cnt_block,
-                                      o, st);
+                                      fin, st);
       }
       o.counts = s.cnt_pre; o.offsets = s.off_pre; o.perm_token = s.cand_token;
       o.perm_w = s.cand_w; o.keys = s.keys; o.cand_slot = s.cand_slot; o.cand_key = s.cand_key;

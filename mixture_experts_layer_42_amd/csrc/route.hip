@@ -552,9 +552,11 @@ constexpr int kNarrowTileBytes = kNarrowRows * kWtRowBytes;
 // pick order or the full softmax sum in butterfly order, and the routing keys of the capacity
 // forms (q_e = rexp_spec(l_e - max), S = q_0 + q_1 + ... left to right, key = q_e / S). Lane r
 // of the group keeps pick r and writes it. With cnt (LDS, one int per expert) every pick is
-// also counted there. Every lane of the group must call this (the butterflies use them all).
+// also counted there; with prow / grow (LDS rows of k entries) the picks and their gates are
+// also kept there. Every lane of the group must call this (the butterflies use them all).
 template <int G>
-MOE_DEV void topk_lanes(float lv, int gl, bool live, int t, int E, const TopkOut &o, int *cnt) {
+MOE_DEV void topk_lanes(float lv, int gl, bool live, int t, int E, const TopkOut &o, int *cnt,
+                        int *prow = nullptr, float *grow = nullptr) {
   const int lane = threadIdx.x & 63, g0 = lane - gl;   // first lane of this group
   bool taken = false;
   float mx = 0.f, qsum = 0.f, myq = 0.f;
@@ -585,6 +587,7 @@ MOE_DEV void topk_lanes(float lv, int gl, bool live, int t, int E, const TopkOut
   if (gl < o.k && live) {
     o.ids[(size_t)t * o.k + gl] = myid;
     o.gates[(size_t)t * o.k + gl] = myq / denom;
+    if (prow) { prow[gl] = myid; grow[gl] = myq / denom; }
   }
   if (o.want_key) {
     const float qv = gl < E ? rexp_spec(__fsub_rn(lv, mx)) : 0.f;
@@ -603,7 +606,8 @@ __global__ __launch_bounds__(64 * kNarrowWaves) void router_mfma_narrow_kernel(c
                                                                  int T, int d, int E,
                                                                  TopkOut topk,
                                                                  int32_t *__restrict__ blk_cnt,
-                                                                 RouterExtra ex) {
+                                                                 RouterExtra ex,
+                                                                 BlkDispatchOut disp) {
   constexpr int U = kNarrowRing;
   constexpr int TT = 16 * TB;   // tokens per workgroup
   constexpr int NW = kNarrowWaves, NT = 64 * NW;
@@ -761,18 +765,53 @@ __global__ __launch_bounds__(64 * kNarrowWaves) void router_mfma_narrow_kernel(c
   if (!topk.ids) return;   // block-uniform
   __syncthreads();
   int *cp = blk_cnt ? cnt : nullptr;
+  // picks and gates of the workgroup's tokens in LDS when it also does the dispatch
+  __shared__ int spick[16 * TB * kNarrowMaxE];
+  __shared__ float sgate[16 * TB * kNarrowMaxE];
+  const bool own = disp.perm_token != nullptr;   // grid-uniform
   if (E <= 8) {
     const int gi = threadIdx.x / 8, gl = threadIdx.x % 8;
     if (gi < TT)   // whole groups of 8 lanes
-      topk_lanes<8>(gl < E ? lg[gi * E + gl] : -INFINITY, gl, t0 + gi < T, t0 + gi, E, topk, cp);
+      topk_lanes<8>(gl < E ? lg[gi * E + gl] : -INFINITY, gl, t0 + gi < T, t0 + gi, E, topk, cp,
+                    own ? spick + gi * topk.k : nullptr, own ? sgate + gi * topk.k : nullptr);
   } else {
     const int gi = threadIdx.x / 16, gl = threadIdx.x % 16;
     if (gi < TT)
-      topk_lanes<16>(gl < E ? lg[gi * E + gl] : -INFINITY, gl, t0 + gi < T, t0 + gi, E, topk, cp);
+      topk_lanes<16>(gl < E ? lg[gi * E + gl] : -INFINITY, gl, t0 + gi < T, t0 + gi, E, topk, cp,
+                     own ? spick + gi * topk.k : nullptr, own ? sgate + gi * topk.k : nullptr);
   }
   if (!blk_cnt) return;
   __syncthreads();
   if (threadIdx.x < E) blk_cnt[(size_t)blockIdx.x * E + threadIdx.x] = cnt[threadIdx.x];
+  if (!own) return;
+  // The one workgroup holds every token (the launcher checks T <= its tokens): the dispatch of
+  // token choice without a capacity limit, as dispatch_blocks_kernel writes it: expert offsets
+  // from the counts, pair (t, j) of expert e at offsets[e] + (picks of e by tokens before t),
+  // token t owning CSR entries t k .. t k + k - 1.
+  __shared__ int soff[kNarrowMaxE];
+  if (threadIdx.x == 0) {
+    int run = 0;
+    for (int e = 0; e < E; ++e) {
+      soff[e] = run;
+      disp.counts[e] = cnt[e];
+      disp.offsets[e] = run;
+      run += cnt[e];
+    }
+    disp.offsets[E] = run;
+  }
+  __syncthreads();
+  const int K = topk.k;
+  for (int i = threadIdx.x; i < T * K; i += NT) {
+    const int t = i / K, e = spick[i];
+    int rank = 0;
+    for (int q = 0; q < t * K; ++q) rank += spick[q] == e;
+    const int pos = soff[e] + rank;
+    disp.perm_token[pos] = t;
+    disp.perm_w[pos] = sgate[i];
+    disp.tok_pos[i] = pos;
+    if (disp.kept) disp.kept[i] = 1;
+  }
+  for (int t = threadIdx.x; t <= T; t += NT) disp.tok_ptr[t] = t * K;
 }
 
 // ----------------------------------------------------------------------------------------
@@ -1928,21 +1967,29 @@ size_t router_w3_bytes(int dtype, int d, int E) {
 hipError_t launch_router(int dtype, const void *x, const float *w, const float *bias,
                          float *logits, int T, int d, int E, bf16_t *w3, hipStream_t st,
                          const TopkOut *topk, bool *topk_done, int *cnt_block,
-                         const RouterExtra *ex, bool *ex_done) {
+                         const RouterExtra *ex, bool *ex_done, const BlkDispatchOut *disp,
+                         bool *disp_done) {
   if (topk_done) *topk_done = false;
   if (cnt_block) *cnt_block = 0;
   if (ex_done) *ex_done = false;
+  if (disp_done) *disp_done = false;
   if (router_narrow_mfma(dtype, d, E)) {
     const TopkOut tk = topk ? *topk : TopkOut{0, 0, 0, 0, nullptr, nullptr, nullptr, nullptr};
     if (topk && topk_done) *topk_done = true;
     const RouterExtra rx = ex ? *ex : RouterExtra{nullptr};
     if (ex && ex_done) *ex_done = true;
+    // one workgroup for every token: it also writes the dispatch (final mode)
+    BlkDispatchOut dsp{};
+    if (disp && topk && tk.blk_cnt && T <= 16 && disp->perm_token && !disp->cand_slot) {
+      dsp = *disp;
+      if (disp_done) *disp_done = true;
+    }
     const int tb = T >= 16 * 2 * 256 ? 2 : 1;   // two token blocks per workgroup halve the W reads
     if (tk.blk_cnt && cnt_block) *cnt_block = 16 * tb;
 #define MOE_NARROW(TBB, NCHH) hipLaunchKernelGGL((router_mfma_narrow_kernel<TBB, NCHH>),          \
                                                dim3((T + 16 * TBB - 1) / (16 * TBB)), dim3(64 * kNarrowWaves), 0, \
                                                st, (const bf16_t *)x, w, bias, logits, T, d, E, tk, \
-                                               tk.blk_cnt, rx)
+                                               tk.blk_cnt, rx, dsp)
     if (tb == 2) { if (E <= 8) MOE_NARROW(2, 1); else MOE_NARROW(2, 2); }
     else { if (E <= 8) MOE_NARROW(1, 1); else MOE_NARROW(1, 2); }
 #undef MOE_NARROW
