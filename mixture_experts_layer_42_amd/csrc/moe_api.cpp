@@ -299,13 +299,14 @@ hipError_t do_route(const moe_problem &p, const void *x, const float *w_router,
     fin.counts = r.counts; fin.offsets = r.offsets; fin.perm_token = r.perm_token;
     fin.perm_w = r.perm_w; fin.kept = r.kept; fin.tok_ptr = r.tok_ptr; fin.tok_pos = r.tok_pos;
   }
-  // expert choice: the router may also write the logits transposed (the selection's column
-  // reads)
+  // expert choice with the register-held selection (at most 16384 tokens): the router may also
+  // write the logits transposed (the selection's column reads)
   const RouterExtra ex{(float *)s.colkeys};
+  const bool want_ex = p.routing == MOE_EXPERT_CHOICE && p.T <= 16384;
   if (!(flags & MOE_ROUTE_LOGITS_IN)) {
     e = launch_router(p.dtype == MOE_BF16 ? 1 : 0, x, w_router, bias, r.logits, p.T, p.d_model,
                       p.E, s.w3, st, p.routing == MOE_TOKEN_CHOICE ? &tk : nullptr, &topk_done,
-                      &cnt_block, p.routing == MOE_EXPERT_CHOICE ? &ex : nullptr, &ex_done,
+                      &cnt_block, want_ex ? &ex : nullptr, &ex_done,
                       blk_dispatch && C < 0 ? &fin : nullptr, &disp_done);
     if (e != hipSuccess) return e;
   }
