@@ -142,6 +142,13 @@ FUSED_TOPK = {
     "E10-drop-bf16": C0.with_(dtype="bf16", T=333, d_model=192, E=10, k=3, d_ff=128, gamma=0.9,
                               bias=("zipf", 1.2)),
     "E9-nodrop-bf16": C0.with_(dtype="bf16", T=50, d_model=64, E=9, k=9, d_ff=64),
+    # at most 16 tokens: the router's one workgroup also writes the dispatch (compared with the
+    # dispatch kernel run on the same logits)
+    "T16-E10-bf16": C0.with_(dtype="bf16", T=16, d_model=192, E=10, k=3, d_ff=64),
+    "T5-E9-k9-bf16": C0.with_(dtype="bf16", T=5, d_model=64, E=9, k=9, d_ff=64),
+    "T16-E8-k8-bf16": C0.with_(dtype="bf16", T=16, d_model=128, E=8, k=8, d_ff=64,
+                               bias=("normal", 0.5)),
+    "T17-E8-bf16": C0.with_(dtype="bf16", T=17, d_model=128, E=8, k=2, d_ff=64),
 }
 
 
