@@ -149,14 +149,22 @@ FUSED_TOPK = {
     "T16-E8-k8-bf16": C0.with_(dtype="bf16", T=16, d_model=128, E=8, k=8, d_ff=64,
                                bias=("normal", 0.5)),
     "T17-E8-bf16": C0.with_(dtype="bf16", T=17, d_model=128, E=8, k=2, d_ff=64),
+    # expert choice: the router also writes the logits transposed, which the selection then
+    # reads instead of the token-major logits
+    "EC-T300-E8-bf16": C0.with_(dtype="bf16", routing="expert", T=300, d_model=128, E=8, k=2,
+                                d_ff=64),
+    "EC-T2500-E10-bf16": C0.with_(dtype="bf16", routing="expert", T=2500, d_model=192, E=10,
+                                  k=3, d_ff=64),
 }
 
 
 @pytest.mark.parametrize("name", list(FUSED_TOPK))
 def test_fused_topk_equals_topk_kernel(name):
     """moe_route with the router computing logits (and, for these shapes, the top-k inside the
-    same kernel) against moe_route fed those very logits (the separate top-k kernel): every
-    routing array bit-identical; and the selection against the oracle on the same logits."""
+    same kernel, the dispatch too for at most 16 tokens, or for expert choice the transposed
+    logits the selection reads) against moe_route fed those very logits (the separate kernels):
+    every routing array bit-identical; and the selection against the oracle on the same
+    logits."""
     cfg = FUSED_TOPK[name]
     inp = inputs_for(cfg)
     dev = dev_weights(inp)
