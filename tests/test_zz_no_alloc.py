@@ -23,6 +23,8 @@ CASES = [
                                routing="expert"),
      dict(T=1000)),
     ("mixtral-shaped-no-drop", mi.MIXTRAL.with_(T=2048, d_ff=64), dict(T=33)),
+    # at most 16 tokens: the router's one workgroup also writes the dispatch
+    ("mixtral-shaped-decode", mi.MIXTRAL.with_(T=16, d_ff=64), dict(T=1)),
 ]
 
 
