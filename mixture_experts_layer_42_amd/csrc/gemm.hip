@@ -9,20 +9,23 @@
 // bf16 path: persistent workgroups walk a tile list built on the device from the
 // per-expert row counts (no host round trip). A tile is 256 rows x 256 columns (a group's
 // last row tile shrinks to 64, 128 or 192 rows when that covers its remaining rows); K goes in
-// slices of 64 through two 64 KB LDS stages (one lands while the other feeds the MFMAs).
+// slices of 64 through two 72 KB LDS stages (one lands while the other feeds the MFMAs; a
+// 256 x 256 tile uses 64 KB of each).
 // Waves (4 as 2 x 2 of 128 x 128, or 8 as 2 x 4 of 128 x 64) compute with
 // v_mfma_f32_32x32x16_bf16 into float32 accumulators. Slices are copied from global memory
 // straight into LDS (gfx950 buffer loads into LDS, no register staging); each 1 KB copy covers 8
 // rows x 128 B, i.e. whole 128-byte lines, which streams about twice as fast as half-line
 // rows. 16-byte chunks are XOR-swizzled by row so the MFMA fragment reads hit distinct banks.
-// Tiles of one expert that share a weight column are consecutive in the tile list, and
-// consecutive list entries are given to workgroups on the same XCD, so the weight slice is
-// fetched into that XCD's L2 once and reused by every row tile. For gate/up the B tile
+// Tiles of one expert go in bands of 4 weight panels, row tile by row tile inside a band, and
+// consecutive list entries are given to workgroups on the same XCD, so the 32 workgroups of an
+// XCD share a few weight panels and row tiles through its L2. A group's last row tile of at
+// most 64 rows may span two panels (64 x 512, "wide", the down GEMM's default). For gate/up the B tile
 // interleaves per wave column the gate rows and the matching up rows, so SiLU(gate) * up is
 // formed in registers and only h is written.
 //
 // float32 path (used when the problem dtype is float32): a plain LDS-tiled SIMT GEMM over
 // the same tile list.
+#include <cstdlib>
 #include <type_traits>
 
 #include "common.h"
@@ -62,9 +65,25 @@ MOE_DEV GroupDesc group_desc(const GemmArgs &a, int g) {
   return d;
 }
 
+// Row tiles of a group whose last row tile holds at most 64 rows may be laid out with "wide"
+// last tiles (bf16 path, see group_tile): the group then has fewer tiles.
+// (only when N is a whole number of column panels: the second panel of a pair then never
+// reaches past N)
+MOE_DEV bool group_wide(int rows, int mt, int N, int bnout) {
+  return rows > 0 && N % bnout == 0 && N / bnout >= 2 && rows - (mt - 1) * 256 <= 64;
+}
+
+// Tiles of a group of `rows` rows and N columns, tiles of TM rows x bnout columns.
+template <int TM>
+MOE_DEV int group_tiles(int rows, int N, int bnout, bool wide) {
+  const int mt = (rows + TM - 1) / TM, ncol = (N + bnout - 1) / bnout;
+  if (!wide || !group_wide(rows, mt, N, bnout)) return mt * ncol;
+  return (ncol / 2) * (2 * mt - 1) + (ncol & 1) * mt;
+}
+
 // tile prefix over groups in LDS: tstart[g] = first tile of group g, tstart[G] = total
 template <int BM, int BNOUT>
-MOE_DEV int build_tile_table(const GemmArgs &a, int *tstart, int *sm) {
+MOE_DEV int build_tile_table(const GemmArgs &a, int *tstart, int *sm, bool wide = false) {
   const int G = a.E + (a.s_rows > 0 ? 1 : 0);
   int run = 0;
   for (int c0 = 0; c0 < G; c0 += blockDim.x) {
@@ -72,7 +91,7 @@ MOE_DEV int build_tile_table(const GemmArgs &a, int *tstart, int *sm) {
     int nt = 0;
     if (g < G) {
       const GroupDesc d = group_desc(a, g);
-      nt = ((d.rows + BM - 1) / BM) * ((d.N + BNOUT - 1) / BNOUT);
+      nt = group_tiles<BM>(d.rows, d.N, BNOUT, wide);
     }
     int tot;
     const int ex = block_excl_scan(nt, sm, &tot);
@@ -181,8 +200,17 @@ MOE_DEV __amdgpu_buffer_rsrc_t operand_rsrc(const void *p) {
 }
 
 // The pipeline stages are separate LDS objects, so loads into one stage are never mistaken
-// for writes to the stage being read.
-struct Stage { char a[BM * kRowBytes]; char b[BN * kRowBytes]; };
+// for writes to the stage being read. A wide tile (kWideMB) puts its 64 A rows at the start of
+// the stage and its 512 B rows right after them (8 KB + 64 KB), hence the longer b.
+constexpr int kWideA = 64 * kRowBytes;
+struct Stage { char a[BM * kRowBytes]; char b[BN * kRowBytes + kWideA]; };
+static_assert(sizeof(Stage) == kWideA + 2 * BN * kRowBytes, "wide layout fills the stage");
+MOE_DEV const char *stage_b(const Stage &st, bool wide) {
+  return wide ? reinterpret_cast<const char *>(&st) + kWideA : st.b;
+}
+MOE_DEV char *stage_b(Stage &st, bool wide) {
+  return wide ? reinterpret_cast<char *>(&st) + kWideA : st.b;
+}
 
 // Row tiles. A group's rows go in tiles of 256; its last tile, holding rem = rows - m0 rows,
 // shrinks to 64 * MB rows with MB = 1 (rem <= 64), 2 (rem <= 128), 3 (rem <= 192) or 4, so a
@@ -190,11 +218,59 @@ struct Stage { char a[BM * kRowBytes]; char b[BN * kRowBytes]; };
 // of a tile owns rows wm * 32 MB .. + 32 MB - 1 as MB blocks of 32.
 MOE_DEV int tile_mb(int rem) { return rem > 192 ? 4 : (rem > 128 ? 3 : (rem > 64 ? 2 : 1)); }
 
+// Wide last row tiles. A 64-row tile costs a quarter of a full tile's MFMAs but, bound by the
+// latency of its copies landing, about 70% of its time. When a group's last row tile holds at
+// most 64 rows and the group has at least two column panels, its column panels go in pairs:
+// the full row tiles of panel 2q, those of panel 2q+1, then one 64-row tile spanning both
+// panels (512 B-columns, mb = kWideMB), which reads its rows once for the pair and keeps the
+// MFMAs of 8 waves busy with 64 x 64 each; an odd last panel keeps its own row tiles. The
+// rows that share a weight panel stay next to each other in the list.
+constexpr int kWideMB = 5;
+struct TileLoc { int n_tile, m0, mb; };   // n_tile: first column panel of the tile
+
+MOE_DEV TileLoc group_tile(int rows, int N, int bnout, bool wide, int local, int band = 1) {
+  const int mt = (rows + BM - 1) / BM, ncol = (N + bnout - 1) / bnout;
+  TileLoc t;
+  if (!wide || !group_wide(rows, mt, N, bnout)) {
+    if (band > 1 && mt > 1) {
+      // bands of `band` panels; inside a band row tile by row tile, its panels in order
+      const int b = local / (mt * band), in = local % (mt * band);
+      const int w = min(band, ncol - b * band);
+      t.n_tile = b * band + in % w;
+      t.m0 = (in / w) * BM;
+    } else {
+      t.n_tile = local / mt;
+      t.m0 = (local % mt) * BM;
+    }
+    t.mb = tile_mb(rows - t.m0);
+    return t;
+  }
+  const int mf = mt - 1, per = 2 * mf + 1, paired = (ncol / 2) * per;
+  if (local < paired) {
+    const int q = local / per, r = local % per;
+    if (r < 2 * mf) {
+      t.n_tile = 2 * q + r / mf;
+      t.m0 = (r % mf) * BM;
+      t.mb = 4;
+    } else {
+      t.n_tile = 2 * q;
+      t.m0 = mf * BM;
+      t.mb = kWideMB;
+    }
+  } else {
+    t.n_tile = ncol - 1;
+    t.m0 = (local - paired) * BM;
+    t.mb = tile_mb(rows - t.m0);
+  }
+  return t;
+}
+
 // fragments of sub-step ks (k = 16 ks .. 16 ks + 15 of the slice)
-template <int W, int MB>
+template <int W, int MB, bool WIDE>
 MOE_DEV void load_frags(const Stage &st, int lane, int wm, int wn, int ks, bf16x8_t (&af)[MB],
                         bf16x8_t (&bfr)[Cfg<W>::NB]) {
   const int chunk = ks * 2 + (lane >> 5);
+  const char *sb = stage_b(st, WIDE);
   // in the order the MFMAs (mb outer, nb inner) consume them: A0, every B, then A1 ..
   // so that the first MFMAs of the sub-step wait only for the reads issued first
 #pragma unroll
@@ -204,7 +280,7 @@ MOE_DEV void load_frags(const Stage &st, int lane, int wm, int wn, int ks, bf16x
 #pragma unroll
       for (int nb = 0; nb < Cfg<W>::NB; ++nb)
         bfr[nb] = *reinterpret_cast<const bf16x8_t *>(
-            st.b + swz(wn * Cfg<W>::WCOLS + nb * 32 + (lane & 31), chunk));
+            sb + swz(wn * Cfg<W>::WCOLS + nb * 32 + (lane & 31), chunk));
     }
   }
 }
@@ -299,7 +375,8 @@ MOE_DEV void make_uniform(Unit &x) {
   x.punit = uni(x.punit); x.mb = uni(x.mb);
 }
 
-// Per-lane byte offsets of a unit's copies from the slice bases (A: MB used, B: B_DMA used).
+// Per-lane byte offsets of a unit's copies from the slice bases (A: A_DMA used, B: B_DMA
+// used; a wide tile copies its second 256 B rows from the same offsets plus one panel).
 struct Offs { uint32_t a[4], b[4]; };
 
 // Loader: wave wv fills A rows wv*TBM/W .. and B rows wv*BN/W .. with copies of 1 KB (8 rows of
@@ -307,12 +384,13 @@ struct Offs { uint32_t a[4], b[4]; };
 // (L%8) ^ ((row/2)%8). For gate/up the B tile holds, per wave column wn, WCOLS/2 gate rows then
 // the matching WCOLS/2 up rows (h columns n_tile*128 + wn*WCOLS/2 + j), so the B rows a wave
 // loads are all gate (wv even) or all up (wv odd).
-template <bool GATE_UP, int W, int MB>
+template <bool GATE_UP, int W, int MB, bool WIDE>
 MOE_DEV void unit_offsets(const Unit &x, Offs &o) {
   using C = Cfg<W>;
-  static_assert(MB <= 4 && C::B_DMA <= 4, "Offs holds 4 + 4 offsets");
-  constexpr int TBM = 64 * MB;
+  constexpr int TBM = WIDE ? 64 : 64 * MB;          // tile rows
   constexpr int A_DMA = TBM * kRowBytes / 1024 / W;
+  static_assert(A_DMA <= 4 && C::B_DMA <= 4, "Offs holds 4 + 4 offsets");
+  static_assert(!WIDE || (W == 8 && MB == 2), "a wide tile is 64 rows of 8 waves of 64 x 64");
   const int lane = threadIdx.x & 63;
   const int wvu = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
 #pragma unroll
@@ -334,31 +412,45 @@ MOE_DEV void unit_offsets(const Unit &x, Offs &o) {
   }
 }
 
-// Copies of K-slice kt of unit x into stage s.
-template <bool GATE_UP, int W, int MB>
+// Copies of K-slice kt of unit x into stage s. The B rows a wave copies are all gate rows (even
+// wave) or all up rows (odd wave). A wide tile copies B-tile rows 256 + r from weight rows one
+// panel further (BN/2 rows for gate/up, BN for down) than those of row r, through the scalar
+// offset (the pair never reaches past N, see group_wide).
+template <bool GATE_UP, int W, int MB, bool WIDE>
 MOE_DEV void unit_issue(const Unit &x, const Offs &o, Stage &s, int kt) {
   using C = Cfg<W>;
-  constexpr int A_DMA = 64 * MB * kRowBytes / 1024 / W;
+  constexpr int A_DMA = (WIDE ? 64 : 64 * MB) * kRowBytes / 1024 / W;
   const int wvu = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
   const char *Ab = (const char *)x.d.A;
   const char *Bb = (const char *)((GATE_UP && (wvu & 1)) ? x.d.B1 : x.d.B0);
   const __amdgpu_buffer_rsrc_t ra = operand_rsrc(Ab), rb = operand_rsrc(Bb);
   const int aofs = wvu * A_DMA * 1024, bofs = wvu * C::B_DMA * 1024;
+  char *sb = stage_b(s, WIDE);
   const int so = (x.k_begin + kt) * kRowBytes;   // K offset of the slice, bytes
 #pragma unroll
   for (int i = 0; i < A_DMA; ++i) b2lds16(ra, o.a[i], so, s.a + aofs + i * 1024);
 #pragma unroll
-  for (int i = 0; i < C::B_DMA; ++i) b2lds16(rb, o.b[i], so, s.b + bofs + i * 1024);
+  for (int i = 0; i < C::B_DMA; ++i) b2lds16(rb, o.b[i], so, sb + bofs + i * 1024);
+  if constexpr (WIDE) {
+    const int so2 = so + (GATE_UP ? BN / 2 : BN) * x.d.K * 2;
+#pragma unroll
+    for (int i = 0; i < C::B_DMA; ++i) b2lds16(rb, o.b[i], so2, sb + BN * kRowBytes + bofs + i * 1024);
+  }
 }
 
 // The offsets of unit x and the copies of its first slice into st0.
 template <bool GATE_UP, int W>
 MOE_DEV void unit_prefetch(const Unit &x, Offs &o, Stage &st0) {
   switch (x.mb) {
-    case 4: unit_offsets<GATE_UP, W, 4>(x, o); unit_issue<GATE_UP, W, 4>(x, o, st0, 0); break;
-    case 3: unit_offsets<GATE_UP, W, 3>(x, o); unit_issue<GATE_UP, W, 3>(x, o, st0, 0); break;
-    case 2: unit_offsets<GATE_UP, W, 2>(x, o); unit_issue<GATE_UP, W, 2>(x, o, st0, 0); break;
-    default: unit_offsets<GATE_UP, W, 1>(x, o); unit_issue<GATE_UP, W, 1>(x, o, st0, 0); break;
+    case 4: unit_offsets<GATE_UP, W, 4, false>(x, o); unit_issue<GATE_UP, W, 4, false>(x, o, st0, 0); break;
+    case 3: unit_offsets<GATE_UP, W, 3, false>(x, o); unit_issue<GATE_UP, W, 3, false>(x, o, st0, 0); break;
+    case 2: unit_offsets<GATE_UP, W, 2, false>(x, o); unit_issue<GATE_UP, W, 2, false>(x, o, st0, 0); break;
+    case kWideMB:
+      if constexpr (W == 8) {
+        unit_offsets<GATE_UP, W, 2, true>(x, o); unit_issue<GATE_UP, W, 2, true>(x, o, st0, 0);
+      }
+      break;
+    default: unit_offsets<GATE_UP, W, 1, false>(x, o); unit_issue<GATE_UP, W, 1, false>(x, o, st0, 0); break;
   }
 }
 
@@ -368,23 +460,24 @@ MOE_DEV void unit_prefetch(const Unit &x, Offs &o, Stage &st0) {
 // operations complete in issue order, so the copies have landed and only stores remain. After
 // the K loop the next unit's first slice is issued before this unit's epilogue, so its copies
 // travel while the outputs are stored. Returns whether this wave's epilogue left stores in
-// flight.
-template <bool GATE_UP, int W, int MB>
+// flight. A wide tile (WIDE, MB = 2) is 64 rows x 512 B-columns: one wave row, wave wv owns
+// all 64 rows of B-columns wv*64 .. +63, the same 2 x 2 blocks as a wave of a 128-row tile.
+template <bool GATE_UP, int W, int MB, bool WIDE>
 MOE_DEV __attribute__((always_inline)) bool gemm_tile(const GemmArgs &args, const Unit &x,
                                                       const Offs &o, Stage &st0, Stage &st1,
                                                       bool stores_pending, bool has_next,
                                                       const Unit &nx, Offs &no) {
   using C = Cfg<W>;
   constexpr int NB = C::NB;
-  constexpr int TBM = 64 * MB;                    // tile rows
+  constexpr int TBM = WIDE ? 64 : 64 * MB;        // tile rows
   constexpr int A_DMA = TBM * kRowBytes / 1024 / W;   // A copies per wave per slice
-  constexpr int DMA = A_DMA + C::B_DMA;
+  constexpr int DMA = A_DMA + (WIDE ? 2 : 1) * C::B_DMA;
   constexpr int BNOUT = GATE_UP ? BN / 2 : BN;
   const GroupDesc &d = x.d;
   const int n_tile = x.n_tile, m0 = x.m0, nk = x.nk, punit = x.punit;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int wm = wv / C::WN, wn = wv % C::WN;
-  auto issue = [&](Stage &s, int kt) { unit_issue<GATE_UP, W, MB>(x, o, s, kt); };
+  const int wm = WIDE ? 0 : wv / C::WN, wn = WIDE ? __builtin_amdgcn_readfirstlane(wv) : wv % C::WN;
+  auto issue = [&](Stage &s, int kt) { unit_issue<GATE_UP, W, MB, WIDE>(x, o, s, kt); };
   f32x16_t acc[MB][NB];
 #pragma unroll
   for (int i = 0; i < MB; ++i)
@@ -409,7 +502,7 @@ MOE_DEV __attribute__((always_inline)) bool gemm_tile(const GemmArgs &args, cons
   // MFMAs of (fa, fb) with the fragment reads of the next sub-step between them
   auto sub = [&](const bf16x8_t (&fa)[MB], const bf16x8_t (&fb)[NB], const Stage &cur, int ks,
                  bf16x8_t (&na)[MB], bf16x8_t (&nb)[NB]) {
-    load_frags<W, MB>(cur, lane, wm, wn, ks, na, nb);
+    load_frags<W, MB, WIDE>(cur, lane, wm, wn, ks, na, nb);
     mfma_block<W, MB>(fa, fb, acc);
     sched_sub<MB * NB, 0, MB + NB>();
     sched_fence();
@@ -419,7 +512,7 @@ MOE_DEV __attribute__((always_inline)) bool gemm_tile(const GemmArgs &args, cons
     wait_and_barrier<decltype(vm)::value>();   // slice kt has landed
     sched_fence();
     issue(refill, min(kt + 1, nk - 1));   // past the end: re-read the last slice
-    load_frags<W, MB>(cur, lane, wm, wn, 0, fa0, fb0);
+    load_frags<W, MB, WIDE>(cur, lane, wm, wn, 0, fa0, fb0);
     mfma_block<W, MB>(fa1, fb1, acc);      // last sub-step of slice kt-1
     sched_sub<MB * NB, DMA, MB + NB>();    // copies and reads between the MFMAs
     sched_fence();
@@ -509,7 +602,8 @@ __global__ __launch_bounds__(64 * W, 1) void gemm_bf16_kernel(GemmArgs args) {
   __shared__ int tstart[kMaxGroups + 1];
   __shared__ int sm[kMaxWaves + 1];
   constexpr int BNOUT = GATE_UP ? BN / 2 : BN;   // output columns per tile (h or o)
-  const int G = build_tile_table<BM, BNOUT>(args, tstart, sm);
+  const bool wide = W == 8 && args.wide;
+  const int G = build_tile_table<BM, BNOUT>(args, tstart, sm, wide);
   const int total = tstart[G];
 
   const SplitPlan sp = split_plan(total, kMaxPersistent, args.K / BK, args.split_ok);
@@ -525,15 +619,14 @@ __global__ __launch_bounds__(64 * W, 1) void gemm_bf16_kernel(GemmArgs args) {
     }
     const int g = find_group(tstart, G, tile);
     x.d = group_desc(args, g);
-    const int local = tile - tstart[g];
-    const int mt = (x.d.rows + BM - 1) / BM;
-    x.n_tile = local / mt;
-    x.m0 = (local % mt) * BM;
+    const TileLoc tl = group_tile(x.d.rows, x.d.N, BNOUT, wide, tile - tstart[g], args.band);
+    x.n_tile = tl.n_tile;
+    x.m0 = tl.m0;
+    x.mb = tl.mb;
     const int nk_all = x.d.K / BK;
     x.k_begin = part * nk_all / nparts;                  // first K-step of this unit
     x.nk = (part + 1) * nk_all / nparts - x.k_begin;     // K-steps of this unit
     x.punit = nparts > 1 ? u - sp.full : -1;
-    x.mb = tile_mb(x.d.rows - x.m0);
     make_uniform(x);
     return x;
   };
@@ -548,10 +641,14 @@ __global__ __launch_bounds__(64 * W, 1) void gemm_bf16_kernel(GemmArgs args) {
     const Unit nx = has_next ? unit_at(u + gridDim.x) : cur;
     Offs no = co;
     switch (cur.mb) {
-      case 4: pending = gemm_tile<GATE_UP, W, 4>(args, cur, co, st0, st1, pending, has_next, nx, no); break;
-      case 3: pending = gemm_tile<GATE_UP, W, 3>(args, cur, co, st0, st1, pending, has_next, nx, no); break;
-      case 2: pending = gemm_tile<GATE_UP, W, 2>(args, cur, co, st0, st1, pending, has_next, nx, no); break;
-      default: pending = gemm_tile<GATE_UP, W, 1>(args, cur, co, st0, st1, pending, has_next, nx, no); break;
+      case 4: pending = gemm_tile<GATE_UP, W, 4, false>(args, cur, co, st0, st1, pending, has_next, nx, no); break;
+      case 3: pending = gemm_tile<GATE_UP, W, 3, false>(args, cur, co, st0, st1, pending, has_next, nx, no); break;
+      case 2: pending = gemm_tile<GATE_UP, W, 2, false>(args, cur, co, st0, st1, pending, has_next, nx, no); break;
+      case kWideMB:
+        if constexpr (W == 8)
+          pending = gemm_tile<GATE_UP, W, 2, true>(args, cur, co, st0, st1, pending, has_next, nx, no);
+        break;
+      default: pending = gemm_tile<GATE_UP, W, 1, false>(args, cur, co, st0, st1, pending, has_next, nx, no); break;
     }
     cur = nx;
     make_uniform(cur);
@@ -574,23 +671,28 @@ __global__ __launch_bounds__(256) void gemm_tail_reduce_kernel(GemmArgs args) {
   constexpr int PART = BM * BN;         // floats per partial tile
   __shared__ int tstart[kMaxGroups + 1];
   __shared__ int sm[kMaxWaves + 1];
-  const int G = build_tile_table<BM, BNOUT>(args, tstart, sm);
+  const bool wide = W == 8 && args.wide;
+  const int G = build_tile_table<BM, BNOUT>(args, tstart, sm, wide);
   const SplitPlan sp = split_plan(tstart[G], kMaxPersistent, args.K / BK, args.split_ok);
   const int items = sp.L * (BM / kReduceRows);
   for (int it = blockIdx.x; it < items; it += gridDim.x) {
-    const int l = it / (BM / kReduceRows), r0 = (it % (BM / kReduceRows)) * kReduceRows;
+    const int l = it / (BM / kReduceRows), ri = it % (BM / kReduceRows);
     const int tile = sp.full + l;
     const int g = find_group(tstart, G, tile);
     const GroupDesc d = group_desc(args, g);
-    const int local = tile - tstart[g];
-    const int mt = (d.rows + BM - 1) / BM;
-    const int n_tile = local / mt, m_tile = local % mt;
-    const int MB = tile_mb(d.rows - m_tile * BM);      // the unit's row-tile height / 64
-    const int c = (threadIdx.x % TPR) * 4;             // first of 4 output columns in the tile
-    const int col = n_tile * BNOUT + c;
+    const TileLoc tl = group_tile(d.rows, d.N, BNOUT, wide, tile - tstart[g], args.band);
+    // item ri: rows ri*32 .. of the tile; of a wide tile (64 rows, two column panels) rows
+    // (ri % 2)*32 .. of panel ri / 2 (items 4..7 have nothing to do)
+    const bool wt = tl.mb == kWideMB;
+    if (wt && ri >= 4) continue;
+    const int r0 = (wt ? ri & 1 : ri) * kReduceRows;
+    const int ch = wt ? ri >> 1 : 0;                   // column panel within the tile
+    const int MB = wt ? 2 : tl.mb;                     // rows per wave row / 32 in the layout
+    const int c = ch * BNOUT + (threadIdx.x % TPR) * 4;   // first of 4 output columns in the tile
+    const int col = tl.n_tile * BNOUT + c;
     if (col >= d.N) continue;                         // N is a multiple of 64: whole groups of 4
     for (int rr = threadIdx.x / TPR; rr < kReduceRows; rr += RPP) {
-      const int tr = r0 + rr, row = m_tile * BM + tr;
+      const int tr = r0 + rr, row = tl.m0 + tr;
       if (row >= d.rows) break;
       const float *P0 = args.partials + (size_t)l * sp.S * PART + part_index<W>(tr, 0, MB);
       if (GATE_UP) {
@@ -1061,6 +1163,26 @@ hipError_t launch_bf16(const GemmArgs &a0, bool gate_up, int max_rows, int num_c
   if (grid > cap) grid = cap;
   if (grid < 1) grid = 1;
   a.grid = grid;
+  // Wide last row tiles (group_tile) for the down GEMM. Measured on one box, same-run A/B: the
+  // down GEMM's 64-row tiles (K = d_ff, 224 slices on the Mixtral-shaped layer) wait on their
+  // copies most of the time, and pairing them took that GEMM from 875 to 848 us (fine-grained
+  // 362 -> 357 us); the gate/up GEMM, whose L2 misses already stream near the fabric's rate,
+  // gained nothing (1619 -> 1626 us; capacity drop -2%, fine-grained +3%). MOE_GEMM_WIDE (read
+  // at every call) = 0 turns them off, = all uses them in both GEMMs. The output is the same bit
+  // for bit in every case: each output element sums its K products in the same MFMA order
+  // whatever tile holds it.
+  const char *wenv = std::getenv("MOE_GEMM_WIDE");
+  const bool w_off = wenv && wenv[0] == '0', w_all = wenv && wenv[0] == 'a';
+  a.wide = (W == 8 && !w_off && (!gate_up || w_all)) ? 1 : 0;
+  // Tile order inside a group: column panels in bands of 4, row tile by row tile within a band
+  // (group_tile), so the 32 workgroups of an XCD, which take 32 consecutive tiles, share about 4
+  // weight panels and 8 row tiles instead of 2-3 panels and up to 13 row tiles. Same-run A/B on
+  // the Mixtral-shaped layer: gate/up 1643 -> 1618 us with bands of 4 (2: 1620, 6: 1632, 8: 1623);
+  // fine-grained 492 -> 489 us, capacity drop unchanged, the down GEMM unchanged.
+  // MOE_GEMM_BAND (read at every call) sets another band width (1: panel by panel). The order
+  // changes no sum.
+  const char *benv = std::getenv("MOE_GEMM_BAND");
+  a.band = benv && *benv ? std::atoi(benv) : 4;
   if (!a.partials) a.split_ok = 0;
   // at most kMaxPersistent/2 split tiles, BM/kReduceRows reduction items each
   int rgrid = kMaxPersistent * (BM / kReduceRows) / 2 + 1;

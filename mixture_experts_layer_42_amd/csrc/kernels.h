@@ -44,6 +44,10 @@ struct GemmArgs {
   float *partials;
   int split_ok;
   int grid;                         // persistent grid size (set by the launcher)
+  int wide;                         // bf16 tiles: a group's last row tile of at most 64 rows
+                                    // spans two column panels (set by the launcher)
+  int band;                         // bf16 tile order: column panels in bands of `band`, row
+                                    // tile by row tile inside a band (<= 1: panel by panel)
   // few rows per group (decode-shaped batches): every group holds at most max_group_rows
   // rows; when that is <= kSkinnyRows a 32/64-row tile streams the weights once, its K range
   // cut into sk_S parts whose float32 sums (rows of sk_pitch floats, routed rows first, then

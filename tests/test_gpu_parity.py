@@ -402,6 +402,50 @@ def test_deterministic_across_launch_shapes(name, monkeypatch):
             assert (_bits(np.asarray(h[k])) == _bits(np.asarray(v))).all(), (k, cus)
 
 
+# groups whose last row tile holds at most 64 rows: the grouped GEMMs run that tile across two
+# column panels (64 x 512 B-columns); routing collapse puts such tiles into the K-split tail,
+# and an odd panel count leaves one panel with its own 64-row tile
+WIDE_CASES = {
+    "collapse-ksplit-bf16": SMALL["collapse-ksplit-bf16"].with_(y_dtype="f32"),
+    "wide-even-panels-bf16": C0.with_(dtype="bf16", y_dtype="f32", T=1536, d_model=1024, E=8,
+                                      k=2, d_ff=1024, bias=("normal", 0.5)),
+    "wide-odd-panels-bf16": C0.with_(dtype="bf16", y_dtype="f32", T=1536, d_model=768, E=8,
+                                     k=2, d_ff=384, bias=("normal", 0.5)),
+}
+
+
+@pytest.mark.parametrize("name", list(WIDE_CASES))
+def test_wide_last_row_tiles(name, monkeypatch):
+    """The grouped GEMMs without wide last row tiles (MOE_GEMM_WIDE=0), with them in the down
+    GEMM (the default), in both GEMMs (MOE_GEMM_WIDE=all), and with panel-by-panel instead of
+    banded tile order (MOE_GEMM_BAND=1) give the same float32 output bit for bit (every output
+    element sums its K products in the same MFMA order whatever tile holds it and whenever it
+    runs), and that output meets the bar against the oracle."""
+    import torch
+    cfg = WIDE_CASES[name]
+    inp = inputs_for(cfg)
+    dev = dev_weights(inp)
+    y_ref, ro = oracle.layer_forward(inp)
+    counts = ro["counts"]
+    short = [int(e) for e in range(cfg.E) if 0 < counts[e] % 256 <= 64]
+    say(f"[wide] {name}: rows per expert {counts.tolist()}, last tile <= 64 rows: {short}")
+    assert short, "no group ends in a 64-row tile: the case would not exercise wide tiles"
+    monkeypatch.setenv("MOE_GEMM_WIDE", "0")
+    y0, _ = run_layer(cfg, dev)
+    monkeypatch.setenv("MOE_GEMM_WIDE", "all")
+    y2, _ = run_layer(cfg, dev)
+    monkeypatch.setenv("MOE_GEMM_BAND", "1")   # the other tile order as well
+    y3, _ = run_layer(cfg, dev)
+    monkeypatch.delenv("MOE_GEMM_BAND")
+    monkeypatch.delenv("MOE_GEMM_WIDE")
+    y1, rb = run_layer(cfg, dev)
+    assert torch.equal(_bits_t(y0), _bits_t(y1)), "wide tiles in the down GEMM changed the output"
+    assert torch.equal(_bits_t(y0), _bits_t(y2)), "wide tiles in both GEMMs changed the output"
+    assert torch.equal(_bits_t(y0), _bits_t(y3)), "banded tile order changed the output"
+    _compare_routing(cfg, rb, ro)
+    check_y(cfg, host_f32(y1), y_ref)
+
+
 def _bits_t(t):
     import torch
     return t.contiguous().view(torch.int16 if t.element_size() == 2 else torch.int32)
