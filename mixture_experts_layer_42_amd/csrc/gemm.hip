@@ -1174,6 +1174,10 @@ hipError_t launch_bf16(const GemmArgs &a0, bool gate_up, int max_rows, int num_c
   const char *wenv = std::getenv("MOE_GEMM_WIDE");
   const bool w_off = wenv && wenv[0] == '0', w_all = wenv && wenv[0] == 'a';
   a.wide = (W == 8 && !w_off && (!gate_up || w_all)) ? 1 : 0;
+  // a wide tile's second-half copies add one panel (at most 256 rows of K elements) to the
+  // slice's scalar byte offset, which must stay below 2^31
+  const long long kmax = a.s_rows > 0 && a.sK > a.K ? a.sK : a.K;
+  if (kmax * (2LL * BN + 2) * 2 >= (1LL << 31)) a.wide = 0;
   // Tile order inside a group: column panels in bands of 4, row tile by row tile within a band
   // (group_tile), so the 32 workgroups of an XCD, which take 32 consecutive tiles, share about 4
   // weight panels and 8 row tiles instead of 2-3 panels and up to 13 row tiles. Same-run A/B on
