@@ -631,7 +631,8 @@ def _random_problem(seed):
     k = int(r.integers(1, min(E, 8) + 1))
     T = int(r.choice([1, 2, 7, 31, 64, 65, 129, 256, 257, 333, 600]))
     kw = dict(dtype="bf16" if bf16 else "f32", T=T, E=E, k=k,
-              d_model=int(r.choice([64, 128, 192, 256])), d_ff=int(r.choice([64, 128, 192, 320])),
+              d_model=int(r.choice([64, 128, 192, 256, 512])),
+              d_ff=int(r.choice([64, 128, 192, 256, 320, 384])),
               d_ff_shared=int(r.choice([0, 0, 64])), renorm_topk=bool(r.random() < 0.8),
               bias=[("none",), ("normal", 1.0), ("zipf", 1.2)][int(r.integers(0, 3))], seed=seed)
     form = r.random()
