@@ -65,10 +65,9 @@ MOE_DEV GroupDesc group_desc(const GemmArgs &a, int g) {
   return d;
 }
 
-// Row tiles of a group whose last row tile holds at most 64 rows may be laid out with "wide"
-// last tiles (bf16 path, see group_tile): the group then has fewer tiles.
-// (only when N is a whole number of column panels: the second panel of a pair then never
-// reaches past N)
+// Whether a group of `rows` rows (mt row tiles of 256) takes wide last row tiles (bf16 path,
+// see group_tile): its last row tile holds at most 64 rows and N is a whole number of at least
+// two column panels of bnout columns, so the second panel of a pair never reaches past N.
 MOE_DEV bool group_wide(int rows, int mt, int N, int bnout) {
   return rows > 0 && N % bnout == 0 && N / bnout >= 2 && rows - (mt - 1) * 256 <= 64;
 }
@@ -224,7 +223,9 @@ MOE_DEV int tile_mb(int rem) { return rem > 192 ? 4 : (rem > 128 ? 3 : (rem > 64
 // the full row tiles of panel 2q, those of panel 2q+1, then one 64-row tile spanning both
 // panels (512 B-columns, mb = kWideMB), which reads its rows once for the pair and keeps the
 // MFMAs of 8 waves busy with 64 x 64 each; an odd last panel keeps its own row tiles. The
-// rows that share a weight panel stay next to each other in the list.
+// tiles that share a weight panel stay next to each other in the list. Groups without wide
+// tiles go in bands of `band` panels, row tile by row tile inside a band (each row tile's
+// panels of the band in order); band <= 1 or a single row tile: panel by panel.
 constexpr int kWideMB = 5;
 struct TileLoc { int n_tile, m0, mb; };   // n_tile: first column panel of the tile
 
