@@ -31,6 +31,20 @@ PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 PEAK_F32_TFLOPS = 157.3        # MI355X float32 vector: 256 CUs x 128 FMA lanes x 2 flop x 2.4 GHz
 
+# The pages' own figures, reported beside the measurements as context (they are whole-model
+# figures on hardware the pages do not state, so no vs_baseline is derived from them):
+# hrletsgo page "MoE vs MoT routing inference cost", basic-structure and measured-figures
+# sections (Mixtral 8x7B sizes and FP16 serving memory); gist.science summary of
+# "Capacity-Aware Inference", Results section (speed-ups of the two drop variants).
+PAGES_CONTEXT = {
+    "mixtral_8x7b_params_total_billion": 46.7,
+    "mixtral_8x7b_params_active_billion": 12.9,
+    "mixtral_8x7b_fp16_serving_gb": 90,
+    "capacity_aware_token_drop_speedup": 1.3,
+    "capacity_aware_expanded_drop_speedup_max": 1.85,
+    "note": "whole-model figures from the pages, hardware not stated: context, not targets",
+}
+
 
 def parse():
     ap = argparse.ArgumentParser()
@@ -452,6 +466,7 @@ def main():
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline: oracle on a token sample", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(inp, args.cpu_sample)
+    out["pages_context"] = PAGES_CONTEXT
     print(json.dumps(out), flush=True)
 
 
