@@ -740,9 +740,11 @@ __global__ __launch_bounds__(256) void gemm_tail_reduce_kernel(GemmArgs args) {
 }
 
 // ----------------------------------------------------------------------------------------
-// Skinny path: groups of at most 64 rows (decode-shaped batches). Every weight element is
-// read once, so the GEMM is bound by streaming the weights from HBM; a 256-row tile would
-// spend its MFMAs on padding. A unit is 32*MB rows x 256 B-columns x one K part of a group;
+// Skinny path: groups of at most 128 rows (decode-shaped and small batches). Every weight
+// element is read once, so the GEMM is bound by streaming the weights from HBM; a 256-row tile
+// would spend its MFMAs on padding, and its two LDS stages cannot cover the HBM latency of the
+// weight slices once no other tile shares them in L2. A unit is 32*MB rows (MB = 1, 2 or 4:
+// stages of 40, 40 or 48 KB) x 256 B-columns x one K part of a group;
 // 4 waves own 64 B-columns each (for gate/up 32 gate and the matching 32 up columns), K in
 // slices of 64 through three LDS stages. K is cut into S parts only as far as the rule in
 // skinny_plan asks (about one or two units per CU: longer units keep the copy pipeline full,
@@ -753,8 +755,13 @@ constexpr int kSkinnyMaxParts = 16;
 
 SkinnyPlan skinny_plan(const GemmArgs &a, bool gate_up) {
   SkinnyPlan sp{0, 1, 0, 0, 0};
-  if (a.elt != 2 || a.max_group_rows > kSkinnyRows) return sp;
-  sp.mb = a.max_group_rows <= 32 ? 1 : 2;
+  // Groups of 65-128 rows (Mixtral-shaped weights, T = 96 and 128, same box, old and new library
+  // in turn): the down GEMM on 128-row units streamed its weights at 70-71% of HBM against 37%
+  // with 128-row regular tiles (324 -> 166-170 us, layer -15%), while the gate/up GEMM, whose
+  // regular tiles already reach 61-63%, fell to 58-60% (386 -> 400 us): it keeps the regular
+  // tiles above 64 rows.
+  if (a.elt != 2 || a.max_group_rows > (gate_up ? kSkinnyRowsGateUp : kSkinnyRows)) return sp;
+  sp.mb = a.max_group_rows <= 32 ? 1 : (a.max_group_rows <= 64 ? 2 : 4);
   const int bno = gate_up ? BN / 2 : BN;   // output columns per unit
   sp.nt = (a.N + bno - 1) / bno;
   sp.snt = a.s_rows > 0 ? (a.sN + bno - 1) / bno : 0;
@@ -1218,13 +1225,17 @@ hipError_t launch_skinny(const GemmArgs &a0, bool gate_up, const SkinnyPlan &sp,
   if (gate_up) {
     if (sp.mb == 1)
       hipLaunchKernelGGL((gemm_skinny_kernel<true, 1>), dim3(grid), dim3(256), 0, st, a);
-    else
+    else if (sp.mb == 2)
       hipLaunchKernelGGL((gemm_skinny_kernel<true, 2>), dim3(grid), dim3(256), 0, st, a);
+    else
+      hipLaunchKernelGGL((gemm_skinny_kernel<true, 4>), dim3(grid), dim3(256), 0, st, a);
   } else {
     if (sp.mb == 1)
       hipLaunchKernelGGL((gemm_skinny_kernel<false, 1>), dim3(grid), dim3(256), 0, st, a);
-    else
+    else if (sp.mb == 2)
       hipLaunchKernelGGL((gemm_skinny_kernel<false, 2>), dim3(grid), dim3(256), 0, st, a);
+    else
+      hipLaunchKernelGGL((gemm_skinny_kernel<false, 4>), dim3(grid), dim3(256), 0, st, a);
   }
   if (sp.S > 1 && !defer_reduce) {
     const long items = (long)(a.rcap + a.s_rows) * (gate_up ? sp.pitch / 2 : sp.pitch) / 4;

@@ -58,6 +58,9 @@ SMALL = {
     "decode-T48-shared-bf16": C0.with_(dtype="bf16", T=48, d_model=256, E=16, k=1, d_ff=512,
                                        d_ff_shared=256, gamma=1.0, bias=("zipf", 1.2)),
     "decode-T1-E64-bf16": C0.with_(dtype="bf16", T=1, d_model=1024, E=64, k=4, d_ff=512),
+    # up to 128 rows per group: the skinny path's 128-row units, with a shared expert of 120 rows
+    "small-T120-shared-bf16": C0.with_(dtype="bf16", T=120, d_model=256, E=4, k=2, d_ff=512,
+                                       d_ff_shared=256, bias=("normal", 0.5)),
     # capacity variants: Expanded Drop (m extra candidates re-home dropped pairs) and
     # capacity per group of experts, under skewed routers
     "expanded-drop-bf16": C0.with_(dtype="bf16", T=500, d_model=128, E=8, k=2, d_ff=192,
@@ -254,7 +257,7 @@ def test_layer_forward_small(name):
 
 
 @pytest.mark.parametrize("name", ["ragged-bf16", "fine-shared-bf16", "expert-choice-bf16",
-                                  "decode-T8-bf16", "decode-T48-shared-bf16",
+                                  "decode-T8-bf16", "decode-T48-shared-bf16", "small-T120-shared-bf16",
                                   "decode-T1-E64-bf16"])
 def test_layer_forward_deterministic_and_equal_to_steps(name):
     """Two runs give bit-identical routing and output; the one-call layer equals the four
@@ -595,10 +598,11 @@ def test_operand_offsets_past_2gib():
     say(f"[big] max|dy|/RMS per-token/global {p32:.4f}/{g32:.4f}")
 
 
-@pytest.mark.parametrize("T", [1, 8, 64])
+@pytest.mark.parametrize("T", [1, 8, 64, 128])
 def test_decode_shaped_layer(T):
     """The Mixtral-shaped layer with a decode-sized batch (T tokens, every expert's rows fit
-    the skinny GEMM path): y of every token against the oracle, through moe_layer_forward
+    the skinny GEMM path, units of 32, 64 or 128 rows): y of every token against the oracle,
+    through moe_layer_forward
     (row gather folded into the GEMM) and through the separate steps (x_perm copied)."""
     cfg = mi.MIXTRAL.with_(T=T)
     say(f"[decode] T={T}: generating inputs")
