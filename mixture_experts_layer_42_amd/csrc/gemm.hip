@@ -740,11 +740,12 @@ __global__ __launch_bounds__(256) void gemm_tail_reduce_kernel(GemmArgs args) {
 }
 
 // ----------------------------------------------------------------------------------------
-// Skinny path: groups of at most 128 rows (decode-shaped and small batches). Every weight
-// element is read once, so the GEMM is bound by streaming the weights from HBM; a 256-row tile
-// would spend its MFMAs on padding, and its two LDS stages cannot cover the HBM latency of the
-// weight slices once no other tile shares them in L2. A unit is 32*MB rows (MB = 1, 2 or 4:
-// stages of 40, 40 or 48 KB) x 256 B-columns x one K part of a group;
+// Skinny path: groups of at most 64 rows (gate/up) or 256 rows (down; decode-shaped and small
+// batches). The GEMM is bound by streaming the weights from HBM: a 256-row tile would spend its
+// MFMAs on padding, and its two LDS stages cannot cover the HBM latency of the weight slices
+// once no other tile shares them in L2. A unit is 32*MB rows (MB = 1, 2 or 4: stages of 40, 40
+// or 48 KB; a group of more than 128 rows takes two 128-row blocks, each streaming the weights)
+// x 256 B-columns x one K part of a group;
 // 4 waves own 64 B-columns each (for gate/up 32 gate and the matching 32 up columns), K in
 // slices of 64 through three LDS stages. K is cut into S parts only as far as the rule in
 // skinny_plan asks (about one or two units per CU: longer units keep the copy pipeline full,
@@ -809,11 +810,16 @@ __global__ __launch_bounds__(256, 1) void gemm_skinny_kernel(GemmArgs args) {
   const int S = args.sk_S;
   const int ntmax = args.s_rows > 0 && args.sN > args.N ? (args.sN + BNOUT - 1) / BNOUT
                                                          : (args.N + BNOUT - 1) / BNOUT;
-  const int units = G * ntmax * S;
+  // row blocks of SBM rows: groups of more than SBM rows (down GEMM, up to 256 rows) stream
+  // their weights once per block; a group's blocks are consecutive units, which run at about
+  // the same time, so the second read of a weight slice mostly finds it in the last-level cache
+  const int rbn = (args.max_group_rows + SBM - 1) / SBM;
+  const int units = G * ntmax * S * rbn;
   for (int u = blockIdx.x; u < units; u += gridDim.x) {
-    const int g = u / (ntmax * S), n_tile = (u / S) % ntmax, part = u % S;
+    const int rb = u % rbn, part = (u / rbn) % S, n_tile = (u / (rbn * S)) % ntmax;
+    const int g = u / (rbn * S * ntmax), m0 = rb * SBM;
     const GroupDesc d = group_desc(args, g);
-    if (d.rows == 0 || n_tile * BNOUT >= d.N) continue;   // uniform over the workgroup
+    if (d.rows <= m0 || n_tile * BNOUT >= d.N) continue;   // uniform over the workgroup
     const int nk = (d.K / BK) / S, k_begin = part * nk;
     const char *Ab = (const char *)d.A;
     uint32_t aoff[MB], boff[8];
@@ -821,7 +827,7 @@ __global__ __launch_bounds__(256, 1) void gemm_skinny_kernel(GemmArgs args) {
     for (int i = 0; i < MB; ++i) {
       const int r = (wvu * MB + i) * 8 + (lane >> 3);
       const int c = (lane & 7) ^ ((r >> 1) & 7);
-      int arow = min(r, d.rows - 1);
+      int arow = min(m0 + r, d.rows - 1);
       if (d.amap) arow = d.amap[arow];
       aoff[i] = ((uint32_t)arow * (uint32_t)d.lda + c * 8) * 2u;
     }
@@ -902,7 +908,7 @@ __global__ __launch_bounds__(256, 1) void gemm_skinny_kernel(GemmArgs args) {
         for (int m = 0; m < MB; ++m)
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
-            const int row = m * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+            const int row = m0 + m * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
             const uint32_t off = ((uint32_t)row * d.ldc + col) * CE;
             if (GATE_UP) {
               const float gv = acc[m][0][i], uv = acc[m][1][i];
@@ -928,7 +934,7 @@ __global__ __launch_bounds__(256, 1) void gemm_skinny_kernel(GemmArgs args) {
         for (int m = 0; m < MB; ++m)
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
-            const int row = m * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+            const int row = m0 + m * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
             if (row < d.rows) P[(size_t)row * args.sk_pitch + col] = acc[m][j][i];
           }
       }
@@ -1219,7 +1225,7 @@ hipError_t launch_skinny(const GemmArgs &a0, bool gate_up, const SkinnyPlan &sp,
   if (sp.S > 1 && !a.partials) return hipErrorInvalidValue;
   const int G = a.E + (a.s_rows > 0 ? 1 : 0);
   const int ntmax = sp.snt > sp.nt ? sp.snt : sp.nt;
-  int grid = G * ntmax * sp.S;
+  int grid = G * ntmax * sp.S * ((a.max_group_rows + 32 * sp.mb - 1) / (32 * sp.mb));
   if (grid > num_cu) grid = num_cu;
   if (grid < 1) grid = 1;
   if (gate_up) {

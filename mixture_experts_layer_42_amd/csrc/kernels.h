@@ -49,9 +49,10 @@ struct GemmArgs {
   int band;                         // bf16 tile order: column panels in bands of `band`, row
                                     // tile by row tile inside a band (<= 1: panel by panel)
   // few rows per group (decode-shaped batches): every group holds at most max_group_rows
-  // rows; when that is <= kSkinnyRows a 32/64/128-row tile streams the weights once, its K range
-  // cut into sk_S parts whose float32 sums (rows of sk_pitch floats, routed rows first, then
-  // the shared rows at row rcap) go to `partials`
+  // rows; when that is <= kSkinnyRows (kSkinnyRowsGateUp for gate/up), 32/64/128-row units
+  // stream the weights (once per 128-row block of a group), their K range cut into sk_S parts
+  // whose float32 sums (rows of sk_pitch floats, routed rows first, then the shared rows at
+  // row rcap) go to `partials`
   int max_group_rows;
   int rcap;                         // routed row capacity (T*k)
   int sk_S, sk_pitch;               // set by the launcher
@@ -59,7 +60,7 @@ struct GemmArgs {
 
 constexpr int kMaxPersistent = 256;   // persistent GEMM workgroups (one per CU on MI355X)
 constexpr size_t kPartialBytes = (size_t)kMaxPersistent * 256 * 256 * 4;
-constexpr int kSkinnyRows = 128;      // groups of at most this many rows take the skinny path
+constexpr int kSkinnyRows = 256;      // groups of at most this many rows take the skinny path
 constexpr int kSkinnyRowsGateUp = 64; // (the gate/up GEMM: only up to this many)
 // float32 partial-sum bytes the skinny path needs for a GEMM (0 if it does not apply)
 size_t skinny_partial_bytes(const GemmArgs &a, bool gate_up);

@@ -61,6 +61,9 @@ SMALL = {
     # up to 128 rows per group: the skinny path's 128-row units, with a shared expert of 120 rows
     "small-T120-shared-bf16": C0.with_(dtype="bf16", T=120, d_model=256, E=4, k=2, d_ff=512,
                                        d_ff_shared=256, bias=("normal", 0.5)),
+    # 200 rows per group: the down GEMM's skinny units in two 128-row blocks per group
+    "small-T200-E2-shared-bf16": C0.with_(dtype="bf16", T=200, d_model=256, E=2, k=2, d_ff=512,
+                                          d_ff_shared=256),
     # capacity variants: Expanded Drop (m extra candidates re-home dropped pairs) and
     # capacity per group of experts, under skewed routers
     "expanded-drop-bf16": C0.with_(dtype="bf16", T=500, d_model=128, E=8, k=2, d_ff=192,
@@ -258,6 +261,7 @@ def test_layer_forward_small(name):
 
 @pytest.mark.parametrize("name", ["ragged-bf16", "fine-shared-bf16", "expert-choice-bf16",
                                   "decode-T8-bf16", "decode-T48-shared-bf16", "small-T120-shared-bf16",
+                                  "small-T200-E2-shared-bf16",
                                   "decode-T1-E64-bf16"])
 def test_layer_forward_deterministic_and_equal_to_steps(name):
     """Two runs give bit-identical routing and output; the one-call layer equals the four
@@ -598,7 +602,7 @@ def test_operand_offsets_past_2gib():
     say(f"[big] max|dy|/RMS per-token/global {p32:.4f}/{g32:.4f}")
 
 
-@pytest.mark.parametrize("T", [1, 8, 64, 128])
+@pytest.mark.parametrize("T", [1, 8, 64, 128, 256])
 def test_decode_shaped_layer(T):
     """The Mixtral-shaped layer with a decode-sized batch (T tokens, every expert's rows fit
     the skinny GEMM path, units of 32, 64 or 128 rows): y of every token against the oracle,
