@@ -740,11 +740,11 @@ __global__ __launch_bounds__(256) void gemm_tail_reduce_kernel(GemmArgs args) {
 }
 
 // ----------------------------------------------------------------------------------------
-// Skinny path: groups of at most 64 rows (gate/up) or 256 rows (down; decode-shaped and small
+// Skinny path: groups of at most 64 rows (gate/up) or 384 rows (down; decode-shaped and small
 // batches). The GEMM is bound by streaming the weights from HBM: a 256-row tile would spend its
 // MFMAs on padding, and its two LDS stages cannot cover the HBM latency of the weight slices
 // once no other tile shares them in L2. A unit is 32*MB rows (MB = 1, 2 or 4: stages of 40, 40
-// or 48 KB; a group of more than 128 rows takes two 128-row blocks, each streaming the weights)
+// or 48 KB; a group of more than 128 rows takes 128-row blocks, each streaming the weights)
 // x 256 B-columns x one K part of a group;
 // 4 waves own 64 B-columns each (for gate/up 32 gate and the matching 32 up columns), K in
 // slices of 64 through three LDS stages. K is cut into S parts only as far as the rule in
@@ -810,7 +810,7 @@ __global__ __launch_bounds__(256, 1) void gemm_skinny_kernel(GemmArgs args) {
   const int S = args.sk_S;
   const int ntmax = args.s_rows > 0 && args.sN > args.N ? (args.sN + BNOUT - 1) / BNOUT
                                                          : (args.N + BNOUT - 1) / BNOUT;
-  // row blocks of SBM rows: groups of more than SBM rows (down GEMM, up to 256 rows) stream
+  // row blocks of SBM rows: groups of more than SBM rows (down GEMM, up to 384 rows) stream
   // their weights once per block; a group's blocks are consecutive units, which run at about
   // the same time, so the second read of a weight slice mostly finds it in the last-level cache
   const int rbn = (args.max_group_rows + SBM - 1) / SBM;
