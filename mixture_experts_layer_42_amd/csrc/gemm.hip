@@ -815,7 +815,9 @@ __global__ __launch_bounds__(256, 1) void gemm_skinny_kernel(GemmArgs args) {
   // the same time, so the second read of a weight slice mostly finds it in the last-level cache
   const int rbn = (args.max_group_rows + SBM - 1) / SBM;
   const int units = G * ntmax * S * rbn;
-  for (int u = blockIdx.x; u < units; u += gridDim.x) {
+  // with several row blocks, consecutive units (the blocks of one weight slice range) go to
+  // workgroups of one XCD, so they can share the slices through its L2
+  for (int u = rbn > 1 ? xcd_virtual_block() : (int)blockIdx.x; u < units; u += gridDim.x) {
     const int rb = u % rbn, part = (u / rbn) % S, n_tile = (u / (rbn * S)) % ntmax;
     const int g = u / (rbn * S * ntmax), m0 = rb * SBM;
     const GroupDesc d = group_desc(args, g);
