@@ -740,7 +740,7 @@ __global__ __launch_bounds__(256) void gemm_tail_reduce_kernel(GemmArgs args) {
 }
 
 // ----------------------------------------------------------------------------------------
-// Skinny path: groups of at most 64 rows (gate/up) or 384 rows (down; decode-shaped and small
+// Skinny path: groups of at most 64 rows (gate/up) or 768 rows (down; decode-shaped and small
 // batches). The GEMM is bound by streaming the weights from HBM: a 256-row tile would spend its
 // MFMAs on padding, and its two LDS stages cannot cover the HBM latency of the weight slices
 // once no other tile shares them in L2. A unit is 32*MB rows (MB = 1, 2 or 4: stages of 40, 40
@@ -804,24 +804,42 @@ __global__ __launch_bounds__(256, 1) void gemm_skinny_kernel(GemmArgs args) {
   constexpr int BNOUT = GATE_UP ? BN / 2 : BN;
   constexpr int NS = 3;   // stages (a fourth measured no faster)
   __shared__ SkStage<MB> st0, st1, st2;
+  __shared__ int ustart[kMaxGroups + 1];
+  __shared__ int usm[kMaxWaves + 1];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int wvu = __builtin_amdgcn_readfirstlane(wv);
   const int G = args.E + (args.s_rows > 0 ? 1 : 0);
   const int S = args.sk_S;
-  const int ntmax = args.s_rows > 0 && args.sN > args.N ? (args.sN + BNOUT - 1) / BNOUT
-                                                         : (args.N + BNOUT - 1) / BNOUT;
-  // row blocks of SBM rows: groups of more than SBM rows (down GEMM, up to 384 rows) stream
-  // their weights once per block; a group's blocks are consecutive units, which run at about
-  // the same time, so the second read of a weight slice mostly finds it in the last-level cache
-  const int rbn = (args.max_group_rows + SBM - 1) / SBM;
-  const int units = G * ntmax * S * rbn;
-  // with several row blocks, consecutive units (the blocks of one weight slice range) go to
-  // workgroups of one XCD, so they can share the slices through its L2
-  for (int u = rbn > 1 ? xcd_virtual_block() : (int)blockIdx.x; u < units; u += gridDim.x) {
-    const int rb = u % rbn, part = (u / rbn) % S, n_tile = (u / (rbn * S)) % ntmax;
-    const int g = u / (rbn * S * ntmax), m0 = rb * SBM;
+  // Units from the device-side row counts: group g has nb = ceil(rows / SBM) row blocks x its
+  // column panels x S K-parts (ustart: prefix over groups). Groups of more than SBM rows (down
+  // GEMM) stream their weights once per block; a group's blocks of one weight range are
+  // consecutive units, which run at about the same time on workgroups of one XCD (when blocks
+  // can exist), so the later reads of a weight slice mostly find it in its L2 or the
+  // last-level cache.
+  {
+    int run = 0;
+    for (int c0 = 0; c0 < G; c0 += blockDim.x) {
+      const int g = c0 + threadIdx.x;
+      int nu = 0;
+      if (g < G) {
+        const GroupDesc d = group_desc(args, g);
+        nu = ((d.rows + SBM - 1) / SBM) * ((d.N + BNOUT - 1) / BNOUT) * S;
+      }
+      int tot;
+      const int ex = block_excl_scan(nu, usm, &tot);
+      if (g < G) ustart[g] = run + ex;
+      run += tot;
+    }
+    if (threadIdx.x == 0) ustart[G] = run;
+    __syncthreads();
+  }
+  const int units = ustart[G];
+  for (int u = args.max_group_rows > SBM ? xcd_virtual_block() : (int)blockIdx.x; u < units;
+       u += gridDim.x) {
+    const int g = find_group(ustart, G, u);
     const GroupDesc d = group_desc(args, g);
-    if (d.rows <= m0 || n_tile * BNOUT >= d.N) continue;   // uniform over the workgroup
+    const int nb = (d.rows + SBM - 1) / SBM, lu = u - ustart[g];
+    const int rb = lu % nb, part = (lu / nb) % S, n_tile = lu / (nb * S), m0 = rb * SBM;
     const int nk = (d.K / BK) / S, k_begin = part * nk;
     const char *Ab = (const char *)d.A;
     uint32_t aoff[MB], boff[8];

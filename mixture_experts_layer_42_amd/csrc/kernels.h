@@ -60,7 +60,7 @@ struct GemmArgs {
 
 constexpr int kMaxPersistent = 256;   // persistent GEMM workgroups (one per CU on MI355X)
 constexpr size_t kPartialBytes = (size_t)kMaxPersistent * 256 * 256 * 4;
-constexpr int kSkinnyRows = 384;      // groups of at most this many rows take the skinny path
+constexpr int kSkinnyRows = 768;      // groups of at most this many rows take the skinny path
 constexpr int kSkinnyRowsGateUp = 64; // (the gate/up GEMM: only up to this many)
 // float32 partial-sum bytes the skinny path needs for a GEMM (0 if it does not apply)
 size_t skinny_partial_bytes(const GemmArgs &a, bool gate_up);

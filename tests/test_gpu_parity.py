@@ -602,7 +602,7 @@ def test_operand_offsets_past_2gib():
     say(f"[big] max|dy|/RMS per-token/global {p32:.4f}/{g32:.4f}")
 
 
-@pytest.mark.parametrize("T", [1, 8, 64, 128, 256, 384])
+@pytest.mark.parametrize("T", [1, 8, 64, 128, 256, 384, 768])
 def test_decode_shaped_layer(T):
     """The Mixtral-shaped layer with a decode-sized batch (T tokens, every expert's rows fit
     the skinny GEMM path, units of 32, 64 or 128 rows): y of every token against the oracle,
