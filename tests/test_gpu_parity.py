@@ -659,7 +659,11 @@ def _random_problem(seed):
     return C0.with_(name=f"random-{seed}", **kw)
 
 
-@pytest.mark.parametrize("seed", range(int(__import__("os").environ.get("MOE_RANDOM_CASES", "48"))))
+_RANDOM_START = int(__import__("os").environ.get("MOE_RANDOM_START", "0"))
+_RANDOM_CASES = int(__import__("os").environ.get("MOE_RANDOM_CASES", "48"))
+
+
+@pytest.mark.parametrize("seed", range(_RANDOM_START, _RANDOM_START + _RANDOM_CASES))
 def test_random_shapes(seed):
     """Seeded random problems over the ABI's options (dtype, ragged T, 1..128 experts, k,
     shared expert, renormalisation, biases, every selection form): routing with the oracle's
